@@ -1,0 +1,255 @@
+// C ABI of libfam.so: argument validation, the host-side budget plan and
+// kernel dispatch. Nothing here allocates device memory or synchronises.
+#include "fam.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "fam_kernels.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+fam_status fail(fam_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+fam_status ok() {
+  g_error.clear();
+  return FAM_OK;
+}
+
+fam_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(FAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr int kMaxSeq = 1 << 28;
+
+struct ScoreShape {
+  int B, Hq, Hkv, S, d;
+  int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss;
+};
+
+fam_status check_scores(const void* q, const void* k, fam_dtype dtype, const ScoreShape& s) {
+  if (!q || !k) return fail(FAM_ERR_INVALID_ARG, "q and k must be non-null");
+  if (dtype != FAM_BF16 && dtype != FAM_FP16)
+    return fail(FAM_ERR_UNSUPPORTED, "dtype %d is not bf16 or fp16", (int)dtype);
+  if (s.B < 1 || s.Hq < 1 || s.Hkv < 1 || s.S < 1)
+    return fail(FAM_ERR_INVALID_ARG, "B, Hq, Hkv and S must be >= 1 (got %d, %d, %d, %d)",
+                s.B, s.Hq, s.Hkv, s.S);
+  if (s.S > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "S = %d exceeds %d", s.S, kMaxSeq);
+  if (s.Hq % s.Hkv != 0)
+    return fail(FAM_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", s.Hq, s.Hkv);
+  if (s.d != 64 && s.d != 128) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64 or 128)", s.d);
+  const int64_t st[6] = {s.q_sb, s.q_sh, s.q_ss, s.k_sb, s.k_sh, s.k_ss};
+  for (int i = 0; i < 6; ++i) {
+    if (st[i] < 0) return fail(FAM_ERR_INVALID_ARG, "strides must be >= 0");
+    if (st[i] % 8 != 0)
+      return fail(FAM_ERR_INVALID_ARG, "strides must be multiples of 8 elements (16 bytes)");
+  }
+  if (!aligned16(q) || !aligned16(k)) return fail(FAM_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  return FAM_OK;
+}
+
+float resolve_scale(float scale, int d) {
+  const double sc = scale > 0.f ? (double)scale : 1.0 / std::sqrt((double)d);
+  return (float)(sc * 1.4426950408889634);  // base-2 logits inside the kernels
+}
+
+fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
+
+// Forced set and candidate range for a head of length S.
+struct Plan {
+  int c0, c1, forced;
+};
+Plan plan_of(int S, int sinks, int recent) {
+  Plan p;
+  p.c0 = sinks < S ? sinks : S;
+  const int64_t tail = (int64_t)S - (int64_t)recent;
+  p.c1 = tail > p.c0 ? (int)tail : p.c0;
+  p.forced = S - (p.c1 - p.c0);
+  return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fam_status_string(fam_status st) {
+  switch (st) {
+    case FAM_OK: return "FAM_OK";
+    case FAM_ERR_INVALID_ARG: return "FAM_ERR_INVALID_ARG";
+    case FAM_ERR_UNSUPPORTED: return "FAM_ERR_UNSUPPORTED";
+    case FAM_ERR_WORKSPACE: return "FAM_ERR_WORKSPACE";
+    case FAM_ERR_HIP: return "FAM_ERR_HIP";
+  }
+  return "FAM_ERR_UNKNOWN";
+}
+
+const char* fam_last_error(void) { return g_error.c_str(); }
+
+fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
+                   int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
+                   int64_t k_ss, float scale, float* lse, void* stream) {
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  fam_status st = check_scores(q, k, dtype, s);
+  if (st != FAM_OK) return st;
+  if (!lse) return fail(FAM_ERR_INVALID_ARG, "lse must be non-null");
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  fam::LseArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse,
+                 q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
+                 resolve_scale(scale, d)};
+  return hip_status(fam::launch_lse(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_lse launch");
+}
+
+fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype, int B, int Hq,
+                    int Hkv, int S, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb,
+                    int64_t k_sh, int64_t k_ss, int W, float scale, float* mass, void* stream) {
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  fam_status st = check_scores(q, k, dtype, s);
+  if (st != FAM_OK) return st;
+  if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
+  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  fam::MassArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, mass,
+                  q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
+                  W < S ? W : S, resolve_scale(scale, d)};
+  return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_mass launch");
+}
+
+fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
+                       int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
+                       int64_t k_ss, int W, float scale, float* lse, float* mass, void* stream) {
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  fam_status st = check_scores(q, k, dtype, s);
+  if (st != FAM_OK) return st;
+  if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
+  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  st = fam_lse(q, k, dtype, B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, scale, lse, stream);
+  if (st != FAM_OK) return st;
+  return fam_mass(q, k, lse, dtype, B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, W, scale,
+                  mass, stream);
+}
+
+fam_status evict_plan(int H, int S, const int64_t* budgets, int sinks, int recent, int64_t* kept,
+                      int64_t* offsets) {
+  if (H < 0) return fail(FAM_ERR_INVALID_ARG, "H must be >= 0 (got %d)", H);
+  if (S < 1) return fail(FAM_ERR_INVALID_ARG, "S must be >= 1 (got %d)", S);
+  if (sinks < 0 || recent < 0) return fail(FAM_ERR_INVALID_ARG, "sinks and recent must be >= 0");
+  if (H > 0 && !budgets) return fail(FAM_ERR_INVALID_ARG, "budgets must be non-null");
+  for (int h = 0; h < H; ++h)
+    if (budgets[h] < 0) return fail(FAM_ERR_INVALID_ARG, "budget of head %d is negative", h);
+  const Plan p = plan_of(S, sinks, recent);
+  int64_t off = 0;
+  if (offsets) offsets[0] = 0;
+  for (int h = 0; h < H; ++h) {
+    int64_t kh = budgets[h] > p.forced ? budgets[h] : p.forced;
+    if (kh > S) kh = S;
+    if (kept) kept[h] = kh;
+    off += kh;
+    if (offsets) offsets[h + 1] = off;
+  }
+  return ok();
+}
+
+fam_status fam_budgets_from_ratios(int H, const double* ratios, int64_t t, int64_t* budgets) {
+  if (H < 0 || t < 0) return fail(FAM_ERR_INVALID_ARG, "H and t must be >= 0");
+  if (H > 0 && (!ratios || !budgets)) return fail(FAM_ERR_INVALID_ARG, "ratios and budgets must be non-null");
+  for (int h = 0; h < H; ++h) {
+    const double r = ratios[h];
+    if (!std::isfinite(r) || r < 0.0) return fail(FAM_ERR_INVALID_ARG, "ratio of head %d is invalid", h);
+    const double b = std::floor(r * (double)t);
+    if (b > 9.0e18) return fail(FAM_ERR_INVALID_ARG, "budget of head %d overflows", h);
+  }
+  for (int h = 0; h < H; ++h) budgets[h] = (int64_t)std::floor(ratios[h] * (double)t);
+  return ok();
+}
+
+fam_status evict_select(const float* scores, int64_t score_row_stride, int H, int S,
+                        const int64_t* budgets, int sinks, int recent, int32_t* idx,
+                        int64_t* offsets_dev, void* stream) {
+  if (H < 0) return fail(FAM_ERR_INVALID_ARG, "H must be >= 0 (got %d)", H);
+  if (S < 1 || S > kMaxSeq) return fail(FAM_ERR_INVALID_ARG, "S = %d out of range", S);
+  if (sinks < 0 || recent < 0) return fail(FAM_ERR_INVALID_ARG, "sinks and recent must be >= 0");
+  if (H == 0) return ok();
+  if (!scores || !idx || !offsets_dev || !budgets)
+    return fail(FAM_ERR_INVALID_ARG, "scores, budgets, idx and offsets_dev must be non-null");
+  if (score_row_stride < S) return fail(FAM_ERR_INVALID_ARG, "score row stride must be >= S");
+  for (int h = 0; h < H; ++h)
+    if (budgets[h] < 0) return fail(FAM_ERR_INVALID_ARG, "budget of head %d is negative", h);
+  const Plan p = plan_of(S, sinks, recent);
+  if (p.c1 - p.c0 > fam::kSelectMaxCandidates)
+    return fail(FAM_ERR_UNSUPPORTED, "%d candidates per head exceed %d", p.c1 - p.c0,
+                fam::kSelectMaxCandidates);
+  int64_t total = 0;
+  for (int h = 0; h < H; ++h) {
+    int64_t kh = budgets[h] > p.forced ? budgets[h] : p.forced;
+    total += kh > S ? S : kh;
+  }
+  fam::SelectArgs a{};
+  a.scores = scores;
+  a.row_stride = score_row_stride;
+  a.idx = idx;
+  a.offsets_dev = offsets_dev;
+  a.total = total;
+  a.S = S;
+  a.H = H;
+  a.c0 = p.c0;
+  a.c1 = p.c1;
+  int64_t off = 0;
+  for (int h0 = 0; h0 < H; h0 += fam::kSelectBatch) {
+    const int n = H - h0 < fam::kSelectBatch ? H - h0 : fam::kSelectBatch;
+    a.head0 = h0;
+    a.nheads = n;
+    for (int i = 0; i < n; ++i) {
+      int64_t kh = budgets[h0 + i] > p.forced ? budgets[h0 + i] : p.forced;
+      if (kh > S) kh = S;
+      a.out_off[i] = off;
+      a.n_choose[i] = (int32_t)(kh - p.forced);
+      off += kh;
+    }
+    const hipError_t e = fam::launch_select(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_status(e, "evict_select launch");
+  }
+  return ok();
+}
+
+fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S, int d,
+                      int64_t k_sh, int64_t k_ss, int64_t v_sh, int64_t v_ss, const int32_t* idx,
+                      const int64_t* offsets_dev, int64_t total_rows, void* k_new, void* v_new,
+                      void* stream) {
+  if (elem_bytes != 2) return fail(FAM_ERR_UNSUPPORTED, "elem_bytes %d (need 2)", elem_bytes);
+  if (H < 1 || S < 1 || total_rows < 0)
+    return fail(FAM_ERR_INVALID_ARG, "need H >= 1, S >= 1, total_rows >= 0");
+  if (d != 64 && d != 128 && d != 256) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64, 128 or 256)", d);
+  if (total_rows == 0) return ok();
+  if (!k || !v || !idx || !offsets_dev || !k_new || !v_new)
+    return fail(FAM_ERR_INVALID_ARG, "pointers must be non-null");
+  const int64_t st[4] = {k_sh, k_ss, v_sh, v_ss};
+  for (int i = 0; i < 4; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0)
+      return fail(FAM_ERR_INVALID_ARG, "strides must be >= 0 and multiples of 8 elements");
+  if (!aligned16(k) || !aligned16(v) || !aligned16(k_new) || !aligned16(v_new))
+    return fail(FAM_ERR_INVALID_ARG, "k, v, k_new and v_new must be 16-byte aligned");
+  fam::CompactArgs a{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), k_sh, k_ss,
+                     v_sh, v_ss, idx, offsets_dev, total_rows, static_cast<uint16_t*>(k_new),
+                     static_cast<uint16_t*>(v_new), H, S, d};
+  return hip_status(fam::launch_compact(a, static_cast<hipStream_t>(stream)), "kv_compact launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,65 @@
+// Device-side helpers shared by the score kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fam {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kInf = __builtin_huge_valf();
+
+struct Bf16 {};
+struct Fp16 {};
+
+// One 32x32x16 MFMA on raw 16-byte operand fragments (8 two-byte elements per
+// lane). Lane l supplies row l%32 of A (or column l%32 of B) and 8 entries of
+// the contraction axis; A and B must use the same assignment of the
+// contraction axis to (lane/32, element), which the callers guarantee by
+// loading both from the same head-dim offsets.
+template <typename T> struct Mma;
+template <> struct Mma<Bf16> {
+  static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+  }
+};
+template <> struct Mma<Fp16> {
+  static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
+                                                  __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+  }
+};
+
+// Row of accumulator entry v held by a lane in the 32x32 MFMA output; the
+// column is lane % 32. Verified on gfx950 for v_mfma_f32_32x32x16_{bf16,f16}.
+__device__ __forceinline__ int acc_row(int v, int lane) {
+  return 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ u32x4_t load16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4_t*>(p);
+}
+__device__ __forceinline__ void store16(uint16_t* p, u32x4_t v) {
+  *reinterpret_cast<u32x4_t*>(p) = v;
+}
+__device__ __forceinline__ u32x4_t zero16() { return u32x4_t{0u, 0u, 0u, 0u}; }
+
+// Pairwise sum of the 16 accumulator-shaped values.
+__device__ __forceinline__ float sum16(const float (&e)[16]) {
+  float a0 = e[0] + e[1], a1 = e[2] + e[3], a2 = e[4] + e[5], a3 = e[6] + e[7];
+  float a4 = e[8] + e[9], a5 = e[10] + e[11], a6 = e[12] + e[13], a7 = e[14] + e[15];
+  return ((a0 + a1) + (a2 + a3)) + ((a4 + a5) + (a6 + a7));
+}
+
+}  // namespace fam

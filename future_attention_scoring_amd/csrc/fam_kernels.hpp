@@ -1,0 +1,68 @@
+// Launch interfaces between the C ABI layer and the HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fam {
+
+enum class Elem { kBf16, kFp16 };
+
+// Causal row log-sum-exp (first pass).
+struct LseArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  float* lse;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int B, Hq, Hkv, S, d, g;
+  float c;  // scale * log2(e)
+};
+hipError_t launch_lse(const LseArgs& a, Elem e, hipStream_t s);
+
+// Key-major future-attention mass (second pass).
+struct MassArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const float* lse;
+  float* mass;
+  int64_t q_sb, q_sh, q_ss;
+  int64_t k_sb, k_sh, k_ss;
+  int B, Hq, Hkv, S, d, g, W;
+  float c;  // scale * log2(e)
+};
+hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s);
+
+// Per-head selection. Heads are launched in batches whose plan travels in
+// the kernel arguments.
+constexpr int kSelectBatch = 64;
+constexpr int kSelectMaxCandidates = 131072;
+struct SelectArgs {
+  const float* scores;
+  int64_t row_stride;
+  int32_t* idx;
+  int64_t* offsets_dev;
+  int64_t total;       // offsets[H]
+  int S, H;
+  int c0, c1;          // candidates are positions [c0, c1)
+  int head0, nheads;   // heads [head0, head0 + nheads) in this launch
+  int64_t out_off[kSelectBatch];
+  int32_t n_choose[kSelectBatch];
+};
+hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+
+// Row gather of K and V into packed caches.
+struct CompactArgs {
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t k_sh, k_ss, v_sh, v_ss;
+  const int32_t* idx;
+  const int64_t* offsets;
+  int64_t total_rows;
+  uint16_t* k_new;
+  uint16_t* v_new;
+  int H, S, d;
+};
+hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+}  // namespace fam

@@ -1,0 +1,172 @@
+// First pass: causal row log-sum-exp on bf16/fp16 MFMA (gfx950).
+//
+// KVpop ("Delayed Memory Scoring"): the normaliser of query i sums exp(logit)
+// over the keys j <= i. Here each query's normaliser is formed online over key
+// tiles, in base 2 internally, and stored as a natural log.
+//
+// Work decomposition
+//   * A "row unit" is 64 consecutive query positions of one query head. The
+//     units of one (batch, KV head) are ordered by position, latest first, and
+//     a workgroup of 4 waves takes 4 consecutive units, so the query heads of
+//     a GQA group (or neighbouring position blocks when the group is smaller
+//     than 4) share every K tile the workgroup stages.
+//   * Each wave keeps its 64 queries' Q fragments in registers as the MFMA B
+//     operand and computes S^T = K_tile * Q^T, so every accumulator column is
+//     one query and the reduction over keys stays inside a lane (the two
+//     half-waves hold disjoint key rows and keep separate running max/sum
+//     that are merged once at the end).
+//   * K tiles of 64 keys are double-buffered through LDS with a 16-byte row
+//     pad (conflict-free ds_read_b128 of the A fragments).
+//   * Workgroups are numbered latest-position-first (the longest causal rows
+//     start first) and with the (batch, KV head) index fastest, so with eight
+//     KV heads each XCD works on a single head's K.
+#include "fam_device.hpp"
+#include "fam_kernels.hpp"
+
+namespace fam {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 64;
+constexpr int kKeyTile = 64;
+
+__device__ __forceinline__ void online_update(f32x16_t acc, int kb, int qblock, int S,
+                                              int lane, float c, float& m, float& l) {
+  const int qrow = qblock + (lane & 31);
+  if (kb + 31 > qblock || kb + 32 > S) {  // diagonal or ragged tile: mask
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      const int key = kb + acc_row(v, lane);
+      if (key > qrow || key >= S) acc[v] = -kInf;
+    }
+  }
+  float mx = acc[0];
+#pragma unroll
+  for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
+  const float m_new = fmaxf(m, mx * c);
+  const float m_use = m_new == -kInf ? 0.f : m_new;
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -m_use));
+  l = fmaf(l, fast_exp2(m - m_use), sum16(e));
+  m = m_new;
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(kThreads, 2) void lse_kernel(LseArgs p, int npb) {
+  constexpr int PITCH = D + 8;                 // LDS row pitch in elements
+  constexpr int KS = D / 16;                   // MFMA k-steps per 32x32 block
+  constexpr int CPR = D / 8;                   // 16-byte chunks per row
+  constexpr int CHUNKS = kKeyTile * CPR / kThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKeyTile * PITCH];
+
+  const int nbh = p.B * p.Hkv;
+  const int bh = blockIdx.x % nbh;
+  const int slot = blockIdx.x / nbh;
+  const int b = bh / p.Hkv, h = bh % p.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  const int unit = slot * kWaves + wave;
+  const bool active = unit < npb * p.g;
+  const int pb = npb - 1 - (active ? unit / p.g : 0);
+  const int qh = h * p.g + (active ? unit % p.g : 0);
+  const int q0 = pb * kRowsPerWave;
+
+  // the workgroup's first unit holds its latest positions
+  const int pb_top = npb - 1 - (slot * kWaves) / p.g;
+  const int kend = min(p.S, (pb_top + 1) * kRowsPerWave);
+  const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
+
+  const uint16_t* qbase = p.q + b * p.q_sb + qh * p.q_sh;
+  const uint16_t* kbase = p.k + b * p.k_sb + h * p.k_sh;
+
+  u32x4_t qf[2][KS];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int row = q0 + 32 * blk + col;
+    const bool ok = active && row < p.S;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qf[blk][ks] = ok ? load16(qbase + (int64_t)row * p.q_ss + ks * 16 + half * 8) : zero16();
+  }
+
+  u32x4_t st[CHUNKS];
+  auto load_tile = [&](int t) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int id = tid + c * kThreads;
+      const int r = id / CPR, ch = id % CPR;
+      const int key = t * kKeyTile + r;
+      st[c] = key < p.S ? load16(kbase + (int64_t)key * p.k_ss + ch * 8) : zero16();
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int id = tid + c * kThreads;
+      const int r = id / CPR, ch = id % CPR;
+      store16(&sk[buf][r * PITCH + ch * 8], st[c]);
+    }
+  };
+
+  float m[2] = {-kInf, -kInf}, l[2] = {0.f, 0.f};
+  load_tile(0);
+  store_tile(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; ++t) {
+    const bool more = t + 1 < ntiles;
+    if (more) load_tile(t + 1);
+    const uint16_t* buf = sk[t & 1];
+#pragma unroll
+    for (int kk = 0; kk < kKeyTile / 32; ++kk) {
+      const int kb = t * kKeyTile + 32 * kk;
+      if (active && kb <= q0 + 63 && kb < p.S) {
+        f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              &buf[(32 * kk + col) * PITCH + ks * 16 + half * 8]);
+          acc0 = Mma<T>::run(a, qf[0][ks], acc0);
+          acc1 = Mma<T>::run(a, qf[1][ks], acc1);
+        }
+        online_update(acc0, kb, q0, p.S, lane, p.c, m[0], l[0]);
+        online_update(acc1, kb, q0 + 32, p.S, lane, p.c, m[1], l[1]);
+      }
+    }
+    if (more) store_tile((t + 1) & 1);
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const float mo = __shfl_xor(m[blk], 32);
+    const float lo = __shfl_xor(l[blk], 32);
+    const float M = fmaxf(m[blk], mo);
+    const float Mu = M == -kInf ? 0.f : M;
+    const float L = l[blk] * fast_exp2(m[blk] - Mu) + lo * fast_exp2(mo - Mu);
+    const int row = q0 + 32 * blk + col;
+    if (active && half == 0 && row < p.S)
+      p.lse[((int64_t)b * p.Hq + qh) * p.S + row] = (M + fast_log2(L)) * kLn2;
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_lse_t(const LseArgs& a, hipStream_t s) {
+  const int npb = (a.S + kRowsPerWave - 1) / kRowsPerWave;
+  const int slots = (npb * a.g + kWaves - 1) / kWaves;
+  const int64_t grid = (int64_t)slots * a.B * a.Hkv;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((lse_kernel<D, T>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lse(const LseArgs& a, Elem e, hipStream_t s) {
+  if (a.d == 128) return e == Elem::kBf16 ? launch_lse_t<128, Bf16>(a, s) : launch_lse_t<128, Fp16>(a, s);
+  return e == Elem::kBf16 ? launch_lse_t<64, Bf16>(a, s) : launch_lse_t<64, Fp16>(a, s);
+}
+
+}  // namespace fam

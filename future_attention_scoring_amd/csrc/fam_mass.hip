@@ -1,0 +1,187 @@
+// Second pass: key-major future-attention mass on bf16/fp16 MFMA (gfx950).
+//
+// KVpop ("Defining Future Attention Utility", Figure 2 "Transposed
+// Attention", and the appendix on the transposed pass): the mass of key j is
+// the sum, over the query heads of its GQA group and over queries i >= j + W,
+// of exp(logit_ij - LSE_i). The page obtains it by swapping the roles of
+// queries and keys in an attention call; here the same sum is formed directly
+// as register column sums, which needs no running maximum because every term
+// exp(logit - LSE) is at most one.
+//
+// Work decomposition
+//   * A workgroup owns 256 consecutive keys of one (batch, KV head); each of
+//     its 4 waves keeps 64 keys' K fragments in registers as the MFMA B
+//     operand and computes S = Q_tile * K^T, so every accumulator column is
+//     one key and the column sum over queries stays inside a lane (the two
+//     half-waves hold disjoint query rows and are added once at the end).
+//   * The workgroup walks the query tiles i >= j0 + W of every query head of
+//     the group; each (tile, head) step stages 32 query rows and their
+//     normalisers (in base-2 units) through double-buffered LDS, shared by
+//     the 4 waves.
+//   * Only band tiles (those that contain some i < j + W) evaluate the window
+//     predicate. Keys that no query can reach (j > S - 1 - W) get exactly 0.
+//   * Per-step partial sums are added into a mid-level accumulator that is
+//     folded into the total every 16 steps, which bounds the fp32 summation
+//     error independently of S.
+//   * Workgroups are numbered earliest-key-first (the longest columns start
+//     first) with the (batch, KV head) index fastest.
+#include "fam_device.hpp"
+#include "fam_kernels.hpp"
+
+namespace fam {
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kKeysPerWave = 64;
+constexpr int kKeysPerWG = kKeysPerWave * kWaves;
+constexpr int kQTile = 32;
+
+// Adds the terms of one 32x32 (query x key) block into `mid`.
+__device__ __forceinline__ void accumulate(f32x16_t acc, const float (&lv)[16], int i0, int jk,
+                                           int W, int lane, float c, float& mid) {
+  if (i0 + 31 < jk + W) return;                    // no query of the tile counts
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -lv[v]));
+  if (i0 < jk + 31 + W) {                          // band tile: window predicate
+    const int j = jk + (lane & 31);
+#pragma unroll
+    for (int v = 0; v < 16; ++v)
+      if (i0 + acc_row(v, lane) < j + W) e[v] = 0.f;
+  }
+  mid += sum16(e);
+}
+
+template <int D, typename T>
+__global__ __launch_bounds__(kThreads, 2) void mass_kernel(MassArgs p) {
+  constexpr int PITCH = D + 8;
+  constexpr int KS = D / 16;
+  constexpr int CPR = D / 8;
+  constexpr int CHUNKS = kQTile * CPR / kThreads;
+  static_assert(CHUNKS >= 1, "tile too small for the workgroup");
+  __shared__ __attribute__((aligned(16))) uint16_t sq[2][kQTile * PITCH];
+  __shared__ __attribute__((aligned(16))) float sl[2][kQTile];
+
+  const int nbh = p.B * p.Hkv;
+  const int bh = blockIdx.x % nbh;
+  const int kbi = blockIdx.x / nbh;
+  const int b = bh / p.Hkv, h = bh % p.Hkv;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int half = lane >> 5, col = lane & 31;
+
+  const int j0 = kbi * kKeysPerWG;
+  const int jw = j0 + wave * kKeysPerWave;
+
+  const uint16_t* kbase = p.k + b * p.k_sb + h * p.k_sh;
+  u32x4_t kf[2][KS];
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    const int key = jw + 32 * blk + col;
+    const bool ok = key < p.S;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      kf[blk][ks] = ok ? load16(kbase + (int64_t)key * p.k_ss + ks * 16 + half * 8) : zero16();
+  }
+
+  float top[2] = {0.f, 0.f}, mid[2] = {0.f, 0.f};
+  const int i_first = j0 + p.W;
+  if (i_first < p.S) {
+    const int t0 = i_first / kQTile;
+    const int t1 = (p.S + kQTile - 1) / kQTile;
+    const int nsteps = (t1 - t0) * p.g;
+
+    u32x4_t st[CHUNKS];
+    float lst = 0.f;
+    auto load_step = [&](int u) {
+      const int t = t0 + u / p.g;
+      const int qh = h * p.g + u % p.g;
+      const uint16_t* qbase = p.q + b * p.q_sb + qh * p.q_sh;
+#pragma unroll
+      for (int c = 0; c < CHUNKS; ++c) {
+        const int id = tid + c * kThreads;
+        const int r = id / CPR, ch = id % CPR;
+        const int row = t * kQTile + r;
+        st[c] = row < p.S ? load16(qbase + (int64_t)row * p.q_ss + ch * 8) : zero16();
+      }
+      if (tid < kQTile) {
+        const int row = t * kQTile + tid;
+        lst = row < p.S ? p.lse[((int64_t)b * p.Hq + qh) * p.S + row] * kLog2e : kInf;
+      }
+    };
+    auto store_step = [&](int buf) {
+#pragma unroll
+      for (int c = 0; c < CHUNKS; ++c) {
+        const int id = tid + c * kThreads;
+        const int r = id / CPR, ch = id % CPR;
+        store16(&sq[buf][r * PITCH + ch * 8], st[c]);
+      }
+      if (tid < kQTile) sl[buf][tid] = lst;
+    };
+
+    load_step(0);
+    store_step(0);
+    __syncthreads();
+    for (int u = 0; u < nsteps; ++u) {
+      const bool more = u + 1 < nsteps;
+      if (more) load_step(u + 1);
+      const int buf = u & 1;
+      const int i0 = (t0 + u / p.g) * kQTile;
+      if (i0 + 31 >= jw + p.W) {                   // wave-uniform: some pair counts
+        float lv[16];
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sl[buf][8 * r4 + 4 * half]);
+          lv[4 * r4 + 0] = x[0];
+          lv[4 * r4 + 1] = x[1];
+          lv[4 * r4 + 2] = x[2];
+          lv[4 * r4 + 3] = x[3];
+        }
+        f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+              &sq[buf][col * PITCH + ks * 16 + half * 8]);
+          acc0 = Mma<T>::run(a, kf[0][ks], acc0);
+          acc1 = Mma<T>::run(a, kf[1][ks], acc1);
+        }
+        accumulate(acc0, lv, i0, jw, p.W, lane, p.c, mid[0]);
+        accumulate(acc1, lv, i0, jw + 32, p.W, lane, p.c, mid[1]);
+      }
+      if ((u & 15) == 15) {
+        top[0] += mid[0];
+        top[1] += mid[1];
+        mid[0] = 0.f;
+        mid[1] = 0.f;
+      }
+      if (more) store_step((u + 1) & 1);
+      __syncthreads();
+    }
+  }
+
+#pragma unroll
+  for (int blk = 0; blk < 2; ++blk) {
+    float tot = top[blk] + mid[blk];
+    tot += __shfl_xor(tot, 32);
+    const int key = jw + 32 * blk + col;
+    if (half == 0 && key < p.S) p.mass[((int64_t)b * p.Hkv + h) * p.S + key] = tot;
+  }
+}
+
+template <int D, typename T>
+hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
+  const int nkb = (a.S + kKeysPerWG - 1) / kKeysPerWG;
+  const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((mass_kernel<D, T>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s) {
+  if (a.d == 128) return e == Elem::kBf16 ? launch_mass_t<128, Bf16>(a, s) : launch_mass_t<128, Fp16>(a, s);
+  return e == Elem::kBf16 ? launch_mass_t<64, Bf16>(a, s) : launch_mass_t<64, Fp16>(a, s);
+}
+
+}  // namespace fam

@@ -1,0 +1,212 @@
+"""Thin ctypes binding over libfam.so (argument marshalling only).
+
+Every function has the name of the C entry point it calls. Tensors are
+torch tensors; torch supplies device memory and the current HIP stream, and
+all computation happens in the library's HIP kernels. If libfam.so has not
+been built the first call raises ``FamError``; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence, Tuple
+
+import numpy as np
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfam.so")
+_lib = None
+
+FAM_BF16, FAM_FP16 = 0, 1
+_STATUS = {0: "FAM_OK", 1: "FAM_ERR_INVALID_ARG", 2: "FAM_ERR_UNSUPPORTED",
+           3: "FAM_ERR_WORKSPACE", 4: "FAM_ERR_HIP"}
+
+# (name, restype, argtypes) of every exported symbol of include/fam.h
+_i, _i64, _f, _p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
+_SIGNATURES = {
+    "fam_status_string": (ctypes.c_char_p, [_i]),
+    "fam_last_error": (ctypes.c_char_p, []),
+    "fam_lse": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64, _f, _p, _p]),
+    "fam_mass": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
+                      _i, _f, _p, _p]),
+    "fam_compute": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
+                         _i, _f, _p, _p, _p]),
+    "evict_plan": (_i, [_i, _i, _p, _i, _i, _p, _p]),
+    "fam_budgets_from_ratios": (_i, [_i, _p, _i64, _p]),
+    "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p]),
+    "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
+}
+EXPORTED = tuple(_SIGNATURES)
+
+
+class FamError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {detail}")
+        self.status = status
+        self.detail = detail
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libfam.so once; raise FamError if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise FamError(-1, f"{_LIB_PATH} is missing; build it with "
+                               "python -m future_attention_scoring_amd.build")
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != 0:
+        raise FamError(status, load().fam_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return FAM_BF16
+    if t.dtype == torch.float16:
+        return FAM_FP16
+    raise FamError(2, f"dtype {t.dtype} is not bfloat16 or float16")
+
+
+def _as4(t: torch.Tensor) -> torch.Tensor:
+    if t.dim() == 3:
+        return t.unsqueeze(0)
+    if t.dim() != 4:
+        raise FamError(1, f"expected [B,H,S,d] or [H,S,d], got shape {tuple(t.shape)}")
+    return t
+
+
+def _score_args(q: torch.Tensor, k: torch.Tensor):
+    q4, k4 = _as4(q), _as4(k)
+    if not (q4.is_cuda and k4.is_cuda):
+        raise FamError(1, "q and k must be device tensors")
+    if q4.dtype != k4.dtype:
+        raise FamError(1, "q and k must share a dtype")
+    if q4.stride(3) != 1 or k4.stride(3) != 1:
+        raise FamError(1, "the head dimension must be contiguous")
+    B, Hq, S, d = q4.shape
+    if k4.shape[0] != B or k4.shape[2] != S or k4.shape[3] != d:
+        raise FamError(1, f"k shape {tuple(k4.shape)} does not match q {tuple(q4.shape)}")
+    Hkv = k4.shape[1]
+    return q4, k4, B, Hq, Hkv, S, d
+
+
+def fam_lse(q: torch.Tensor, k: torch.Tensor, scale: Optional[float] = None,
+            lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+    q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
+    _check(load().fam_lse(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv, S, d,
+                          *q4.stride()[:3], *k4.stride()[:3], 0.0 if scale is None else scale,
+                          lse.data_ptr(), _stream(q4)))
+    return lse if q.dim() == 4 else lse[0]
+
+
+def fam_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
+             scale: Optional[float] = None, mass: Optional[torch.Tensor] = None) -> torch.Tensor:
+    q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
+    lse = lse.contiguous()
+    if lse.numel() != B * Hq * S or lse.dtype != torch.float32:
+        raise FamError(1, "lse must be fp32 [B, Hq, S]")
+    if mass is None:
+        mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
+    _check(load().fam_mass(q4.data_ptr(), k4.data_ptr(), lse.data_ptr(), _dtype_code(q4), B, Hq,
+                           Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
+                           0.0 if scale is None else scale, mass.data_ptr(), _stream(q4)))
+    return mass if q.dim() == 4 else mass[0]
+
+
+def fam_compute(q: torch.Tensor, k: torch.Tensor, W: int, scale: Optional[float] = None,
+                lse: Optional[torch.Tensor] = None, mass: Optional[torch.Tensor] = None
+                ) -> Tuple[torch.Tensor, torch.Tensor]:
+    q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
+    if lse is None:
+        lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
+    if mass is None:
+        mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
+    _check(load().fam_compute(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv, S, d,
+                              *q4.stride()[:3], *k4.stride()[:3], int(W),
+                              0.0 if scale is None else scale, lse.data_ptr(), mass.data_ptr(),
+                              _stream(q4)))
+    if q.dim() == 3:
+        return lse.view(Hq, S), mass.view(Hkv, S)
+    return lse, mass
+
+
+def _i64_array(values: Sequence[int]) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(values, dtype=np.int64))
+
+
+def evict_plan(budgets: Sequence[int], S: int, sinks: int, recent: int
+               ) -> Tuple[np.ndarray, np.ndarray]:
+    b = _i64_array(budgets)
+    H = b.size
+    kept = np.empty(H, dtype=np.int64)
+    offsets = np.empty(H + 1, dtype=np.int64)
+    _check(load().evict_plan(H, int(S), b.ctypes.data, int(sinks), int(recent),
+                             kept.ctypes.data, offsets.ctypes.data))
+    return kept, offsets
+
+
+def fam_budgets_from_ratios(ratios: Sequence[float], t: int) -> np.ndarray:
+    r = np.ascontiguousarray(np.asarray(ratios, dtype=np.float64))
+    out = np.empty(r.size, dtype=np.int64)
+    _check(load().fam_budgets_from_ratios(r.size, r.ctypes.data, int(t), out.ctypes.data))
+    return out
+
+
+def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,
+                 idx: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None
+                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise FamError(1, "scores must be a device fp32 [H, S] tensor")
+    if scores.stride(1) != 1:
+        raise FamError(1, "scores rows must be contiguous")
+    H, S = scores.shape
+    b = _i64_array(budgets)
+    if b.size != H:
+        raise FamError(1, f"{b.size} budgets for {H} heads")
+    _, host_off = evict_plan(b, S, sinks, recent)
+    total = int(host_off[-1])
+    if idx is None:
+        idx = torch.empty(total, dtype=torch.int32, device=scores.device)
+    if offsets is None:
+        offsets = torch.empty(H + 1, dtype=torch.int64, device=scores.device)
+    _check(load().evict_select(scores.data_ptr(), scores.stride(0), H, S, b.ctypes.data,
+                               int(sinks), int(recent), idx.data_ptr(), offsets.data_ptr(),
+                               _stream(scores)))
+    return idx, offsets
+
+
+def kv_compact(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, offsets: torch.Tensor,
+               total_rows: Optional[int] = None, k_new: Optional[torch.Tensor] = None,
+               v_new: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    if k.dim() != 3 or v.shape != k.shape or k.dtype != v.dtype:
+        raise FamError(1, "k and v must be [H, S, d] tensors of one dtype and shape")
+    if k.element_size() != 2 or k.stride(2) != 1 or v.stride(2) != 1:
+        raise FamError(1, "k and v need 2-byte elements with a contiguous last axis")
+    H, S, d = k.shape
+    rows = int(idx.numel()) if total_rows is None else int(total_rows)
+    if k_new is None:
+        k_new = torch.empty((rows, d), dtype=k.dtype, device=k.device)
+    if v_new is None:
+        v_new = torch.empty((rows, d), dtype=v.dtype, device=v.device)
+    _check(load().kv_compact(k.data_ptr(), v.data_ptr(), 2, H, S, d, k.stride(0), k.stride(1),
+                             v.stride(0), v.stride(1), idx.data_ptr(), offsets.data_ptr(), rows,
+                             k_new.data_ptr(), v_new.data_ptr(), _stream(k)))
+    return k_new, v_new

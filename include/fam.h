@@ -1,0 +1,210 @@
+/*
+ * fam.h -- future-attention mass and budgeted KV-cache eviction on gfx950.
+ *
+ * C ABI of libfam.so. Every entry point takes plain pointers and sizes.
+ * Device pointers are HIP device memory on the current device; `stream` is a
+ * hipStream_t passed as void* (NULL means the default stream).
+ *
+ * Conventions shared by every entry point
+ *   - Strides are in elements. The last (head-dim) axis is contiguous.
+ *   - The library never allocates or frees device memory and keeps no state
+ *     between calls, apart from loaded code objects and a thread-local error
+ *     string. The caller owns every buffer.
+ *   - Device entry points only enqueue work on `stream` and return; they never
+ *     synchronise. Outputs are valid once the caller has synchronised the
+ *     stream.
+ *   - All arguments are validated before anything is launched. On failure an
+ *     entry point returns a non-zero fam_status, launches nothing and leaves
+ *     every output untouched; fam_last_error() then describes the failure.
+ *   - No C++ exception and no abort crosses this boundary.
+ *
+ * Sources (titles and sections of the pages this library implements)
+ *   [KVpop]  "KVpop - Key-Value Cache Compression with Predictive Online
+ *            Pruning" (paperglide summary)
+ *   [KVP]    "Learning to Evict from Key-Value Cache" (paperlayer summary)
+ *   [LKV]    "LKV: End-to-End Learning of Head-wise Budgets and Token
+ *            Selection for LLM KV Cache Eviction" (picx summary)
+ *   [Blog]   "How much KV cache can you prune before quality degrades?"
+ *            (bilalrana.com)
+ */
+#ifndef FAM_H
+#define FAM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FAM_OK = 0,
+  FAM_ERR_INVALID_ARG = 1, /* a size, stride, pointer or budget is invalid   */
+  FAM_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype...) */
+  FAM_ERR_WORKSPACE = 3,   /* reserved                                       */
+  FAM_ERR_HIP = 4          /* the HIP runtime reported an error at launch    */
+} fam_status;
+
+typedef enum {
+  FAM_BF16 = 0, /* bfloat16 */
+  FAM_FP16 = 1  /* IEEE binary16 */
+} fam_dtype;
+
+/* Human-readable name of a status code (static storage). */
+const char* fam_status_string(fam_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). The pointer
+ * stays valid until the next call into the library on this thread. */
+const char* fam_last_error(void);
+
+/* ------------------------------------------------------------------------
+ * fam_lse -- causal row log-sum-exp (first pass).
+ *
+ * [KVpop] "Delayed Memory Scoring": the normaliser of query i is the log of
+ * the sum of exp(logit) over the keys it may attend to; under causal masking
+ * these are keys j <= i, the query's own position included.
+ *
+ *   lse[b, qh, i] = log( sum_{j <= i} exp(scale * <q[b,qh,i,:], k[b,qh/g,j,:]>) )
+ *
+ * natural log, fp32, with g = Hq / Hkv (query head qh reads KV head qh / g).
+ *
+ *   q      device, [B, Hq, S, d] of `dtype`, strides (q_sb, q_sh, q_ss)
+ *   k      device, [B, Hkv, S, d] of `dtype`, strides (k_sb, k_sh, k_ss)
+ *   scale  softmax scale; a value <= 0 selects 1/sqrt(d)
+ *   lse    device out, [B, Hq, S] fp32, contiguous, fully overwritten
+ *
+ * Requirements: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; d in {64, 128};
+ * q and k 16-byte aligned with row strides (q_ss, k_ss) multiples of 8
+ * elements; every stride >= 0 and the tensors addressable with them.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (d, dtype), FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_lse(const void* q, const void* k, fam_dtype dtype,
+                   int B, int Hq, int Hkv, int S, int d,
+                   int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                   int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                   float scale, float* lse, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fam_mass -- per-KV-head future-attention mass (second, key-major pass).
+ *
+ * [KVpop] "Defining Future Attention Utility" and Figure 2 ("Transposed
+ * Attention"): the utility of key j is the attention it receives from queries
+ * that arrive after it has left the protected window of W recent tokens,
+ * i.e. from queries i >= j + W; transposing queries and keys turns that
+ * column sum into a row sum. [KVpop] "Delayed Memory Scoring" and the
+ * appendix on the transposed pass: subtract each query's normaliser from its
+ * logits. The query heads of a GQA group are summed.
+ *
+ *   mass[b, h, j] = sum_{qh : qh / g == h} sum_{i = j + W}^{S - 1}
+ *                   exp(scale * <q[b,qh,i,:], k[b,h,j,:]> - lse[b,qh,i])
+ *
+ * Keys j > S - 1 - W get exactly 0. No S x S map is formed.
+ *
+ *   lse    device, [B, Hq, S] fp32 contiguous (normally fam_lse's output)
+ *   W      protected recent window, W >= 0 (W >= S makes every mass 0)
+ *   mass   device out, [B, Hkv, S] fp32, contiguous, fully overwritten
+ *   other arguments and requirements as for fam_lse.
+ * ---------------------------------------------------------------------- */
+fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype,
+                    int B, int Hq, int Hkv, int S, int d,
+                    int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                    int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                    int W, float scale, float* mass, void* stream);
+
+/* fam_compute -- fam_lse followed by fam_mass on the same stream. */
+fam_status fam_compute(const void* q, const void* k, fam_dtype dtype,
+                       int B, int Hq, int Hkv, int S, int d,
+                       int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                       int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                       int W, float scale, float* lse, float* mass, void* stream);
+
+/* ------------------------------------------------------------------------
+ * evict_plan -- host-only budget plan (no device work).
+ *
+ * [KVpop] "The KVpop Scoring Module" / Figure 1: the sinks and the recent
+ * window are always kept and the rest of the per-head budget goes to the
+ * best-scored long-range tokens; [KVP] A.2 and [Blog] "What we did" keep
+ * the first and the newest tokens the same way.
+ *
+ * The forced set is F = [0, min(sinks, S)) U [max(0, S - recent), S). A
+ * budget is the total number of rows a head keeps, forced rows included:
+ *   kept[h]    = min(S, max(budgets[h], |F|))
+ *   offsets[0] = 0, offsets[h + 1] = offsets[h] + kept[h]
+ *
+ *   budgets  host, [H] int64, each >= 0
+ *   kept     host out, [H] int64 (may be NULL)
+ *   offsets  host out, [H + 1] int64 (may be NULL)
+ * Errors: FAM_ERR_INVALID_ARG (H < 0, S < 1, sinks/recent < 0, a negative
+ * budget, budgets NULL with H > 0).
+ * ---------------------------------------------------------------------- */
+fam_status evict_plan(int H, int S, const int64_t* budgets, int sinks, int recent,
+                      int64_t* kept, int64_t* offsets);
+
+/* ------------------------------------------------------------------------
+ * fam_budgets_from_ratios -- host-only, b[h] = floor(ratios[h] * t).
+ *
+ * [LKV] "LKV-H: Learning Global Budget Allocation": a head's discrete budget
+ * at length t is the floor of its frozen retention ratio times t. The
+ * product is formed in double precision.
+ *   ratios   host, [H] double, each finite and >= 0
+ *   budgets  host out, [H] int64
+ * Errors: FAM_ERR_INVALID_ARG (negative or non-finite ratio, overflow).
+ * ---------------------------------------------------------------------- */
+fam_status fam_budgets_from_ratios(int H, const double* ratios, int64_t t, int64_t* budgets);
+
+/* ------------------------------------------------------------------------
+ * evict_select -- per-head top-k selection with forced sinks and window.
+ *
+ * [KVP] section 3: the top-b entries of a ranking form the cache and the
+ * lowest-ranked entries are evicted. [KVpop] "The KVpop Scoring Module":
+ * sinks + window + top-k of the remaining tokens. Among the candidates
+ * C = [min(sinks,S), max(min(sinks,S), S - recent)) the kept[h] - |F|
+ * best are chosen by score descending; equal scores go to the lower
+ * position; -0.0 equals +0.0; NaN ranks below every number.
+ *
+ *   scores      device, [H, S] fp32, row stride `score_row_stride` (>= S)
+ *   budgets     host, [H] int64 (as for evict_plan)
+ *   idx         device out, [offsets[H]] int32: for each head h, the kept
+ *               positions in ascending order at idx[offsets[h] ...]
+ *   offsets_dev device out, [H + 1] int64: the offsets of evict_plan
+ *
+ * Requirements: H >= 0, 1 <= S; every head's candidate count (S minus the
+ * forced rows) at most 131072. H == 0 is a no-op.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (too many candidates),
+ * FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status evict_select(const float* scores, int64_t score_row_stride, int H, int S,
+                        const int64_t* budgets, int sinks, int recent,
+                        int32_t* idx, int64_t* offsets_dev, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kv_compact -- gather kept K and V rows into a new packed cache.
+ *
+ * [KVP] section 4.1 and A.2 (physical tensor compaction) and [Blog]
+ * "What we did" (the retained entries are copied into a new cache tensor).
+ *
+ *   k_new[r, :] = k[h, idx[r], :],  v_new[r, :] = v[h, idx[r], :]
+ *   for offsets_dev[h] <= r < offsets_dev[h + 1]; a bit copy.
+ *
+ *   k, v         device, [H, S, d] of `elem_bytes`-byte elements, strides
+ *                (k_sh, k_ss) and (v_sh, v_ss) in elements
+ *   idx          device, [total_rows] int32, normally evict_select's output
+ *   offsets_dev  device, [H + 1] int64, non-decreasing, offsets_dev[0] = 0,
+ *                offsets_dev[H] = total_rows
+ *   k_new, v_new device out, [total_rows, d] contiguous
+ *
+ * Requirements: elem_bytes == 2; d * 2 a multiple of 16; k, v, k_new, v_new
+ * 16-byte aligned; row strides multiples of 8 elements. An index outside
+ * [0, S) yields a zero row instead of a read out of bounds.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S, int d,
+                      int64_t k_sh, int64_t k_ss, int64_t v_sh, int64_t v_ss,
+                      const int32_t* idx, const int64_t* offsets_dev, int64_t total_rows,
+                      void* k_new, void* v_new, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FAM_H */

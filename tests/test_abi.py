@@ -1,0 +1,128 @@
+"""CPU tests of the C-ABI boundary (no device work).
+
+* libfam.so loads and exports every function that include/fam.h declares;
+* the host-only budget plan and ratio floors match the oracle;
+* invalid arguments are rejected with the documented status before anything
+  touches the GPU (the pointers passed here are never dereferenced).
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from future_attention_scoring_amd import fam
+from oracle import select_oracle as so
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+INVALID, UNSUPPORTED = 1, 2
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "fam.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+(\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_lists_the_binding_signatures():
+    assert header_functions() == sorted(fam.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(fam.lib_path())
+    for name in header_functions():
+        assert hasattr(lib, name), name
+    fam.load()
+
+
+def test_status_strings():
+    lib = fam.load()
+    assert lib.fam_status_string(0) == b"FAM_OK"
+    assert lib.fam_status_string(4) == b"FAM_ERR_HIP"
+
+
+@pytest.mark.parametrize("S,sinks,recent", [(100, 4, 8), (10, 4, 20), (5, 0, 0), (1, 1, 1), (300, 0, 32)])
+def test_plan_matches_oracle(S, sinks, recent):
+    budgets = [0, 3, 12, 50, 99, 100, 101, 5000]
+    kept, off = fam.evict_plan(budgets, S, sinks, recent)
+    k_ref, off_ref = so.plan(budgets, S, sinks, recent)
+    assert kept.tolist() == k_ref.tolist()
+    assert off.tolist() == off_ref.tolist()
+
+
+def test_budgets_from_ratios_matches_oracle():
+    r = np.random.default_rng(0).dirichlet(np.ones(8)) * 8 * 0.15
+    assert fam.fam_budgets_from_ratios(r, 131072).tolist() == so.budgets_from_ratios(r, 131072).tolist()
+    with pytest.raises(fam.FamError) as e:
+        fam.fam_budgets_from_ratios([0.1, -0.2], 100)
+    assert e.value.status == INVALID
+
+
+def test_plan_rejects_bad_arguments():
+    with pytest.raises(fam.FamError) as e:
+        fam.evict_plan([1, -1], 10, 0, 0)
+    assert e.value.status == INVALID
+    with pytest.raises(fam.FamError):
+        fam.evict_plan([1], 0, 0, 0)
+    with pytest.raises(fam.FamError):
+        fam.evict_plan([1], 10, -1, 0)
+
+
+FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation first
+
+
+def lse_call(**over):
+    a = dict(q=FAKE, k=FAKE, dtype=0, B=1, Hq=4, Hkv=2, S=64, d=128, q_sb=0, q_sh=64 * 128,
+             q_ss=128, k_sb=0, k_sh=64 * 128, k_ss=128, scale=0.0, lse=FAKE, stream=None)
+    a.update(over)
+    return fam.load().fam_lse(*a.values())
+
+
+@pytest.mark.parametrize("over,status", [
+    (dict(Hq=3), INVALID), (dict(d=96), UNSUPPORTED), (dict(dtype=7), UNSUPPORTED),
+    (dict(S=0), INVALID), (dict(q=FAKE + 2), INVALID), (dict(q_ss=130), INVALID),
+    (dict(k_sh=-8), INVALID), (dict(lse=None), INVALID), (dict(q=None), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(S=(1 << 28) + 1), UNSUPPORTED),
+])
+def test_fam_lse_validation(over, status):
+    assert lse_call(**over) == status
+    assert fam.load().fam_last_error() != b""
+
+
+def test_fam_mass_and_compute_validation():
+    lib = fam.load()
+    st = lib.fam_mass(FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, -1, 0.0, FAKE, None)
+    assert st == INVALID
+    st = lib.fam_compute(FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE, None, None)
+    assert st == INVALID
+
+
+def test_evict_select_validation():
+    lib = fam.load()
+    b = np.array([10, -1], dtype=np.int64)
+    assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, None) == INVALID
+    b = np.array([10, 10], dtype=np.int64)
+    assert lib.evict_select(FAKE, 99, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, None) == INVALID
+    assert lib.evict_select(FAKE, 200000, 2, 200000, b.ctypes.data, 4, 4, FAKE, FAKE, None) == UNSUPPORTED
+    assert lib.evict_select(FAKE, 100, 0, 100, None, 4, 4, FAKE, FAKE, None) == 0  # H == 0: no-op
+
+
+def test_kv_compact_validation():
+    lib = fam.load()
+    args = [FAKE, FAKE, 2, 2, 100, 128, 12800, 128, 12800, 128, FAKE, FAKE, 10, FAKE, FAKE, None]
+    bad = list(args)
+    bad[2] = 4
+    assert lib.kv_compact(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[5] = 72
+    assert lib.kv_compact(*bad) == UNSUPPORTED
+    bad = list(args)
+    bad[13] = FAKE + 4
+    assert lib.kv_compact(*bad) == INVALID
+    bad = list(args)
+    bad[7] = 132
+    assert lib.kv_compact(*bad) == INVALID
+    bad = list(args)
+    bad[12] = 0
+    assert lib.kv_compact(*bad) == 0  # nothing to copy

@@ -1,0 +1,241 @@
+"""GPU parity of fam_lse / fam_mass / fam_compute against the fp64 oracle.
+
+Tolerances (from the method's stated bar): |lse_gpu - lse_ref| <= 1e-3, and
+|mass_gpu - mass_ref| / mass_ref <= 2e-3 on every key with mass_ref > 0; keys
+that no query can reach (j > S - 1 - W) must be exactly 0. The GPU reads bf16
+(or fp16) inputs and the oracle reads the same values converted exactly to
+fp64.
+
+Sizes the oracle finishes in seconds are compared element by element; at the
+32k and 128k workloads the oracle computes sampled rows and the keys whose
+future queries lie in the last rows, and properties that hold at any size
+(the W = 0 column-sum invariant, the uniform and single-sink closed forms)
+are checked on every output.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from future_attention_scoring_amd import fam, workloads
+from oracle import fam_oracle as fo
+
+pytestmark = pytest.mark.gpu
+
+LSE_TOL = 1e-3
+MASS_RTOL = 2e-3
+DEV = "cuda:0"
+
+
+def say(msg):
+    print(f"\n[case] {msg}", flush=True)
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().cpu().to(torch.float64).numpy()
+
+
+def check_lse(got, ref):
+    err = np.abs(np.asarray(got, np.float64) - ref).max()
+    assert err <= LSE_TOL, f"lse max abs err {err}"
+    return err
+
+
+def check_mass(got, ref, S, W):
+    got = np.asarray(got, np.float64)
+    if W < S:
+        assert np.all(got[..., S - W:] == 0.0), "unreachable keys must be exactly 0"
+    else:
+        assert np.all(got == 0.0)
+    pos = ref > 0
+    if pos.any():
+        rel = np.abs(got[pos] - ref[pos]) / np.maximum(ref[pos], np.finfo(np.float32).tiny)
+        assert rel.max() <= MASS_RTOL, f"mass max rel err {rel.max()}"
+        return rel.max()
+    return 0.0
+
+
+def rand_inputs(seed, B, Hq, Hkv, S, d, dtype, spread=1.0):
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(B, Hq, S, d, generator=g) * spread).to(dtype)
+    k = (torch.randn(B, Hkv, S, d, generator=g) * spread).to(dtype)
+    return q, k
+
+
+SMALL = [
+    # (seed, B, Hq, Hkv, S, d, W, dtype)
+    (1, 1, 4, 1, 1, 128, 0, torch.bfloat16),
+    (2, 1, 4, 2, 7, 64, 3, torch.bfloat16),
+    (3, 2, 8, 2, 100, 128, 10, torch.bfloat16),
+    (4, 1, 4, 4, 333, 64, 0, torch.bfloat16),
+    (5, 1, 8, 1, 1000, 128, 64, torch.bfloat16),
+    (6, 1, 2, 1, 257, 128, 300, torch.bfloat16),
+    (7, 1, 4, 2, 640, 128, 31, torch.float16),
+    (8, 1, 3, 3, 129, 64, 1, torch.bfloat16),
+    (9, 1, 6, 2, 200, 128, 5, torch.bfloat16),
+    (10, 1, 16, 2, 300, 64, 7, torch.bfloat16),
+    (11, 1, 4, 1, 1537, 128, 513, torch.bfloat16),
+    (12, 1, 2, 2, 2048, 64, 2047, torch.float16),
+]
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,S,d,W,dtype", SMALL)
+def test_small_and_ragged_against_full_oracle(seed, B, Hq, Hkv, S, d, W, dtype):
+    say(f"small seed={seed} B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} W={W} {dtype}")
+    q, k = rand_inputs(seed, B, Hq, Hkv, S, d, dtype, spread=1.3)
+    lse, mass = fam.fam_compute(q.to(DEV), k.to(DEV), W)
+    torch.cuda.synchronize()
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), W)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, S, W)
+
+
+def test_explicit_scale_and_strided_views():
+    say("explicit scale, non-contiguous head stride")
+    S, d = 384, 128
+    base = torch.randn(1, 8, S, d, generator=torch.Generator().manual_seed(3)).to(torch.bfloat16)
+    q = base[:, ::2]                       # head stride 2*S*d
+    k = torch.randn(1, 2, S, d, generator=torch.Generator().manual_seed(4)).to(torch.bfloat16)
+    lse, mass = fam.fam_compute(q.to(DEV), k.to(DEV), 16, scale=0.05)
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), 16, scale=0.05)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, S, 16)
+
+
+def test_tiny_workload_full_oracle():
+    wl = workloads.tiny()
+    say(wl.name)
+    t = wl.tensors(with_v=False)
+    lse, mass = fam.fam_compute(t["q"].to(DEV), t["k"].to(DEV), wl.W)
+    lse_ref, mass_ref = fo.fam(to64(t["q"]), to64(t["k"]), wl.W)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, wl.S, wl.W)
+
+
+def test_qwen3_4b_layer_two_groups_full_oracle():
+    wl = workloads.qwen3_4b_layer()
+    say(wl.name)
+    t = wl.tensors(with_v=False)
+    lse, mass = fam.fam_compute(t["q"].to(DEV), t["k"].to(DEV), wl.W)
+    lse, mass = lse.cpu().numpy()[0], mass.cpu().numpy()[0]
+    g = wl.group
+    for h in (0, wl.Hkv - 1):
+        qg = to64(t["q"][0, h * g:(h + 1) * g])
+        kh = to64(t["k"][0, h:h + 1])
+        lse_ref, mass_ref = fo.fam(qg, kh, wl.W)
+        check_lse(lse[h * g:(h + 1) * g], lse_ref)
+        check_mass(mass[h:h + 1], mass_ref, wl.S, wl.W)
+
+
+def sampled_checks(wl, t, lse, mass, group, n_rows=24, tail=768):
+    """Oracle on sampled LSE rows and on the keys whose queries are all in the tail."""
+    g, S, W = wl.group, wl.S, wl.W
+    rng = np.random.default_rng(wl.seed)
+    qg = to64(t["q"][0, group * g:(group + 1) * g])
+    kh = to64(t["k"][0, group])
+    scale = 1.0 / math.sqrt(wl.d)
+    rows = np.unique(np.concatenate([rng.integers(0, S, n_rows), [0, 1, S - 1]]))
+    for n in range(g):
+        ref = fo.causal_lse_rows(qg[n], kh, rows, scale)
+        check_lse(lse[group * g + n, rows], ref)
+    tail_start = S - tail
+    lse_tail = np.stack([fo.causal_lse_rows(qg[n], kh, np.arange(tail_start, S), scale) for n in range(g)])
+    keys = np.arange(max(0, tail_start - W), S)
+    ref = fo.future_mass_keys(qg, kh, lse_tail, tail_start, keys, W, scale)
+    got = mass[group, keys]
+    full = np.zeros(S)
+    full[keys] = ref
+    gfull = np.zeros(S)
+    gfull[keys] = got
+    check_mass(gfull[None], full[None], S, W)
+
+
+def test_long_trace_sampled():
+    wl = workloads.long_trace()
+    say(wl.name)
+    t = wl.tensors(q_heads=range(wl.Hq), kv_heads=range(wl.Hkv), with_v=False)
+    lse, mass = fam.fam_compute(t["q"].to(DEV), t["k"].to(DEV), wl.W)
+    lse, mass = lse.cpu().numpy()[0], mass.cpu().numpy()[0]
+    sampled_checks(wl, t, lse, mass, group=3)
+
+
+def test_llama_128k_sampled():
+    wl = workloads.llama31_8b_128k()
+    say(wl.name)
+    t = wl.tensors(with_v=False)
+    lse, mass = fam.fam_compute(t["q"].to(DEV), t["k"].to(DEV), wl.W)
+    lse, mass = lse.cpu().numpy()[0], mass.cpu().numpy()[0]
+    sampled_checks(wl, t, lse, mass, group=5, n_rows=8, tail=640)
+
+
+@pytest.mark.parametrize("S,Hq,Hkv,d", [(8192, 32, 8, 128), (131072, 32, 8, 128), (5000, 6, 2, 64)])
+def test_w0_invariant_full_size(S, Hq, Hkv, d):
+    say(f"W=0 invariant S={S} Hq={Hq} Hkv={Hkv} d={d}")
+    gen = torch.Generator(device=DEV).manual_seed(S)
+    q = torch.randn(1, Hq, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    k = torch.randn(1, Hkv, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    _, mass = fam.fam_compute(q, k, 0)
+    tot = mass.double().sum(dim=-1).cpu().numpy()[0]
+    g = Hq // Hkv
+    np.testing.assert_allclose(tot, np.full(Hkv, S * g), rtol=1e-4)
+
+
+def harmonic_prefix(n):
+    return np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1, dtype=np.float64))])
+
+
+@pytest.mark.parametrize("S,W", [(131072, 512), (32768, 256), (3000, 0)])
+def test_uniform_logits_closed_form_full_size(S, W):
+    say(f"uniform closed form S={S} W={W}")
+    Hq, Hkv, d = 8, 2, 128
+    q = torch.zeros(1, Hq, S, d, device=DEV, dtype=torch.bfloat16)
+    k = torch.randn(1, Hkv, S, d, device=DEV, generator=torch.Generator(device=DEV).manual_seed(1)).to(torch.bfloat16)
+    lse, mass = fam.fam_compute(q, k, W)
+    Hn = harmonic_prefix(S)
+    lse_ref = np.log(np.arange(1, S + 1, dtype=np.float64))
+    check_lse(lse.cpu().numpy()[0], lse_ref[None, :])
+    j = np.arange(S)
+    ref = np.where(j <= S - 1 - W, (Hq // Hkv) * (Hn[S] - Hn[np.minimum(j + W, S)]), 0.0)
+    check_mass(mass.cpu().numpy()[0], np.broadcast_to(ref, (Hkv, S)), S, W)
+
+
+@pytest.mark.parametrize("S,W,a,b", [(65536, 100, 4.0, 4.0), (777, 3, 8.0, 2.0)])
+def test_single_sink_closed_form(S, W, a, b):
+    say(f"single sink S={S} W={W}")
+    Hq, Hkv, d = 4, 1, 128
+    q = torch.zeros(1, Hq, S, d, dtype=torch.bfloat16)
+    q[..., 0] = a
+    k = torch.zeros(1, Hkv, S, d, dtype=torch.bfloat16)
+    k[0, 0, 0, 0] = b
+    lse, mass = fam.fam_compute(q.to(DEV), k.to(DEV), W)
+    c = a * b / math.sqrt(d)
+    ec = math.exp(c)
+    i = np.arange(S, dtype=np.float64)
+    check_lse(lse.cpu().numpy()[0], np.log(ec + i)[None, :])
+    inv = 1.0 / (ec + i)
+    suffix = np.concatenate([np.cumsum(inv[::-1])[::-1], [0.0]])  # suffix[m] = sum_{i>=m} inv
+    ref = np.zeros(S)
+    ref[0] = Hq * ec * suffix[min(W, S)]
+    jj = np.arange(1, S)
+    ref[1:] = Hq * suffix[np.minimum(jj + W, S)]
+    check_mass(mass.cpu().numpy()[0], ref[None, :], S, W)
+
+
+def test_deterministic_bitwise():
+    say("determinism")
+    q, k = rand_inputs(21, 1, 8, 2, 4099, 128, torch.bfloat16)
+    q, k = q.to(DEV), k.to(DEV)
+    a = fam.fam_compute(q, k, 64)
+    b = fam.fam_compute(q, k, 64)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_separate_passes_match_compute():
+    say("fam_lse + fam_mass == fam_compute")
+    q, k = rand_inputs(22, 1, 4, 1, 999, 64, torch.bfloat16)
+    q, k = q.to(DEV), k.to(DEV)
+    lse = fam.fam_lse(q, k)
+    mass = fam.fam_mass(q, k, lse, 17)
+    lse2, mass2 = fam.fam_compute(q, k, 17)
+    assert torch.equal(lse, lse2) and torch.equal(mass, mass2)
