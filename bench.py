@@ -1,0 +1,198 @@
+"""Benchmark of the future-attention-mass + eviction hot path on one MI355X.
+
+One step = fam_lse + fam_mass (the two-pass future-attention mass) +
+evict_select (per-head budgets b_h = floor(r_h * S), 4 sinks, recent window)
++ kv_compact (gather of the kept K/V rows), on the Llama-3.1-8B-like layer at
+128k tokens (32 query / 8 KV heads, d = 128, bf16, W = 512). Inputs are
+seeded synthetic tensors, resident in HBM before timing starts.
+
+Prints one JSON line. `value` is causal key-query pairs per second of the
+whole step; `roofline` describes the slowest kernel (algorithmic work per
+launch over its mean HIP-event duration); `cpu_baseline` times the fp64
+oracle on a bounded sample of the same workload.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                       [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+from future_attention_scoring_amd import fam, workloads
+
+PEAK_BF16_FLOPS = 2.5e15     # MI355X dense bf16 MFMA (published)
+PEAK_HBM_BYTES = 8.0e12      # MI355X HBM3E (published)
+WORKLOADS = {
+    "llama-128k": workloads.llama31_8b_128k,
+    "qwen3-4b-8k": workloads.qwen3_4b_layer,
+    "long-trace-32k": workloads.long_trace,
+}
+
+
+def algorithmic_work(wl, kept_total):
+    """Counts the bench divides by (per launch)."""
+    S, W, Hq, Hkv, d = wl.S, wl.W, wl.Hq, wl.Hkv, wl.d
+    causal_pairs = Hq * S * (S + 1) // 2
+    future_pairs = Hq * (S - W) * (S - W + 1) // 2 if W < S else 0
+    esize = 2
+    return {
+        "causal_pairs": causal_pairs,
+        "lse_flops": 2 * d * causal_pairs,
+        "mass_flops": 2 * d * future_pairs,
+        "select_bytes": 4 * Hkv * S + 4 * kept_total,
+        "compact_bytes": 2 * 2 * kept_total * d * esize,
+    }
+
+
+def cpu_baseline(wl, prefix=32768):
+    """Time the fp64 oracle on the first `prefix` positions of KV group 0."""
+    from oracle import fam_oracle  # test infrastructure: only this leg uses it
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    g = wl.group
+    q = wl.q_heads(range(g))[:, :prefix].astype(np.float32)
+    k = wl.k_heads([0])[:, :prefix].astype(np.float32)
+    q64 = workloads.to_dtype(q, wl.dtype).to(torch.float64).numpy()
+    k64 = workloads.to_dtype(k, wl.dtype).to(torch.float64).numpy()
+    t0 = time.perf_counter()
+    fam_oracle.fam(q64, k64, wl.W)
+    dt = time.perf_counter() - t0
+    pairs = g * prefix * (prefix + 1) // 2
+    return {"value": pairs / dt, "unit": "pairs/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": (f"oracle LSE + mass (fp64) on the first {prefix} positions of KV group 0 "
+                       f"({g} query heads) of {wl.name}; {pairs} causal pairs")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="llama-128k", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by KV head with no exchange; see the design notes)", file=sys.stderr)
+        sys.exit(2)
+
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
+    wl = WORKLOADS[args.workload]()
+    t = wl.tensors()
+    q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
+    del t
+    bi = wl.budget_inputs()
+    budgets = (fam.fam_budgets_from_ratios(bi["ratios"], bi["t"]).tolist() if "ratios" in bi
+               else [bi["uniform"]] * wl.Hkv)
+    kept, offsets_host = fam.evict_plan(budgets, wl.S, wl.sinks, wl.recent)
+    total = int(offsets_host[-1])
+    B, Hq, Hkv, S, d = 1, wl.Hq, wl.Hkv, wl.S, wl.d
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    idx = torch.empty(total, dtype=torch.int32, device=dev)
+    offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=dev)
+    k_new = torch.empty((total, d), dtype=k.dtype, device=dev)
+    v_new = torch.empty((total, d), dtype=v.dtype, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        fam.fam_lse(q, k, lse=lse)
+        if events:
+            events[1].record(stream)
+        fam.fam_mass(q, k, lse, wl.W, mass=mass)
+        if events:
+            events[2].record(stream)
+        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets)
+        if events:
+            events[3].record(stream)
+        fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)
+        if events:
+            events[4].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["fam_lse", "fam_mass", "evict_select", "kv_compact"]
+    ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+          for j, n in enumerate(names)}
+    work = algorithmic_work(wl, total)
+    ms_step = wall * 1e3 / args.steps
+    t_fam = (ms["fam_lse"] + ms["fam_mass"]) * 1e-3
+    t_ec = (ms["evict_select"] + ms["kv_compact"]) * 1e-3
+    lines = {
+        "fam_lse": ("mfma", work["lse_flops"] / (ms["fam_lse"] * 1e-3), PEAK_BF16_FLOPS, "TFLOP/s"),
+        "fam_mass": ("mfma", work["mass_flops"] / (ms["fam_mass"] * 1e-3), PEAK_BF16_FLOPS, "TFLOP/s"),
+        "evict_select": ("hbm", work["select_bytes"] / (ms["evict_select"] * 1e-3), PEAK_HBM_BYTES, "GB/s"),
+        "kv_compact": ("hbm", work["compact_bytes"] / (ms["kv_compact"] * 1e-3), PEAK_HBM_BYTES, "GB/s"),
+    }
+    roof = {}
+    for n, (bound, ach, peak, unit) in lines.items():
+        scale = 1e12 if unit == "TFLOP/s" else 1e9
+        roof[n] = {"bound": bound, "achieved": round(ach / scale, 3), "peak": peak / scale,
+                   "unit": unit, "frac": round(ach / peak, 4), "traffic": None,
+                   "ms": round(ms[n], 4)}
+    dominant = max(names, key=lambda n: ms[n])
+    out = {
+        "metric": "future-attn-mass causal key-query pairs/s (+ % bf16 MFMA peak; evict+compact GB/s)",
+        "value": work["causal_pairs"] / (ms_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": 1, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
+                   "head_dim": d, "window": wl.W, "sinks": wl.sinks, "recent": wl.recent,
+                   "kept_total": total, "budgets": [int(b) for b in budgets]},
+        "fam_mfma_frac": round((work["lse_flops"] + work["mass_flops"]) / t_fam / PEAK_BF16_FLOPS, 4),
+        "fam_pairs_per_s": work["causal_pairs"] / t_fam,
+        "evict_compact_gbps": round((work["select_bytes"] + work["compact_bytes"]) / t_ec / 1e9, 2),
+        "evict_compact_hbm_frac": round((work["select_bytes"] + work["compact_bytes"]) / t_ec / PEAK_HBM_BYTES, 4),
+        "kernel_ms": {n: round(ms[n], 4) for n in names},
+        "roofline": dict(roof[dominant], kernel=dominant),
+        "roofline_all": roof,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
