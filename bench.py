@@ -151,6 +151,8 @@ def main():
     mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
     idx = torch.empty(total, dtype=torch.int32, device=dev)
     offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(16, fam.evict_select_workspace_size(Hkv, S, wl.sinks, wl.recent)),
+                     dtype=torch.uint8, device=dev)
     k_new = torch.empty((total, d), dtype=k.dtype, device=dev)
     v_new = torch.empty((total, d), dtype=v.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
@@ -166,7 +168,8 @@ def main():
         fam.fam_mass(q, k, lse, wl.W, mass=mass)
         if events:
             events[2].record(stream)
-        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets)
+        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets,
+                         workspace=ws)
         if events:
             events[3].record(stream)
         fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)

@@ -38,6 +38,7 @@ fam_status hip_status(hipError_t e, const char* what) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kMaxSeq = 1 << 28;
+constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
 struct ScoreShape {
   int B, Hq, Hkv, S, d;
@@ -62,6 +63,9 @@ fam_status check_scores(const void* q, const void* k, fam_dtype dtype, const Sco
       return fail(FAM_ERR_INVALID_ARG, "strides must be multiples of 8 elements (16 bytes)");
   }
   if (!aligned16(q) || !aligned16(k)) return fail(FAM_ERR_INVALID_ARG, "q and k must be 16-byte aligned");
+  // the kernels address a 64-row tile with 32-bit offsets
+  if (s.q_ss > kMaxRowStride || s.k_ss > kMaxRowStride)
+    return fail(FAM_ERR_UNSUPPORTED, "row strides above %lld elements", (long long)kMaxRowStride);
   return FAM_OK;
 }
 
@@ -180,9 +184,25 @@ fam_status fam_budgets_from_ratios(int H, const double* ratios, int64_t t, int64
   return ok();
 }
 
+namespace {
+int select_chunks(const Plan& p) {
+  const int a0 = p.c0 & ~3;
+  const int n = (p.c1 - a0 + fam::kSelectChunk - 1) / fam::kSelectChunk;
+  return n < 1 ? 1 : n;
+}
+int select_slots(int H) { return H < fam::kSelectBatch ? (H < 1 ? 1 : H) : fam::kSelectBatch; }
+}  // namespace
+
+size_t evict_select_workspace_size(int H, int S, int sinks, int recent) {
+  if (H < 0 || S < 1 || sinks < 0 || recent < 0) return 0;
+  const Plan p = plan_of(S, sinks, recent);
+  return fam::select_workspace_bytes(select_slots(H), select_chunks(p));
+}
+
 fam_status evict_select(const float* scores, int64_t score_row_stride, int H, int S,
                         const int64_t* budgets, int sinks, int recent, int32_t* idx,
-                        int64_t* offsets_dev, void* stream) {
+                        int64_t* offsets_dev, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   if (H < 0) return fail(FAM_ERR_INVALID_ARG, "H must be >= 0 (got %d)", H);
   if (S < 1 || S > kMaxSeq) return fail(FAM_ERR_INVALID_ARG, "S = %d out of range", S);
   if (sinks < 0 || recent < 0) return fail(FAM_ERR_INVALID_ARG, "sinks and recent must be >= 0");
@@ -196,6 +216,12 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   if (p.c1 - p.c0 > fam::kSelectMaxCandidates)
     return fail(FAM_ERR_UNSUPPORTED, "%d candidates per head exceed %d", p.c1 - p.c0,
                 fam::kSelectMaxCandidates);
+  const size_t need_ws = evict_select_workspace_size(H, S, sinks, recent);
+  if (!workspace || workspace_bytes < need_ws)
+    return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need_ws,
+                workspace ? workspace_bytes : (size_t)0);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   int64_t total = 0;
   for (int h = 0; h < H; ++h) {
     int64_t kh = budgets[h] > p.forced ? budgets[h] : p.forced;
@@ -206,11 +232,14 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   a.row_stride = score_row_stride;
   a.idx = idx;
   a.offsets_dev = offsets_dev;
+  a.ws = workspace;
   a.total = total;
   a.S = S;
   a.H = H;
   a.c0 = p.c0;
   a.c1 = p.c1;
+  a.slots = select_slots(H);
+  a.nchunk = select_chunks(p);
   int64_t off = 0;
   for (int h0 = 0; h0 < H; h0 += fam::kSelectBatch) {
     const int n = H - h0 < fam::kSelectBatch ? H - h0 : fam::kSelectBatch;

@@ -33,22 +33,27 @@ struct MassArgs {
 };
 hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s);
 
-// Per-head selection. Heads are launched in batches whose plan travels in
-// the kernel arguments.
+// Per-head selection. Heads are launched in batches of up to kSelectBatch
+// whose plan travels in the kernel arguments; each head's candidates are
+// split into chunks of kSelectChunk positions.
 constexpr int kSelectBatch = 64;
+constexpr int kSelectChunk = 4096;
 constexpr int kSelectMaxCandidates = 131072;
 struct SelectArgs {
   const float* scores;
   int64_t row_stride;
   int32_t* idx;
   int64_t* offsets_dev;
+  void* ws;            // workspace of select_workspace_bytes(slots, nchunk)
   int64_t total;       // offsets[H]
   int S, H;
   int c0, c1;          // candidates are positions [c0, c1)
   int head0, nheads;   // heads [head0, head0 + nheads) in this launch
+  int slots, nchunk;   // workspace head slots (>= nheads) and chunks per head
   int64_t out_off[kSelectBatch];
   int32_t n_choose[kSelectBatch];
 };
+size_t select_workspace_bytes(int slots, int nchunk);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 
 // Row gather of K and V into packed caches.

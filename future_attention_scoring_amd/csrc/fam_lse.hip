@@ -92,14 +92,28 @@ __global__ __launch_bounds__(kThreads, 2) void lse_kernel(LseArgs p, int npb) {
       qf[blk][ks] = ok ? load16(qbase + (int64_t)row * p.q_ss + ks * 16 + half * 8) : zero16();
   }
 
+  // staging: a uniform tile pointer plus fixed per-thread 32-bit offsets; the
+  // ragged last tile clamps its rows (keys >= S are masked in the update)
+  int off[CHUNKS];
+#pragma unroll
+  for (int c = 0; c < CHUNKS; ++c) {
+    const int id = tid + c * kThreads;
+    off[c] = (id / CPR) * (int)p.k_ss + (id % CPR) * 8;
+  }
   u32x4_t st[CHUNKS];
   auto load_tile = [&](int t) {
+    const int r0 = t * kKeyTile;
+    if (r0 + kKeyTile <= p.S) {
+      const uint16_t* tile = kbase + (int64_t)r0 * p.k_ss;
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-      const int id = tid + c * kThreads;
-      const int r = id / CPR, ch = id % CPR;
-      const int key = t * kKeyTile + r;
-      st[c] = key < p.S ? load16(kbase + (int64_t)key * p.k_ss + ch * 8) : zero16();
+      for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off[c]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < CHUNKS; ++c) {
+        const int id = tid + c * kThreads;
+        const int key = min(r0 + id / CPR, p.S - 1);
+        st[c] = load16(kbase + (int64_t)key * p.k_ss + (id % CPR) * 8);
+      }
     }
   };
   auto store_tile = [&](int buf) {

@@ -14,17 +14,20 @@
 //     operand and computes S = Q_tile * K^T, so every accumulator column is
 //     one key and the column sum over queries stays inside a lane (the two
 //     half-waves hold disjoint query rows and are added once at the end).
-//   * The workgroup walks the query tiles i >= j0 + W of every query head of
-//     the group; each (tile, head) step stages 32 query rows and their
-//     normalisers (in base-2 units) through double-buffered LDS, shared by
-//     the 4 waves.
-//   * Only band tiles (those that contain some i < j + W) evaluate the window
+//   * The workgroup walks the 64-row query tiles i >= j0 + W of every query
+//     head of the group, latest tile first, so the workgroups of one head that
+//     run at the same time read the same Q tiles (the L2 absorbs most of the
+//     re-reads). Each (tile, head) step stages 64 query rows and their
+//     normalisers (in base-2 units) through double-buffered LDS; the tile
+//     base is a uniform pointer and each thread keeps fixed 32-bit offsets.
+//   * Only band steps (those that contain some i < j + W) evaluate the window
 //     predicate. Keys that no query can reach (j > S - 1 - W) get exactly 0.
 //   * Per-step partial sums are added into a mid-level accumulator that is
-//     folded into the total every 16 steps, which bounds the fp32 summation
+//     folded into the total every 8 steps, which bounds the fp32 summation
 //     error independently of S.
 //   * Workgroups are numbered earliest-key-first (the longest columns start
-//     first) with the (batch, KV head) index fastest.
+//     first) with the (batch, KV head) index fastest, so with eight KV heads
+//     every XCD works on one head.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -35,31 +38,36 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWG = kKeysPerWave * kWaves;
-constexpr int kQTile = 32;
+constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
 
-// Adds the terms of one 32x32 (query x key) block into `mid`.
-__device__ __forceinline__ void accumulate(f32x16_t acc, const float (&lv)[16], int i0, int jk,
-                                           int W, int lane, float c, float& mid) {
-  if (i0 + 31 < jk + W) return;                    // no query of the tile counts
+// Sum of exp2(c*s - L) over one 32x32 block, no window predicate.
+__device__ __forceinline__ float block_sum_full(const f32x16_t& acc, const float (&lv)[16], float c) {
   float e[16];
 #pragma unroll
   for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -lv[v]));
-  if (i0 < jk + 31 + W) {                          // band tile: window predicate
-    const int j = jk + (lane & 31);
+  return sum16(e);
+}
+
+// Same with the window predicate i >= j + W.
+__device__ __forceinline__ float block_sum_band(const f32x16_t& acc, const float (&lv)[16], int i0,
+                                                int jk, int W, int lane, float c) {
+  if (i0 + 31 < jk + W) return 0.f;
+  float e[16];
+  const int j = jk + (lane & 31);
 #pragma unroll
-    for (int v = 0; v < 16; ++v)
-      if (i0 + acc_row(v, lane) < j + W) e[v] = 0.f;
+  for (int v = 0; v < 16; ++v) {
+    const float x = fast_exp2(fmaf(acc[v], c, -lv[v]));
+    e[v] = i0 + acc_row(v, lane) < j + W ? 0.f : x;
   }
-  mid += sum16(e);
+  return sum16(e);
 }
 
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads, 2) void mass_kernel(MassArgs p) {
+__global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   constexpr int PITCH = D + 8;
   constexpr int KS = D / 16;
   constexpr int CPR = D / 8;
   constexpr int CHUNKS = kQTile * CPR / kThreads;
-  static_assert(CHUNKS >= 1, "tile too small for the workgroup");
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][kQTile * PITCH];
   __shared__ __attribute__((aligned(16))) float sl[2][kQTile];
 
@@ -87,36 +95,55 @@ __global__ __launch_bounds__(kThreads, 2) void mass_kernel(MassArgs p) {
   float top[2] = {0.f, 0.f}, mid[2] = {0.f, 0.f};
   const int i_first = j0 + p.W;
   if (i_first < p.S) {
+    const int g = p.g;
     const int t0 = i_first / kQTile;
     const int t1 = (p.S + kQTile - 1) / kQTile;
-    const int nsteps = (t1 - t0) * p.g;
+    const int nsteps = (t1 - t0) * g;
+    // tiles t >= t_full have every row i >= j0 + 255 + W: no predicate needed
+    const int t_full = (j0 + kKeysPerWG - 1 + p.W + kQTile - 1) / kQTile;
+    const int nfull = max(0, t1 - max(t_full, t0)) * g;
 
+    // per-thread staging offsets (elements) inside a tile, fixed for the whole loop
+    // (the host guarantees kQTile * q_ss < 2^31, so tile offsets fit in 32 bits)
+    int off[CHUNKS];
+#pragma unroll
+    for (int c = 0; c < CHUNKS; ++c) {
+      const int id = tid + c * kThreads;
+      off[c] = (id / CPR) * (int)p.q_ss + (id % CPR) * 8;
+    }
+    const uint16_t* qgroup = p.q + b * p.q_sb + (int64_t)(h * g) * p.q_sh;
+    const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.S;
     u32x4_t st[CHUNKS];
     float lst = 0.f;
     auto load_step = [&](int u) {
-      const int t = t0 + u / p.g;
-      const int qh = h * p.g + u % p.g;
-      const uint16_t* qbase = p.q + b * p.q_sb + qh * p.q_sh;
+      const int t = t1 - 1 - u / g;
+      const int gi = u % g;
+      const int r0 = t * kQTile;
+      const uint16_t* tile = qgroup + gi * p.q_sh + (int64_t)r0 * p.q_ss;   // uniform
+      if (r0 + kQTile <= p.S) {
 #pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int id = tid + c * kThreads;
-        const int r = id / CPR, ch = id % CPR;
-        const int row = t * kQTile + r;
-        st[c] = row < p.S ? load16(qbase + (int64_t)row * p.q_ss + ch * 8) : zero16();
+        for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off[c]);
+      } else {  // ragged last tile: clamp rows (their normaliser is +inf)
+#pragma unroll
+        for (int c = 0; c < CHUNKS; ++c) {
+          const int id = tid + c * kThreads;
+          const int row = min(r0 + id / CPR, p.S - 1);
+          st[c] = load16(qgroup + gi * p.q_sh + (int64_t)row * p.q_ss + (id % CPR) * 8);
+        }
       }
       if (tid < kQTile) {
-        const int row = t * kQTile + tid;
-        lst = row < p.S ? p.lse[((int64_t)b * p.Hq + qh) * p.S + row] * kLog2e : kInf;
+        const int row = r0 + tid;
+        const float x = lgroup[(int64_t)gi * p.S + min(row, p.S - 1)];
+        lst = row < p.S ? x : kInf;
       }
     };
     auto store_step = [&](int buf) {
 #pragma unroll
       for (int c = 0; c < CHUNKS; ++c) {
         const int id = tid + c * kThreads;
-        const int r = id / CPR, ch = id % CPR;
-        store16(&sq[buf][r * PITCH + ch * 8], st[c]);
+        store16(&sq[buf][(id / CPR) * PITCH + (id % CPR) * 8], st[c]);
       }
-      if (tid < kQTile) sl[buf][tid] = lst;
+      if (tid < kQTile) sl[buf][tid] = lst * kLog2e;
     };
 
     load_step(0);
@@ -126,29 +153,38 @@ __global__ __launch_bounds__(kThreads, 2) void mass_kernel(MassArgs p) {
       const bool more = u + 1 < nsteps;
       if (more) load_step(u + 1);
       const int buf = u & 1;
-      const int i0 = (t0 + u / p.g) * kQTile;
-      if (i0 + 31 >= jw + p.W) {                   // wave-uniform: some pair counts
-        float lv[16];
+      const int i0t = (t1 - 1 - u / g) * kQTile;
+      const bool full = u < nfull;
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sl[buf][8 * r4 + 4 * half]);
-          lv[4 * r4 + 0] = x[0];
-          lv[4 * r4 + 1] = x[1];
-          lv[4 * r4 + 2] = x[2];
-          lv[4 * r4 + 3] = x[3];
-        }
-        f32x16_t acc0 = {}, acc1 = {};
+      for (int rb = 0; rb < kQTile / 32; ++rb) {
+        const int i0 = i0t + 32 * rb;
+        if (full || i0 + 31 >= jw + p.W) {
+          float lv[16];
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-          const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-              &sq[buf][col * PITCH + ks * 16 + half * 8]);
-          acc0 = Mma<T>::run(a, kf[0][ks], acc0);
-          acc1 = Mma<T>::run(a, kf[1][ks], acc1);
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sl[buf][32 * rb + 8 * r4 + 4 * half]);
+            lv[4 * r4 + 0] = x[0];
+            lv[4 * r4 + 1] = x[1];
+            lv[4 * r4 + 2] = x[2];
+            lv[4 * r4 + 3] = x[3];
+          }
+          f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&sq[buf][(32 * rb + col) * PITCH + ks * 16 + half * 8]);
+            acc0 = Mma<T>::run(a, kf[0][ks], acc0);
+            acc1 = Mma<T>::run(a, kf[1][ks], acc1);
+          }
+          if (full) {
+            mid[0] += block_sum_full(acc0, lv, p.c);
+            mid[1] += block_sum_full(acc1, lv, p.c);
+          } else {
+            mid[0] += block_sum_band(acc0, lv, i0, jw, p.W, lane, p.c);
+            mid[1] += block_sum_band(acc1, lv, i0, jw + 32, p.W, lane, p.c);
+          }
         }
-        accumulate(acc0, lv, i0, jw, p.W, lane, p.c, mid[0]);
-        accumulate(acc1, lv, i0, jw + 32, p.W, lane, p.c, mid[1]);
       }
-      if ((u & 15) == 15) {
+      if ((u & 7) == 7) {
         top[0] += mid[0];
         top[1] += mid[1];
         mid[0] = 0.f;

@@ -33,7 +33,8 @@ _SIGNATURES = {
                          _i, _f, _p, _p, _p]),
     "evict_plan": (_i, [_i, _i, _p, _i, _i, _p, _p]),
     "fam_budgets_from_ratios": (_i, [_i, _p, _i64, _p]),
-    "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p]),
+    "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
+    "evict_select_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -170,9 +171,13 @@ def fam_budgets_from_ratios(ratios: Sequence[float], t: int) -> np.ndarray:
     return out
 
 
+def evict_select_workspace_size(H: int, S: int, sinks: int, recent: int) -> int:
+    return int(load().evict_select_workspace_size(int(H), int(S), int(sinks), int(recent)))
+
+
 def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,
-                 idx: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None
-                 ) -> Tuple[torch.Tensor, torch.Tensor]:
+                 idx: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
         raise FamError(1, "scores must be a device fp32 [H, S] tensor")
     if scores.stride(1) != 1:
@@ -187,8 +192,12 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
         idx = torch.empty(total, dtype=torch.int32, device=scores.device)
     if offsets is None:
         offsets = torch.empty(H + 1, dtype=torch.int64, device=scores.device)
+    if workspace is None:
+        nbytes = evict_select_workspace_size(H, S, sinks, recent)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=scores.device)
     _check(load().evict_select(scores.data_ptr(), scores.stride(0), H, S, b.ctypes.data,
                                int(sinks), int(recent), idx.data_ptr(), offsets.data_ptr(),
+                               workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(scores)))
     return idx, offsets
 

@@ -41,7 +41,7 @@ typedef enum {
   FAM_OK = 0,
   FAM_ERR_INVALID_ARG = 1, /* a size, stride, pointer or budget is invalid   */
   FAM_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype...) */
-  FAM_ERR_WORKSPACE = 3,   /* reserved                                       */
+  FAM_ERR_WORKSPACE = 3,   /* the workspace is missing or too small          */
   FAM_ERR_HIP = 4          /* the HIP runtime reported an error at launch    */
 } fam_status;
 
@@ -75,7 +75,8 @@ const char* fam_last_error(void);
  *
  * Requirements: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; d in {64, 128};
  * q and k 16-byte aligned with row strides (q_ss, k_ss) multiples of 8
- * elements; every stride >= 0 and the tensors addressable with them.
+ * elements and at most 2^24 elements; every stride >= 0 and the tensors
+ * addressable with them.
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (d, dtype), FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
 fam_status fam_lse(const void* q, const void* k, fam_dtype dtype,
@@ -167,15 +168,25 @@ fam_status fam_budgets_from_ratios(int H, const double* ratios, int64_t t, int64
  *   idx         device out, [offsets[H]] int32: for each head h, the kept
  *               positions in ascending order at idx[offsets[h] ...]
  *   offsets_dev device out, [H + 1] int64: the offsets of evict_plan
+ *   workspace   device scratch of at least
+ *               evict_select_workspace_size(H, S, sinks, recent) bytes,
+ *               16-byte aligned, owned by the caller; its contents on entry
+ *               do not matter and on return are unspecified. Calls that
+ *               share a workspace must be ordered on one stream.
  *
  * Requirements: H >= 0, 1 <= S; every head's candidate count (S minus the
- * forced rows) at most 131072. H == 0 is a no-op.
+ * forced rows) at most 131072. H == 0 is a no-op (nothing is written).
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (too many candidates),
- * FAM_ERR_HIP.
+ * FAM_ERR_WORKSPACE (missing or too small workspace), FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
 fam_status evict_select(const float* scores, int64_t score_row_stride, int H, int S,
                         const int64_t* budgets, int sinks, int recent,
-                        int32_t* idx, int64_t* offsets_dev, void* stream);
+                        int32_t* idx, int64_t* offsets_dev,
+                        void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of device workspace evict_select needs for these sizes (host-only;
+ * 0 for invalid sizes). */
+size_t evict_select_workspace_size(int H, int S, int sinks, int recent);
 
 /* ------------------------------------------------------------------------
  * kv_compact -- gather kept K and V rows into a new packed cache.

@@ -98,14 +98,30 @@ def test_fam_mass_and_compute_validation():
     assert st == INVALID
 
 
+WORKSPACE = 3
+
+
 def test_evict_select_validation():
     lib = fam.load()
+    ws = lib.evict_select_workspace_size(2, 100, 4, 4)
+    assert ws > 0 and lib.evict_select_workspace_size(-1, 100, 4, 4) == 0
     b = np.array([10, -1], dtype=np.int64)
-    assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, None) == INVALID
+    assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, ws, None) == INVALID
     b = np.array([10, 10], dtype=np.int64)
-    assert lib.evict_select(FAKE, 99, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, None) == INVALID
-    assert lib.evict_select(FAKE, 200000, 2, 200000, b.ctypes.data, 4, 4, FAKE, FAKE, None) == UNSUPPORTED
-    assert lib.evict_select(FAKE, 100, 0, 100, None, 4, 4, FAKE, FAKE, None) == 0  # H == 0: no-op
+    assert lib.evict_select(FAKE, 99, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, ws, None) == INVALID
+    big = lib.evict_select_workspace_size(2, 200000, 4, 4)
+    assert lib.evict_select(FAKE, 200000, 2, 200000, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, big, None) == UNSUPPORTED
+    assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, ws - 1, None) == WORKSPACE
+    assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, None, ws, None) == WORKSPACE
+    assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE + 8, ws, None) == INVALID
+    assert lib.evict_select(FAKE, 100, 0, 100, None, 4, 4, FAKE, FAKE, None, 0, None) == 0  # H == 0: no-op
+
+
+def test_workspace_size_grows_with_heads_and_length():
+    lib = fam.load()
+    a = lib.evict_select_workspace_size(8, 131072 + 516, 4, 512)
+    assert a >= lib.evict_select_workspace_size(8, 4096, 4, 512)
+    assert lib.evict_select_workspace_size(128, 8192, 4, 32) == lib.evict_select_workspace_size(64, 8192, 4, 32)
 
 
 def test_kv_compact_validation():
