@@ -10,22 +10,27 @@
 // for "not a candidate"). A candidate's composite is (key << 32 | ~position):
 // composites are distinct, and the chosen set is the n_choose largest.
 //
-// Three launches over (chunk, head) workgroups; a chunk is 4096 candidate
-// positions of one head, 16 per thread in registers:
-//   1. hist:    per chunk, an LDS histogram of key bits 31..21 (level 1).
-//   2. collect: every chunk sums the head's level-1 histograms and finds the
-//               bin b1 holding the n_choose-th composite; it counts its keys
-//               above b1, lists the composites of its keys inside b1, and
-//               builds their histogram of key bits 20..10 (level 2).
-//   3. finish:  every chunk sums the level-2 histograms (bin b2), walks the
-//               head's b1 lists once to count, per chunk, the entries above
-//               (b1, b2) and to gather those equal to it into LDS, runs an
-//               exact radix select over the gathered composites, derives
-//               every chunk's chosen count and hence its output base, and
-//               writes its chosen positions in ascending order. Chunk 0 also
-//               writes the sinks, the window and the offsets.
-// A whole bin that is taken needs no further level. If the (b1, b2) entries
-// do not fit in LDS, the exact select streams the b1 lists instead.
+// Three launches over (chunk, head) workgroups. A chunk is 4096 candidate
+// positions of one head; thread t holds positions 16t .. 16t+15 of it in
+// registers. Workgroups exchange data only across launch boundaries (a
+// device-scope fence per workgroup costs more than a launch on this chip),
+// and each launch issues its global loads together, so that it costs about
+// one memory round trip:
+//   1. hist:    per chunk, an LDS histogram of key bits 31..22 (level 1),
+//               stored as descending cumulative counts (u16 per bin).
+//   2. collect: every chunk sums the head's level-1 counts and finds the bin
+//               b1 holding the n_choose-th composite, counts its keys above
+//               and inside b1, and writes its keys inside b1 to a list
+//               grouped by key bits 21..12 (level 2, descending; a counting
+//               sort in LDS) with its cumulative level-2 counts beside it.
+//   3. scatter: every chunk sums the level-2 counts (bin b2), gathers the few
+//               (b1, b2) entries of all chunks, picks the exact threshold
+//               composite among them, derives every chunk's chosen count and
+//               hence its own output base, and writes its chosen positions
+//               in ascending order. The resolution is repeated per chunk on
+//               L2-resident data instead of costing another launch. Chunk 0
+//               also writes the sinks, the window and the offsets.
+// A bin that is taken whole needs no further level.
 // Output per head: sinks, then the chosen candidates, then the window.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
@@ -34,11 +39,15 @@ namespace fam {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kPerThread = kSelectChunk / kThreads;  // 16
-constexpr int kIters = kPerThread / 4;               // float4 loads per thread
-constexpr int kBins = 2048;
+constexpr int kPerThread = kSelectChunk / kThreads;  // 16 consecutive positions
+constexpr int kBins = 1024;                          // per histogram level (10 key bits)
+constexpr int kBinsPerThread = kBins / kThreads;     // 4 bins = one 8-byte u16 group
+constexpr int kRadixBins = 2048;                     // exact pick: 11 bits per pass
 constexpr int kMaxChunks = (kSelectMaxCandidates + 3) / kSelectChunk + 1;
-constexpr int kLdsList = 8192;                       // (b1, b2) entries held in LDS
+constexpr int kLdsList = 4096;  // (b1, b2) entries held in LDS
+constexpr int kRankMax = 128;   // up to this many, rank them by direct comparison
+
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ uint32_t order_key(float f) {
   uint32_t u = __float_as_uint(f);
@@ -51,15 +60,16 @@ __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
   return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - pos);
 }
 __device__ __forceinline__ uint32_t comp_pos(uint64_t v) { return 0xffffffffu - (uint32_t)v; }
-__device__ __forceinline__ uint32_t comp_d2(uint64_t v) { return (uint32_t)(v >> 42) & 2047u; }
+__device__ __forceinline__ uint32_t key_top(uint32_t k) { return k >> 22; }
+__device__ __forceinline__ uint32_t key_mid(uint32_t k) { return (k >> 12) & 1023u; }
 
 // Workspace of one launch: per head slot, per chunk.
 struct Ws {
-  uint64_t* list;   // [slots][nchunk][kSelectChunk] composites of the keys inside bin b1
-  uint16_t* hist1;  // [slots][nchunk][kBins]
-  uint16_t* hist2;  // [slots][nchunk][kBins]
-  int* cnt;         // [slots][nchunk][2]: (# inside b1, # above b1)
-  int* state;       // [slots][4]: b1, need (inside b1), # inside b1, whole-bin flag
+  uint64_t* list;   // [slots][nchunk][kSelectChunk] composites inside b1, mid bits descending
+  uint16_t* cum1;   // [slots][nchunk][kBins] # keys with top bits >= bin
+  uint16_t* cum2;   // [slots][nchunk][kBins] # keys inside b1 with mid bits >= bin
+  int* cnt;         // [slots][nchunk][2]: # keys above b1, # inside b1
+  int* st;          // [slots][4]: b1, keys still needed from b1, whole-bin flag
 };
 
 __host__ __device__ inline size_t ws_bytes(int slots, int nchunk) {
@@ -74,28 +84,53 @@ __device__ __forceinline__ Ws ws_of(const SelectArgs& p) {
   char* base = static_cast<char*>(p.ws);
   w.list = reinterpret_cast<uint64_t*>(base);
   base += nh * nc * kSelectChunk * sizeof(uint64_t);
-  w.hist1 = reinterpret_cast<uint16_t*>(base);
+  w.cum1 = reinterpret_cast<uint16_t*>(base);
   base += nh * nc * kBins * sizeof(uint16_t);
-  w.hist2 = reinterpret_cast<uint16_t*>(base);
+  w.cum2 = reinterpret_cast<uint16_t*>(base);
   base += nh * nc * kBins * sizeof(uint16_t);
   w.cnt = reinterpret_cast<int*>(base);
   base += nh * nc * 2 * sizeof(int);
-  w.state = reinterpret_cast<int*>(base);
+  w.st = reinterpret_cast<int*>(base);
   return w;
 }
 
-// Keys of this thread's 16 positions: pos(i) = base + (i/4)*1024 + 4*tid + i%4.
-// Interior chunks issue their four 16-byte loads back to back.
+__device__ __forceinline__ int chunks_of(const SelectArgs& p) {
+  const int a0 = p.c0 & ~3;
+  return max(1, (p.c1 - a0 + kSelectChunk - 1) / kSelectChunk);
+}
+
+// Workgroup -> (chunk w, head slot hl). Consecutive workgroup ids go to
+// consecutive XCDs (round robin over kXcds), so all chunks of a head are
+// placed on one XCD: the head's scores, histograms and lists then stay in
+// that XCD's L2 across the three launches. Returns false for the padding
+// workgroups of a last, partial group of heads.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool wg_coords(const SelectArgs& p, int& w, int& hl) {
+  const int id = blockIdx.x, x = id % kXcds, j = id / kXcds;
+  const int grp = j / p.nchunk;
+  w = j - grp * p.nchunk;
+  hl = x + kXcds * grp;
+  return hl < p.nheads;
+}
+
+// No candidate or every candidate is chosen: only the scatter launch works.
+__device__ __forceinline__ bool trivial_head(const SelectArgs& p, int n_choose) {
+  return n_choose == 0 || n_choose == p.c1 - p.c0;
+}
+
+// Keys of positions base + 16*tid + i (0 outside the candidate range).
+// Interior chunks of 16-byte aligned rows issue four 16-byte loads.
 __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row, int base,
                                            uint32_t (&k)[kPerThread]) {
+  const int first = base + kPerThread * (int)threadIdx.x;
   const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
   if (vec_ok && base >= p.c0 && base + kSelectChunk <= p.c1) {
-    f32x4_t f[kIters];
+    f32x4_t f[kPerThread / 4];
 #pragma unroll
-    for (int it = 0; it < kIters; ++it)
-      f[it] = *reinterpret_cast<const f32x4_t*>(row + base + it * (4 * kThreads) + 4 * threadIdx.x);
+    for (int it = 0; it < kPerThread / 4; ++it)
+      f[it] = *reinterpret_cast<const f32x4_t*>(row + first + 4 * it);
 #pragma unroll
-    for (int it = 0; it < kIters; ++it)
+    for (int it = 0; it < kPerThread / 4; ++it)
 #pragma unroll
       for (int c = 0; c < 4; ++c) k[4 * it + c] = order_key(f[it][c]);
     return;
@@ -103,37 +138,10 @@ __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row
   // edge chunk: every load reads a clamped in-range position, then masks
   float f[kPerThread];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int q = base + (i / 4) * (4 * kThreads) + 4 * (int)threadIdx.x + (i % 4);
-    f[i] = row[min(max(q, p.c0), p.c1 - 1)];
-  }
+  for (int i = 0; i < kPerThread; ++i) f[i] = row[min(max(first + i, p.c0), p.c1 - 1)];
 #pragma unroll
-  for (int i = 0; i < kPerThread; ++i) {
-    const int q = base + (i / 4) * (4 * kThreads) + 4 * (int)threadIdx.x + (i % 4);
-    k[i] = (q >= p.c0 && q < p.c1) ? order_key(f[i]) : 0u;
-  }
-}
-
-// LDS counter increment with the lanes that share the first active lane's
-// slot combined into one atomic (scores cluster, so a few slots take most
-// of the increments and same-address atomics would serialise).
-__device__ __forceinline__ void agg_inc(uint32_t* cnt, uint32_t slot, bool valid) {
-  const uint64_t vmask = __ballot(valid);
-  if (vmask == 0) return;
-  const int lane = threadIdx.x & 63;
-  const int leader = __ffsll((unsigned long long)vmask) - 1;
-  const uint32_t ls = __shfl(slot, leader);
-  const bool same = valid && slot == ls;
-  const uint64_t smask = __ballot(same);
-  if (same) {
-    if (lane == leader) atomicAdd(&cnt[ls], (uint32_t)__popcll(smask));
-  } else if (valid) {
-    atomicAdd(&cnt[slot], 1u);
-  }
-}
-
-__device__ __forceinline__ int chunk_pos(int base, int i) {
-  return base + (i / 4) * (4 * kThreads) + 4 * (int)threadIdx.x + (i % 4);
+  for (int i = 0; i < kPerThread; ++i)
+    k[i] = (first + i >= p.c0 && first + i < p.c1) ? order_key(f[i]) : 0u;
 }
 
 // Inclusive prefix sum over the 256 threads; `total` receives the sum.
@@ -159,7 +167,7 @@ __device__ int block_scan(int v, int* sh, int& total) {
 }
 
 // Wave 0 computes out[c] = sum_{c' < c} val(c') for c < n <= 64 and out[n] =
-// the total (all loads issued at once). The caller synchronises afterwards.
+// the total, all loads issued at once. The caller synchronises afterwards.
 template <typename F>
 __device__ __forceinline__ void wave0_exclusive_scan(int n, F val, int* out) {
   if (threadIdx.x < 64) {
@@ -174,6 +182,85 @@ __device__ __forceinline__ void wave0_exclusive_scan(int n, F val, int* out) {
     if (lane < n) out[lane] = v - x;
     if (lane == 63) out[n] = v;
   }
+}
+
+// This thread's 4 bins of an LDS histogram as descending inclusive
+// cumulative counts: cum[j] = # elements in bins >= 4*tid + j.
+__device__ __forceinline__ void descending_cum(const uint32_t* hist, int* sh,
+                                               uint32_t (&cum)[kBinsPerThread]) {
+  uint32_t h[kBinsPerThread];
+  int local = 0;
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) {
+    h[j] = hist[kBinsPerThread * threadIdx.x + j];
+    local += (int)h[j];
+  }
+  int total;
+  const int incl = block_scan(local, sh, total);
+  uint32_t run = (uint32_t)(total - incl);
+#pragma unroll
+  for (int j = kBinsPerThread - 1; j >= 0; --j) {
+    run += h[j];
+    cum[j] = run;
+  }
+}
+
+// This thread's 4 counts (each <= kSelectChunk) as packed u16 at dst.
+__device__ __forceinline__ void store_u16x4(uint16_t* dst, const uint32_t (&v)[kBinsPerThread]) {
+  u32x2_t r;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) r[q] = (v[2 * q] & 0xffffu) | (v[2 * q + 1] << 16);
+  *reinterpret_cast<u32x2_t*>(dst + kBinsPerThread * threadIdx.x) = r;
+}
+
+__device__ __forceinline__ uint32_t u16_at(u32x2_t v, int j) {
+  const uint32_t word = j < 2 ? v[0] : v[1];
+  return (j & 1) ? word >> 16 : word & 0xffffu;
+}
+
+// Every chunk's packed u16 counts of this thread's 4 bins, all loads in flight.
+__device__ __forceinline__ void load_cums(const uint16_t* src, int nchunk_h,
+                                          u32x2_t (&v)[kMaxChunks]) {
+  src += kBinsPerThread * threadIdx.x;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+    v[c] = c < nchunk_h ? *reinterpret_cast<const u32x2_t*>(src + (size_t)c * kBins)
+                        : u32x2_t{0u, 0u};
+}
+
+__device__ __forceinline__ void sum_cums(const u32x2_t (&v)[kMaxChunks],
+                                         uint32_t (&acc)[kBinsPerThread]) {
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) acc[j] = 0u;
+#pragma unroll
+  for (int c = 0; c < kMaxChunks; ++c)
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      acc[2 * q] += v[c][q] & 0xffffu;
+      acc[2 * q + 1] += v[c][q] >> 16;
+    }
+}
+
+// Given the head's descending cumulative counts of this thread's bins (staged
+// through `cum`, kBins + 1 entries of LDS), find the bin b with
+// cum[b] >= need > cum[b + 1]: out3 = {b, cum[b + 1], cum[b] - cum[b + 1]}.
+__device__ void find_cum_bin(const uint32_t (&acc)[kBinsPerThread], uint32_t* cum, int need,
+                             int* out3) {
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) cum[kBinsPerThread * threadIdx.x + j] = acc[j];
+  if (threadIdx.x == 0) cum[kBins] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < kBinsPerThread; ++j) {
+    const int b = kBinsPerThread * threadIdx.x + j;
+    const uint32_t hi = cum[b], lo = cum[b + 1];
+    if (hi >= (uint32_t)need && lo < (uint32_t)need) {
+      out3[0] = b;
+      out3[1] = (int)lo;
+      out3[2] = (int)(hi - lo);
+    }
+  }
+  __syncthreads();
 }
 
 // Over an LDS histogram of nb bins (nb a multiple of 256), find the bin that
@@ -198,137 +285,174 @@ __device__ void find_bin(const uint32_t* hist, int nb, int need, int* sh, int* o
   __syncthreads();
 }
 
-// Sum of the head's per-chunk u16 histograms into LDS (8 loads in flight).
-__device__ void sum_hists(const uint16_t* src, int nchunk_h, uint32_t* hist) {
-  constexpr int BPT = kBins / kThreads;  // 8 bins = one 16-byte load per chunk
-  uint32_t acc[BPT] = {};
-  src += threadIdx.x * BPT;
-  for (int w0 = 0; w0 < nchunk_h; w0 += 8) {
-    u32x4_t v[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      v[j] = w0 + j < nchunk_h ? *reinterpret_cast<const u32x4_t*>(src + (size_t)(w0 + j) * kBins)
-                               : u32x4_t{0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        acc[2 * q] += v[j][q] & 0xffffu;
-        acc[2 * q + 1] += v[j][q] >> 16;
-      }
+// The need-th largest of n distinct composites whose top 20 bits are equal;
+// fetch(g) returns entry g (from LDS or from the global lists). Small sets
+// rank every entry by direct comparison and return the entry itself; larger
+// ones run a radix select over the low 44 bits (4 x 11) and return those
+// bits.
+template <typename F>
+__device__ uint64_t pick_threshold(int n, int need, F fetch, uint32_t* hist, int* sh, int* res,
+                                   uint64_t* sh_thr) {
+  if (n <= kRankMax) {
+    for (int g = threadIdx.x; g < n; g += kThreads) {
+      const uint64_t x = fetch(g);
+      int r = 0;
+      for (int j = 0; j < n; ++j) r += fetch(j) > x ? 1 : 0;
+      if (r == need - 1) *sh_thr = x;
+    }
+    __syncthreads();
+    return *sh_thr;
   }
+  uint64_t prefix = 0, pmask = 0;
+  int rem = need;
+  const uint64_t lowmask = (1ull << 44) - 1;
+  for (int lev = 0; lev < 4; ++lev) {
+    const int sft = 33 - 11 * lev;
+    constexpr int nb = kRadixBins;
+    for (int i = threadIdx.x; i < nb; i += kThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int g0 = threadIdx.x; g0 < n; g0 += kThreads * 8) {
+      uint64_t v[8];
 #pragma unroll
-  for (int j = 0; j < BPT; ++j) hist[threadIdx.x * BPT + j] = acc[j];
-  __syncthreads();
-}
-
-__device__ __forceinline__ void store_hist(const uint32_t* hist, uint16_t* dst) {
-  for (int i = threadIdx.x; i < kBins; i += kThreads) dst[i] = (uint16_t)hist[i];
-}
-
-__device__ __forceinline__ int chunks_of(const SelectArgs& p) {
-  const int a0 = p.c0 & ~3;
-  return max(1, (p.c1 - a0 + kSelectChunk - 1) / kSelectChunk);
+      for (int j = 0; j < 8; ++j) {
+        const int g = g0 + j * kThreads;
+        v[j] = g < n ? fetch(g) : 0ull;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const uint64_t x = v[j] & lowmask;
+        if (g0 + j * kThreads < n && (x & pmask) == prefix)
+          atomicAdd(&hist[(x >> sft) & (uint64_t)(nb - 1)], 1u);
+      }
+    }
+    __syncthreads();
+    find_bin(hist, nb, rem, sh, res);
+    rem -= res[1];
+    prefix |= (uint64_t)res[0] << sft;
+    pmask |= (uint64_t)(nb - 1) << sft;
+    __syncthreads();
+  }
+  return prefix;
 }
 
 // ---------------------------------------------------------------- launch 1
 __global__ __launch_bounds__(kThreads) void sel_hist(SelectArgs p) {
   __shared__ uint32_t hist[kBins];
-  const int hl = blockIdx.y, w = blockIdx.x;
-  const int n_choose = p.n_choose[hl];
-  if (n_choose == 0 || n_choose == p.c1 - p.c0) return;
+  __shared__ int sh[8];
+  int w, hl;
+  if (!wg_coords(p, w, hl)) return;
+  if (trivial_head(p, p.n_choose[hl])) return;
   const int base = (p.c0 & ~3) + w * kSelectChunk;
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
-  __syncthreads();
   const float* row = p.scores + (int64_t)(p.head0 + hl) * p.row_stride;
   uint32_t k[kPerThread];
   load_chunk(p, row, base, k);
-#pragma unroll
-  for (int i = 0; i < kPerThread; ++i) agg_inc(hist, k[i] >> 21, k[i] != 0u);
+  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
   __syncthreads();
-  const Ws ws = ws_of(p);
-  store_hist(hist, ws.hist1 + ((size_t)hl * p.nchunk + w) * kBins);
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i)
+    if (k[i] != 0u) atomicAdd(&hist[key_top(k[i])], 1u);
+  __syncthreads();
+  uint32_t cum[kBinsPerThread];
+  descending_cum(hist, sh, cum);
+  store_u16x4(ws_of(p).cum1 + ((size_t)hl * p.nchunk + w) * kBins, cum);
 }
 
 // ---------------------------------------------------------------- launch 2
 __global__ __launch_bounds__(kThreads) void sel_collect(SelectArgs p) {
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[kBins];     // level-2 histogram, then bucket cursors
+  __shared__ uint32_t cum[kBins + 1];  // the head's level-1 cumulative counts
   __shared__ int sh[8];
   __shared__ int res[3];
-  __shared__ int n_list;
-  const int hl = blockIdx.y, w = blockIdx.x;
+
+  int w, hl;
+  if (!wg_coords(p, w, hl)) return;
   const int n_choose = p.n_choose[hl];
-  if (n_choose == 0 || n_choose == p.c1 - p.c0) return;
+  if (trivial_head(p, n_choose)) return;
   const int base = (p.c0 & ~3) + w * kSelectChunk;
   const int nchunk_h = chunks_of(p);
   const Ws ws = ws_of(p);
-  sum_hists(ws.hist1 + (size_t)hl * p.nchunk * kBins, nchunk_h, hist);
-  find_bin(hist, kBins, n_choose, sh, res);
-  const uint32_t b1 = (uint32_t)res[0];
-  const int need = n_choose - res[1];
-  const int in_b1 = res[2];
-  const bool whole = need == in_b1;
-  if (w == 0 && threadIdx.x == 0) {
-    int* st = ws.state + hl * 4;
-    st[0] = (int)b1;
-    st[1] = need;
-    st[2] = in_b1;
-    st[3] = whole ? 1 : 0;
-  }
-  for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
-  if (threadIdx.x == 0) n_list = 0;
-  __syncthreads();
   const float* row = p.scores + (int64_t)(p.head0 + hl) * p.row_stride;
   uint32_t k[kPerThread];
   load_chunk(p, row, base, k);
-  uint64_t* list = ws.list + ((size_t)hl * p.nchunk + w) * kSelectChunk;
-  int above = 0;
-  const int lane = threadIdx.x & 63;
+
+  // level 1: the head's bin b1
+  {
+    u32x2_t v[kMaxChunks];
+    load_cums(ws.cum1 + (size_t)hl * p.nchunk * kBins, nchunk_h, v);
+    uint32_t acc[kBinsPerThread];
+    sum_cums(v, acc);
+    for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
+    find_cum_bin(acc, cum, n_choose, res);
+  }
+  const uint32_t b1 = (uint32_t)res[0];
+  const int need1 = n_choose - res[1];
+  const bool whole1 = need1 == res[2];
+  if (w == 0 && threadIdx.x == 0) {
+    int* st = ws.st + hl * 4;
+    st[0] = (int)b1;
+    st[1] = need1;
+    st[2] = whole1 ? 1 : 0;
+  }
+
+  // this chunk: keys above b1, keys inside b1 and their level-2 histogram
+  int packed = 0;  // (# above) << 16 | # inside, each <= 4096
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) {
-    const uint32_t top = k[i] >> 21;
-    above += (k[i] != 0u && top > b1) ? 1 : 0;
-    const bool in = k[i] != 0u && top == b1;
-    // one list-slot atomic per wave
-    const uint64_t m = __ballot(in);
-    const int leader = m != 0 ? __ffsll((unsigned long long)m) - 1 : 0;
-    int slot0 = 0;
-    if (m != 0 && lane == leader) slot0 = atomicAdd(&n_list, __popcll(m));
-    slot0 = __shfl(slot0, leader);
-    if (in && !whole) {
-      const int slot = slot0 + __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-      list[slot] = composite(k[i], (uint32_t)chunk_pos(base, i));
-    }
-    if (!whole) agg_inc(hist, (k[i] >> 10) & 2047u, in);
+    const bool valid = k[i] != 0u;
+    packed += (valid && key_top(k[i]) > b1) ? (1 << 16) : 0;
+    const bool in = valid && key_top(k[i]) == b1;
+    packed += in ? 1 : 0;
+    if (!whole1 && in) atomicAdd(&hist[key_mid(k[i])], 1u);
   }
   int total;
-  block_scan(above, sh, total);  // (its barriers also order the LDS atomics)
-  if (!whole) store_hist(hist, ws.hist2 + ((size_t)hl * p.nchunk + w) * kBins);
+  block_scan(packed, sh, total);  // (its barriers also order the LDS atomics)
+  if (!whole1) {
+    // cumulative level-2 counts; bucket b starts after the keys with mid > b
+    uint32_t c2[kBinsPerThread];
+    descending_cum(hist, sh, c2);
+    store_u16x4(ws.cum2 + ((size_t)hl * p.nchunk + w) * kBins, c2);
+#pragma unroll
+    for (int j = 0; j < kBinsPerThread; ++j) {
+      const int b = kBinsPerThread * threadIdx.x + j;
+      hist[b] = c2[j] - hist[b];
+    }
+    __syncthreads();
+    uint64_t* list = ws.list + ((size_t)hl * p.nchunk + w) * kSelectChunk;
+    const uint32_t first = (uint32_t)(base + kPerThread * (int)threadIdx.x);
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      if (k[i] != 0u && key_top(k[i]) == b1) {
+        const uint32_t slot = atomicAdd(&hist[key_mid(k[i])], 1u);
+        list[slot] = composite(k[i], first + i);
+      }
+    }
+  }
   if (threadIdx.x == 0) {
     int* c = ws.cnt + ((size_t)hl * p.nchunk + w) * 2;
-    c[0] = n_list;
-    c[1] = total;
+    c[0] = total >> 16;
+    c[1] = total & 0xffff;
   }
 }
 
 // ---------------------------------------------------------------- launch 3
-__global__ __launch_bounds__(kThreads) void sel_finish(SelectArgs p) {
-  __shared__ uint32_t hist[kBins];
+__global__ __launch_bounds__(kThreads) void sel_scatter(SelectArgs p) {
+  __shared__ uint32_t hist[kRadixBins];
+  __shared__ uint32_t cum[kBins + 1];
   __shared__ uint64_t lst[kLdsList];
   __shared__ int sh[8];
   __shared__ int res[3];
-  __shared__ int list_off[kMaxChunks + 1];
-  __shared__ uint32_t chunk_sel[kMaxChunks];
-  __shared__ int chunk_off[kMaxChunks + 1];
-  __shared__ int n_lds;
+  __shared__ uint64_t sh_thr;
+  __shared__ int a1[kMaxChunks], i1[kMaxChunks], a2[kMaxChunks], hi2[kMaxChunks];
+  __shared__ int goff[kMaxChunks + 1], choff[kMaxChunks + 1];
+  __shared__ uint32_t chosen[kMaxChunks];
 
-  const int hl = blockIdx.y, w = blockIdx.x;
+  int w, hl;
+  if (!wg_coords(p, w, hl)) return;
   const int h = p.head0 + hl;
   const int n_choose = p.n_choose[hl];
   const int c0 = p.c0, c1 = p.c1, S = p.S;
   int32_t* dst = p.idx + p.out_off[hl];
   const int a0 = c0 & ~3;
-  const int nchunk_h = chunks_of(p);
   const int base = a0 + w * kSelectChunk;
 
   if (w == 0) {
@@ -345,148 +469,116 @@ __global__ __launch_bounds__(kThreads) void sel_finish(SelectArgs p) {
       dst[i] = i;
     return;
   }
-
+  const int nchunk_h = chunks_of(p);
   const Ws ws = ws_of(p);
-  const int* st = ws.state + hl * 4;
+  const float* row = p.scores + (int64_t)h * p.row_stride;
+  uint32_t k[kPerThread];
+  load_chunk(p, row, base, k);
+  // level-2 counts are loaded with everything else; unused if b1 is whole
+  const uint16_t* cum2 = ws.cum2 + (size_t)hl * p.nchunk * kBins;
+  u32x2_t v[kMaxChunks];
+  load_cums(cum2, nchunk_h, v);
+  const int* cnt = ws.cnt + (size_t)hl * p.nchunk * 2;
+  for (int c = threadIdx.x; c < nchunk_h; c += kThreads) {
+    a1[c] = cnt[2 * c];
+    i1[c] = cnt[2 * c + 1];
+  }
+  const int* st = ws.st + hl * 4;
   const uint32_t b1 = (uint32_t)st[0];
   const int need1 = st[1];
-  const bool whole1 = st[3] != 0;
-  const float* row = p.scores + (int64_t)h * p.row_stride;
-  const int* cnt = ws.cnt + (size_t)hl * p.nchunk * 2;
-
-  for (int c = threadIdx.x; c < nchunk_h; c += kThreads) chunk_sel[c] = (uint32_t)cnt[2 * c + 1];
-  wave0_exclusive_scan(nchunk_h, [&](int c) { return cnt[2 * c]; }, list_off);
-  if (threadIdx.x == 0) n_lds = 0;
+  const bool whole1 = st[2] != 0;
   __syncthreads();
 
-  uint32_t b2 = 0;
   bool whole2 = true;
+  uint32_t b2 = 0;
   uint64_t thr = 0;  // inside (b1, b2), chosen iff composite >= thr
   if (whole1) {
-    for (int c = threadIdx.x; c < nchunk_h; c += kThreads) chunk_sel[c] += (uint32_t)cnt[2 * c];
-    __syncthreads();
+    for (int c = threadIdx.x; c < nchunk_h; c += kThreads) chosen[c] = a1[c] + i1[c];
   } else {
-    const int n_b1 = list_off[nchunk_h];
-    const uint64_t* lists = ws.list + (size_t)hl * p.nchunk * kSelectChunk;
-    // entry g (< n_b1) of the concatenated b1 lists; `c` is a chunk hint that
-    // only moves forward (each thread visits increasing g)
-    auto entry = [&](int g, int& c) {
-      while (c + 1 < nchunk_h && list_off[c + 1] <= g) ++c;
-      return lists[(size_t)c * kSelectChunk + (g - list_off[c])];
-    };
-    sum_hists(ws.hist2 + (size_t)hl * p.nchunk * kBins, nchunk_h, hist);
-    find_bin(hist, kBins, need1, sh, res);
+    {
+      uint32_t acc[kBinsPerThread];
+      sum_cums(v, acc);
+      find_cum_bin(acc, cum, need1, res);
+    }
     b2 = (uint32_t)res[0];
     const int need2 = need1 - res[1];
     const int in_b2 = res[2];
     whole2 = need2 == in_b2;
-    const bool in_lds = in_b2 <= kLdsList;
-    // one walk over the b1 entries: per-chunk counts above b2 (and, for a
-    // whole b2, inside it); the b2 entries go to LDS
-    {
-      int ch = 0;
-      for (int g0 = threadIdx.x; g0 < n_b1 + (kThreads * 8 - 1) - (n_b1 + kThreads * 8 - 1) % (kThreads * 8) ; g0 += kThreads * 8) {
-        uint64_t v[8];
+    // per chunk: # inside b1 with mid >= b2 (hi2) and > b2 (a2), taken from
+    // the registers of the threads that own bins b2 and b2 + 1
+    if ((int)threadIdx.x == (int)(b2 / kBinsPerThread)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int g = g0 + j * kThreads;
-          v[j] = g < n_b1 ? entry(g, ch) : 0ull;
-        }
+      for (int c = 0; c < kMaxChunks; ++c)
+        if (c < nchunk_h) hi2[c] = (int)u16_at(v[c], (int)(b2 % kBinsPerThread));
+    }
+    if (b2 + 1 < (uint32_t)kBins) {
+      if ((int)threadIdx.x == (int)((b2 + 1) / kBinsPerThread)) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int g = g0 + j * kThreads;
-          const bool ok = g < n_b1;
-          const uint32_t d2 = comp_d2(v[j]);
-          const uint32_t c = ok ? (comp_pos(v[j]) - (uint32_t)a0) / kSelectChunk : 0u;
-          agg_inc(chunk_sel, c, ok && (d2 > b2 || (d2 == b2 && whole2)));
-          if (ok && d2 == b2 && !whole2 && in_lds) {
-            const int slot = atomicAdd(&n_lds, 1);
-            if (slot < kLdsList) lst[slot] = v[j];
-          }
-        }
+        for (int c = 0; c < kMaxChunks; ++c)
+          if (c < nchunk_h) a2[c] = (int)u16_at(v[c], (int)((b2 + 1) % kBinsPerThread));
       }
+    } else {
+      for (int c = threadIdx.x; c < nchunk_h; c += kThreads) a2[c] = 0;
     }
     __syncthreads();
-    if (!whole2) {
-      // radix select of the need2-th largest composite among the (b1, b2)
-      // entries, over its low 42 bits (key bits 9..0, inverted position):
-      // 11 + 11 + 11 + 9 bits
-      const int n = in_lds ? min(n_lds, kLdsList) : n_b1;
-      uint64_t prefix = 0, pmask = 0;
-      int rem = need2;
-      const uint64_t lowmask = (1ull << 42) - 1;
-      for (int lev = 0; lev < 4; ++lev) {
-        const int sft = lev < 3 ? 31 - 11 * lev : 0;
-        const int nb = lev < 3 ? 2048 : 512;
-        for (int i = threadIdx.x; i < kBins; i += kThreads) hist[i] = 0u;
-        __syncthreads();
-        int ch = 0;
-        for (int g0 = threadIdx.x; g0 < n; g0 += kThreads * 8) {
-          uint64_t v[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int g = g0 + j * kThreads;
-            v[j] = g < n ? (in_lds ? lst[g] : entry(g, ch)) : 0ull;
-          }
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int g = g0 + j * kThreads;
-            const uint64_t x = v[j] & lowmask;
-            if (g < n && (in_lds || comp_d2(v[j]) == b2) && (x & pmask) == prefix)
-              atomicAdd(&hist[(x >> sft) & (uint64_t)(nb - 1)], 1u);
-          }
-        }
-        __syncthreads();
-        find_bin(hist, nb, rem, sh, res);
-        rem -= res[1];
-        prefix |= (uint64_t)res[0] << sft;
-        pmask |= (uint64_t)(nb - 1) << sft;
-        __syncthreads();
-      }
-      thr = ((uint64_t)b1 << 53) | ((uint64_t)b2 << 42) | prefix;
-      // chosen (b1, b2) entries per chunk
-      int ch = 0;
-      for (int g = threadIdx.x; g < n; g += kThreads) {
-        const uint64_t v = in_lds ? lst[g] : entry(g, ch);
-        if ((in_lds || comp_d2(v) == b2) && v >= thr)
-          atomicAdd(&chunk_sel[(comp_pos(v) - (uint32_t)a0) / kSelectChunk], 1u);
-      }
+    if (whole2) {
+      for (int c = threadIdx.x; c < nchunk_h; c += kThreads) chosen[c] = a1[c] + hi2[c];
+    } else {
+      wave0_exclusive_scan(nchunk_h, [&](int c) { return hi2[c] - a2[c]; }, goff);
       __syncthreads();
+      const uint64_t* lists = ws.list + (size_t)hl * p.nchunk * kSelectChunk;
+      // entry g of the concatenated (b1, b2) runs of the chunk lists
+      auto global_entry = [&](int g) {
+        int lo = 0, hi = nchunk_h - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (goff[mid] <= g) lo = mid;
+          else hi = mid - 1;
+        }
+        return lists[(size_t)lo * kSelectChunk + a2[lo] + (g - goff[lo])];
+      };
+      const bool in_lds = in_b2 <= kLdsList;
+      if (in_lds) {
+        for (int g = threadIdx.x; g < in_b2; g += kThreads) lst[g] = global_entry(g);
+        __syncthreads();
+      }
+      auto fetch = [&](int g) { return in_lds ? lst[g] : global_entry(g); };
+      const uint64_t t = pick_threshold(in_b2, need2, fetch, hist, sh, res, &sh_thr);
+      thr = in_b2 <= kRankMax ? t : (((uint64_t)b1 << 54) | ((uint64_t)b2 << 44) | t);
+      for (int c = threadIdx.x; c < nchunk_h; c += kThreads) chosen[c] = a1[c] + a2[c];
+      __syncthreads();
+      for (int g = threadIdx.x; g < in_b2; g += kThreads) {
+        const uint64_t e = fetch(g);
+        if (e >= thr) atomicAdd(&chosen[(comp_pos(e) - (uint32_t)a0) / kSelectChunk], 1u);
+      }
     }
   }
-  wave0_exclusive_scan(nchunk_h, [&](int c) { return (int)chunk_sel[c]; }, chunk_off);
+  __syncthreads();
+  wave0_exclusive_scan(nchunk_h, [&](int c) { return (int)chosen[c]; }, choff);
   __syncthreads();
 
   // ordered write of this chunk's chosen positions
-  uint32_t k[kPerThread];
-  load_chunk(p, row, base, k);
-  int out = c0 + chunk_off[w];
   const int out_end = c0 + n_choose;
+  const uint32_t first = (uint32_t)(base + kPerThread * (int)threadIdx.x);
+  uint32_t sel = 0;
 #pragma unroll
-  for (int it = 0; it < kIters; ++it) {
-    bool sel[4];
-    int n_mine = 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint32_t key = k[4 * it + c];
-      const uint32_t top = key >> 21, d2 = (key >> 10) & 2047u;
-      bool s = key != 0u && top > b1;
-      if (key != 0u && top == b1) {
-        if (whole1 || d2 > b2) s = true;
-        else if (d2 == b2) s = whole2 || composite(key, (uint32_t)chunk_pos(base, 4 * it + c)) >= thr;
-      }
-      sel[c] = s;
-      n_mine += s;
+  for (int i = 0; i < kPerThread; ++i) {
+    const uint32_t key = k[i];
+    bool s = key != 0u && key_top(key) > b1;
+    if (key != 0u && key_top(key) == b1) {
+      const uint32_t d2 = key_mid(key);
+      if (whole1 || d2 > b2) s = true;
+      else if (d2 == b2) s = whole2 || composite(key, first + i) >= thr;
     }
-    int total;
-    const int incl = block_scan(n_mine, sh, total);
-    int o = out + incl - n_mine;
+    sel |= (s ? 1u : 0u) << i;
+  }
+  const int n_mine = __popc(sel);
+  int total;
+  int o = c0 + choff[w] + block_scan(n_mine, sh, total) - n_mine;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      if (sel[c] && o < out_end) dst[o] = chunk_pos(base, 4 * it + c);
-      o += sel[c];
-    }
-    out += total;
+  for (int i = 0; i < kPerThread; ++i) {
+    if (((sel >> i) & 1u) && o < out_end) dst[o] = (int32_t)(first + i);
+    o += (int)((sel >> i) & 1u);
   }
 }
 
@@ -495,10 +587,11 @@ __global__ __launch_bounds__(kThreads) void sel_finish(SelectArgs p) {
 size_t select_workspace_bytes(int slots, int nchunk) { return ws_bytes(slots, nchunk); }
 
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
-  const dim3 grid(a.nchunk, a.nheads);
+  const int groups = (a.nheads + kXcds - 1) / kXcds;
+  const dim3 grid(kXcds * a.nchunk * groups);
   hipLaunchKernelGGL(sel_hist, grid, dim3(kThreads), 0, s, a);
   hipLaunchKernelGGL(sel_collect, grid, dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(sel_finish, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
