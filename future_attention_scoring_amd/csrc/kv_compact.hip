@@ -7,9 +7,14 @@
 // A row of d two-byte elements is d/8 16-byte chunks; a wave moves 64 such
 // chunks per instruction (4 rows for d = 128), reading one contiguous source
 // row per group of lanes and writing fully contiguous output. Each thread
-// issues all of its loads before its stores. The head of an output row comes
-// from the offsets: a block binary-searches its first row once and then walks
-// forward, since rows are ordered by head.
+// issues all of its loads before its stores.
+//
+// The head of an output row comes from the offsets. With fewer than 256
+// heads, a block stages all of offsets[0..H] in LDS in the same memory round
+// trip as its idx loads and searches there; otherwise it binary-searches the
+// global offsets. Every byte is touched once, so loads and stores carry the
+// non-temporal hint: on this chip that keeps the gather at the same rate
+// whether or not the caches hold dirty data from earlier kernels.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -19,45 +24,62 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kRowsPerBlock = 64;
 
+__device__ __forceinline__ u32x4_t load16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+}
+__device__ __forceinline__ void store16_nt(uint16_t* p, u32x4_t v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4_t*>(p));
+}
+
 template <int CPR>
 __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs p) {
   constexpr int ROWS_PER_PASS = kThreads / CPR;
   constexpr int PASSES = kRowsPerBlock / ROWS_PER_PASS;
+  __shared__ int64_t offs[kThreads];
   const int64_t r0 = (int64_t)blockIdx.x * kRowsPerBlock;
   const int64_t rend = min(p.total_rows, r0 + kRowsPerBlock);
   const int tid = threadIdx.x;
   const int ch = tid % CPR;
+  const bool lds_heads = p.H < kThreads;  // offsets[0 .. H] fit in LDS
+  if (lds_heads && tid <= p.H) offs[tid] = p.offsets[tid];
+  int src[PASSES];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t r = r0 + tid / CPR + (int64_t)i * ROWS_PER_PASS;
+    src[i] = r < rend ? p.idx[r] : -1;
+  }
+  __syncthreads();
 
-  // last head h with offsets[h] <= r0
+  // last head h with offsets[h] <= this thread's first row
+  const int64_t rfirst = r0 + tid / CPR;
   int lo = 0, hi = p.H - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (p.offsets[mid] <= r0) lo = mid; else hi = mid - 1;
+    if ((lds_heads ? offs[mid] : p.offsets[mid]) <= rfirst) lo = mid;
+    else hi = mid - 1;
   }
   int h = lo;
 
   u32x4_t kv[PASSES], vv[PASSES];
-  int64_t rows[PASSES];
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
-    const int64_t r = r0 + tid / CPR + (int64_t)i * ROWS_PER_PASS;
-    rows[i] = r;
+    const int64_t r = rfirst + (int64_t)i * ROWS_PER_PASS;
     kv[i] = zero16();
     vv[i] = zero16();
     if (r < rend) {
-      while (h + 1 < p.H && r >= p.offsets[h + 1]) ++h;
-      const int src = p.idx[r];
-      if (src >= 0 && src < p.S) {
-        kv[i] = load16(p.k + h * p.k_sh + (int64_t)src * p.k_ss + ch * 8);
-        vv[i] = load16(p.v + h * p.v_sh + (int64_t)src * p.v_ss + ch * 8);
+      while (h + 1 < p.H && r >= (lds_heads ? offs[h + 1] : p.offsets[h + 1])) ++h;
+      if (src[i] >= 0 && src[i] < p.S) {
+        kv[i] = load16_nt(p.k + h * p.k_sh + (int64_t)src[i] * p.k_ss + ch * 8);
+        vv[i] = load16_nt(p.v + h * p.v_sh + (int64_t)src[i] * p.v_ss + ch * 8);
       }
     }
   }
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
-    if (rows[i] < rend) {
-      store16(p.k_new + rows[i] * p.d + ch * 8, kv[i]);
-      store16(p.v_new + rows[i] * p.d + ch * 8, vv[i]);
+    const int64_t r = rfirst + (int64_t)i * ROWS_PER_PASS;
+    if (r < rend) {
+      store16_nt(p.k_new + r * p.d + ch * 8, kv[i]);
+      store16_nt(p.v_new + r * p.d + ch * 8, vv[i]);
     }
   }
 }
