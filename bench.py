@@ -1,6 +1,7 @@
 """Benchmark of the future-attention-mass + eviction hot path on one MI355X.
 
-One step = fam_lse + fam_mass (the two-pass future-attention mass) +
+One step = fam_key_norms + fam_lse (first pass, bounded form) + fam_mass
+(the key-major second pass) +
 evict_select (per-head budgets b_h = floor(r_h * S), 4 sinks, recent window)
 + kv_compact (gather of the kept K/V rows), on the Llama-3.1-8B-like layer at
 128k tokens (32 query / 8 KV heads, d = 128, bf16, W = 512). Inputs are
@@ -157,12 +158,14 @@ def main():
     v_new = torch.empty((total, d), dtype=v.dtype, device=dev)
     stream = torch.cuda.current_stream(dev)
 
+    knorm = torch.empty((B, Hkv, fam.fam_key_norm_parts(S)), dtype=torch.float32, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
     def step(events=None):
         if events:
             events[0].record(stream)
-        fam.fam_lse(q, k, lse=lse)
+        fam.fam_key_norms(k, knorm=knorm)
+        fam.fam_lse(q, k, lse=lse, knorm=knorm)
         if events:
             events[1].record(stream)
         fam.fam_mass(q, k, lse, wl.W, mass=mass)

@@ -74,6 +74,18 @@ float resolve_scale(float scale, int d) {
   return (float)(sc * 1.4426950408889634);  // base-2 logits inside the kernels
 }
 
+// Arguments of the first pass and of the key-norm pass; with `knorm` non-null
+// the row shift is the Cauchy-Schwarz bound built from the key-norm partial
+// maxima stored there ([B * Hkv][nkn] floats).
+fam::LseArgs lse_args(const void* q, const void* k, const ScoreShape& s, float scale, float* lse,
+                      float* knorm) {
+  fam::LseArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse,
+                 s.q_sb, s.q_sh, s.q_ss, s.k_sb, s.k_sh, s.k_ss, s.B, s.Hq, s.Hkv, s.S, s.d,
+                 s.Hq / s.Hkv, resolve_scale(scale, s.d), knorm,
+                 knorm ? fam_key_norm_parts(s.S) : 0};
+  return a;
+}
+
 fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
 
 // Forced set and candidate range for a head of length S.
@@ -106,17 +118,28 @@ const char* fam_status_string(fam_status st) {
 
 const char* fam_last_error(void) { return g_error.c_str(); }
 
+int fam_key_norm_parts(int S) { return S < 1 ? 0 : (S < fam::kNormParts ? S : fam::kNormParts); }
+
+fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, int d,
+                         int64_t k_sb, int64_t k_sh, int64_t k_ss, float* knorm, void* stream) {
+  const ScoreShape s{B, Hkv, Hkv, S, d, k_sb, k_sh, k_ss, k_sb, k_sh, k_ss};
+  fam_status st = check_scores(k, k, dtype, s);
+  if (st != FAM_OK) return st;
+  if (!knorm) return fail(FAM_ERR_INVALID_ARG, "knorm must be non-null");
+  const fam::LseArgs a = lse_args(k, k, s, 0.f, nullptr, knorm);
+  return hip_status(fam::launch_knorm(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
+                    "fam_key_norms launch");
+}
+
 fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
                    int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
-                   int64_t k_ss, float scale, float* lse, void* stream) {
+                   int64_t k_ss, float scale, const float* knorm, float* lse, void* stream) {
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   if (!lse) return fail(FAM_ERR_INVALID_ARG, "lse must be non-null");
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
-  fam::LseArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse,
-                 q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
-                 resolve_scale(scale, d)};
+  const fam::LseArgs a = lse_args(q, k, s, scale, lse, const_cast<float*>(knorm));
   return hip_status(fam::launch_lse(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_lse launch");
 }
 
@@ -144,8 +167,14 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
-  st = fam_lse(q, k, dtype, B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, scale, lse, stream);
-  if (st != FAM_OK) return st;
+  // The key-norm partial maxima ([B * Hkv][P] floats, P <= S) occupy the
+  // start of `mass` until the mass pass overwrites it.
+  const fam::LseArgs a = lse_args(q, k, s, scale, lse, mass);
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = fam::launch_knorm(a, elem_of(dtype), hs);
+  if (e != hipSuccess) return hip_status(e, "fam_compute key-norm launch");
+  e = fam::launch_lse(a, elem_of(dtype), hs);
+  if (e != hipSuccess) return hip_status(e, "fam_compute lse launch");
   return fam_mass(q, k, lse, dtype, B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, W, scale,
                   mass, stream);
 }

@@ -55,6 +55,28 @@ __device__ __forceinline__ void store16(uint16_t* p, u32x4_t v) {
 }
 __device__ __forceinline__ u32x4_t zero16() { return u32x4_t{0u, 0u, 0u, 0u}; }
 
+// Sum of squares of the 8 two-byte elements of a 16-byte fragment, in fp32.
+template <typename T> __device__ float sumsq8(u32x4_t v);
+template <> __device__ __forceinline__ float sumsq8<Bf16>(u32x4_t v) {
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float lo = __uint_as_float(v[w] << 16), hi = __uint_as_float(v[w] & 0xffff0000u);
+    s = fmaf(lo, lo, fmaf(hi, hi, s));
+  }
+  return s;
+}
+template <> __device__ __forceinline__ float sumsq8<Fp16>(u32x4_t v) {
+  float s = 0.f;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const float lo = (float)__builtin_bit_cast(_Float16, (unsigned short)(v[w] & 0xffffu));
+    const float hi = (float)__builtin_bit_cast(_Float16, (unsigned short)(v[w] >> 16));
+    s = fmaf(lo, lo, fmaf(hi, hi, s));
+  }
+  return s;
+}
+
 // Pairwise sum of the 16 accumulator-shaped values.
 __device__ __forceinline__ float sum16(const float (&e)[16]) {
   float a0 = e[0] + e[1], a1 = e[2] + e[3], a2 = e[4] + e[5], a3 = e[6] + e[7];

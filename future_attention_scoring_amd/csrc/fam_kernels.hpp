@@ -17,7 +17,14 @@ struct LseArgs {
   int64_t k_sb, k_sh, k_ss;
   int B, Hq, Hkv, S, d, g;
   float c;  // scale * log2(e)
+  // Key-norm bound: knorm[(b * Hkv + h) * nkn + p] is the largest |k_j|^2
+  // over key range p of that KV head (written by launch_knorm). Null selects
+  // the running-maximum form of the first pass.
+  float* knorm;
+  int nkn;
 };
+constexpr int kNormParts = 64;  // partial key-norm maxima per (batch, KV head)
+hipError_t launch_knorm(const LseArgs& a, Elem e, hipStream_t s);
 hipError_t launch_lse(const LseArgs& a, Elem e, hipStream_t s);
 
 // Key-major future-attention mass (second pass).

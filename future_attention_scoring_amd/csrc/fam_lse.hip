@@ -1,8 +1,8 @@
 // First pass: causal row log-sum-exp on bf16/fp16 MFMA (gfx950).
 //
 // KVpop ("Delayed Memory Scoring"): the normaliser of query i sums exp(logit)
-// over the keys j <= i. Here each query's normaliser is formed online over key
-// tiles, in base 2 internally, and stored as a natural log.
+// over the keys j <= i. Here each query's normaliser is formed over key tiles,
+// in base 2 internally, and stored as a natural log.
 //
 // Work decomposition
 //   * A "row unit" is 64 consecutive query positions of one query head. The
@@ -13,13 +13,24 @@
 //   * Each wave keeps its 64 queries' Q fragments in registers as the MFMA B
 //     operand and computes S^T = K_tile * Q^T, so every accumulator column is
 //     one query and the reduction over keys stays inside a lane (the two
-//     half-waves hold disjoint key rows and keep separate running max/sum
-//     that are merged once at the end).
+//     half-waves hold disjoint key rows and are merged once at the end).
 //   * K tiles of 64 keys are double-buffered through LDS with a 16-byte row
 //     pad (conflict-free ds_read_b128 of the A fragments).
 //   * Workgroups are numbered latest-position-first (the longest causal rows
 //     start first) and with the (batch, KV head) index fastest, so with eight
 //     KV heads each XCD works on a single head's K.
+//
+// Shift of the exponentials. Any per-row shift M gives the same normaliser,
+// M + log2(sum_j exp2(c*s_ij - M)), as long as the terms neither overflow nor
+// all vanish. Two forms are used:
+//   * running maximum (the standard online form): exact for any input;
+//   * fixed bound (when the caller provides key norms): by Cauchy-Schwarz,
+//     c*s_ij <= M_i = c * |q_i| * max_j |k_j|, so no term exceeds one and the
+//     per-term maximum and rescaling disappear from the inner loop. If the
+//     bound is so loose that some row's sum falls below 2^-80 (then terms that
+//     underflow could matter), the workgroup repeats its sweep with the
+//     running maximum. A sum of at least 2^-80 over at most 2^28 terms leaves
+//     the underflowed part below 2^-98 of it.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -30,17 +41,23 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 64;
 constexpr int kKeyTile = 64;
+constexpr float kMinBoundSum = 0x1p-80f;
 
-__device__ __forceinline__ void online_update(f32x16_t acc, int kb, int qblock, int S,
-                                              int lane, float c, float& m, float& l) {
+// Causal and ragged-tile mask of a 32x32 block (keys on rows, queries on columns).
+__device__ __forceinline__ void mask_block(f32x16_t& acc, int kb, int qblock, int S, int lane) {
   const int qrow = qblock + (lane & 31);
-  if (kb + 31 > qblock || kb + 32 > S) {  // diagonal or ragged tile: mask
+  if (kb + 31 > qblock || kb + 32 > S) {
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int key = kb + acc_row(v, lane);
       if (key > qrow || key >= S) acc[v] = -kInf;
     }
   }
+}
+
+__device__ __forceinline__ void online_update(f32x16_t acc, int kb, int qblock, int S,
+                                              int lane, float c, float& m, float& l) {
+  mask_block(acc, kb, qblock, S, lane);
   float mx = acc[0];
 #pragma unroll
   for (int v = 1; v < 16; ++v) mx = fmaxf(mx, acc[v]);
@@ -53,8 +70,52 @@ __device__ __forceinline__ void online_update(f32x16_t acc, int kb, int qblock, 
   m = m_new;
 }
 
+__device__ __forceinline__ void bound_update(f32x16_t acc, int kb, int qblock, int S,
+                                             int lane, float c, float M, float& l) {
+  mask_block(acc, kb, qblock, S, lane);
+  float e[16];
+#pragma unroll
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -M));
+  l += sum16(e);
+}
+
+// Maximum of |k_j|^2 over one part of the keys of one (batch, KV head).
 template <int D, typename T>
-__global__ __launch_bounds__(kThreads, 2) void lse_kernel(LseArgs p, int npb) {
+__global__ __launch_bounds__(kThreads) void knorm_kernel(LseArgs p, int chunk) {
+  constexpr int CPR = D / 8;             // 16-byte pieces per key row
+  constexpr int KPP = kThreads / CPR;    // keys per pass of the workgroup
+  constexpr int U = 8;                   // passes in flight
+  __shared__ float red[kWaves];
+  const int part = blockIdx.x % p.nkn, bh = blockIdx.x / p.nkn;
+  const int b = bh / p.Hkv, h = bh % p.Hkv;
+  const uint16_t* kbase = p.k + b * p.k_sb + h * p.k_sh;
+  const int j0 = part * chunk, j1 = min(p.S, j0 + chunk);
+  const int tid = threadIdx.x, lane = tid & 63, piece = tid % CPR;
+  float mx = 0.f;
+  for (int base = j0; base < j1; base += KPP * U) {
+    u32x4_t v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int j = base + u * KPP + tid / CPR;
+      v[u] = j < j1 ? load16(kbase + (int64_t)j * p.k_ss + piece * 8) : zero16();
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float ss = sumsq8<T>(v[u]);
+#pragma unroll
+      for (int o = CPR / 2; o > 0; o >>= 1) ss += __shfl_xor(ss, o);
+      mx = fmaxf(mx, ss);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+  if (lane == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  if (tid == 0) p.knorm[(int64_t)bh * p.nkn + part] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+template <int D, typename T, bool BOUND>
+__global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
   constexpr int PITCH = D + 8;                 // LDS row pitch in elements
   constexpr int KS = D / 16;                   // MFMA k-steps per 32x32 block
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
@@ -125,6 +186,70 @@ __global__ __launch_bounds__(kThreads, 2) void lse_kernel(LseArgs p, int npb) {
     }
   };
 
+  float* lse_row = p.lse + ((int64_t)b * p.Hq + qh) * p.S + q0;
+  bool done = false;
+
+  if constexpr (BOUND) {
+    // row bounds from |q_i| (this wave's registers) and the head's max |k|^2
+    float kk = lane < p.nkn ? p.knorm[(int64_t)bh * p.nkn + lane] : 0.f;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) kk = fmaxf(kk, __shfl_xor(kk, o));
+    float M[2], l[2] = {0.f, 0.f};
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float qq = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) qq += sumsq8<T>(qf[blk][ks]);
+      qq += __shfl_xor(qq, 32);
+      M[blk] = p.c * sqrtf(qq * kk);
+    }
+    load_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int t = 0; t < ntiles; ++t) {
+      const bool more = t + 1 < ntiles;
+      if (more) load_tile(t + 1);
+      const uint16_t* buf = sk[t & 1];
+#pragma unroll
+      for (int kk2 = 0; kk2 < kKeyTile / 32; ++kk2) {
+        const int kb = t * kKeyTile + 32 * kk2;
+        if (active && kb <= q0 + 63 && kb < p.S) {
+          f32x16_t acc0 = {}, acc1 = {};
+#pragma unroll
+          for (int ks = 0; ks < KS; ++ks) {
+            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
+                &buf[(32 * kk2 + col) * PITCH + ks * 16 + half * 8]);
+            acc0 = Mma<T>::run(a, qf[0][ks], acc0);
+            acc1 = Mma<T>::run(a, qf[1][ks], acc1);
+          }
+          bound_update(acc0, kb, q0, p.S, lane, p.c, M[0], l[0]);
+          bound_update(acc1, kb, q0 + 32, p.S, lane, p.c, M[1], l[1]);
+        }
+      }
+      if (more) store_tile((t + 1) & 1);
+      __syncthreads();
+    }
+    float L[2];
+    int loose = 0;
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      L[blk] = l[blk] + __shfl_xor(l[blk], 32);
+      const int row = q0 + 32 * blk + col;
+      if (active && row < p.S && L[blk] < kMinBoundSum) loose = 1;
+    }
+    if (!__syncthreads_or(loose)) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int row = q0 + 32 * blk + col;
+        if (active && half == 0 && row < p.S)
+          lse_row[32 * blk + col] = (M[blk] + fast_log2(L[blk])) * kLn2;
+      }
+      done = true;
+    }
+  }
+  if (done) return;
+
+  // running maximum: the plain form, or the repeat of a loose bound
   float m[2] = {-kInf, -kInf}, l[2] = {0.f, 0.f};
   load_tile(0);
   store_tile(0);
@@ -157,12 +282,11 @@ __global__ __launch_bounds__(kThreads, 2) void lse_kernel(LseArgs p, int npb) {
   for (int blk = 0; blk < 2; ++blk) {
     const float mo = __shfl_xor(m[blk], 32);
     const float lo = __shfl_xor(l[blk], 32);
-    const float M = fmaxf(m[blk], mo);
-    const float Mu = M == -kInf ? 0.f : M;
+    const float Mx = fmaxf(m[blk], mo);
+    const float Mu = Mx == -kInf ? 0.f : Mx;
     const float L = l[blk] * fast_exp2(m[blk] - Mu) + lo * fast_exp2(mo - Mu);
     const int row = q0 + 32 * blk + col;
-    if (active && half == 0 && row < p.S)
-      p.lse[((int64_t)b * p.Hq + qh) * p.S + row] = (M + fast_log2(L)) * kLn2;
+    if (active && half == 0 && row < p.S) lse_row[32 * blk + col] = (Mx + fast_log2(L)) * kLn2;
   }
 }
 
@@ -172,7 +296,19 @@ hipError_t launch_lse_t(const LseArgs& a, hipStream_t s) {
   const int slots = (npb * a.g + kWaves - 1) / kWaves;
   const int64_t grid = (int64_t)slots * a.B * a.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((lse_kernel<D, T>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  if (a.knorm)
+    hipLaunchKernelGGL((lse_kernel<D, T, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  else
+    hipLaunchKernelGGL((lse_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  return hipGetLastError();
+}
+
+template <int D, typename T>
+hipError_t launch_knorm_t(const LseArgs& a, hipStream_t s) {
+  const int chunk = (a.S + a.nkn - 1) / a.nkn;
+  const int64_t grid = (int64_t)a.nkn * a.B * a.Hkv;
+  if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL((knorm_kernel<D, T>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, chunk);
   return hipGetLastError();
 }
 
@@ -181,6 +317,11 @@ hipError_t launch_lse_t(const LseArgs& a, hipStream_t s) {
 hipError_t launch_lse(const LseArgs& a, Elem e, hipStream_t s) {
   if (a.d == 128) return e == Elem::kBf16 ? launch_lse_t<128, Bf16>(a, s) : launch_lse_t<128, Fp16>(a, s);
   return e == Elem::kBf16 ? launch_lse_t<64, Bf16>(a, s) : launch_lse_t<64, Fp16>(a, s);
+}
+
+hipError_t launch_knorm(const LseArgs& a, Elem e, hipStream_t s) {
+  if (a.d == 128) return e == Elem::kBf16 ? launch_knorm_t<128, Bf16>(a, s) : launch_knorm_t<128, Fp16>(a, s);
+  return e == Elem::kBf16 ? launch_knorm_t<64, Bf16>(a, s) : launch_knorm_t<64, Fp16>(a, s);
 }
 
 }  // namespace fam

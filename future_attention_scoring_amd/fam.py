@@ -26,7 +26,10 @@ _i, _i64, _f, _p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
 _SIGNATURES = {
     "fam_status_string": (ctypes.c_char_p, [_i]),
     "fam_last_error": (ctypes.c_char_p, []),
-    "fam_lse": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64, _f, _p, _p]),
+    "fam_key_norm_parts": (_i, [_i]),
+    "fam_key_norms": (_i, [_p, _i, _i, _i, _i, _i, _i64, _i64, _i64, _p, _p]),
+    "fam_lse": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64, _f, _p, _p,
+                     _p]),
     "fam_mass": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
                       _i, _f, _p, _p]),
     "fam_compute": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -107,14 +110,40 @@ def _score_args(q: torch.Tensor, k: torch.Tensor):
     return q4, k4, B, Hq, Hkv, S, d
 
 
+def fam_key_norm_parts(S: int) -> int:
+    return int(load().fam_key_norm_parts(int(S)))
+
+
+def fam_key_norms(k: torch.Tensor, knorm: Optional[torch.Tensor] = None) -> torch.Tensor:
+    k4 = _as4(k)
+    if not k4.is_cuda or k4.stride(3) != 1:
+        raise FamError(1, "k must be a device tensor with a contiguous head dimension")
+    B, Hkv, S, d = k4.shape
+    P = fam_key_norm_parts(S)
+    if knorm is None:
+        knorm = torch.empty((B, Hkv, P), dtype=torch.float32, device=k4.device)
+    elif knorm.numel() != B * Hkv * P or knorm.dtype != torch.float32 or not knorm.is_contiguous():
+        raise FamError(1, f"knorm must be contiguous fp32 [B, Hkv, {P}]")
+    _check(load().fam_key_norms(k4.data_ptr(), _dtype_code(k4), B, Hkv, S, d, *k4.stride()[:3],
+                                knorm.data_ptr(), _stream(k4)))
+    return knorm if k.dim() == 4 else knorm[0]
+
+
 def fam_lse(q: torch.Tensor, k: torch.Tensor, scale: Optional[float] = None,
-            lse: Optional[torch.Tensor] = None) -> torch.Tensor:
+            lse: Optional[torch.Tensor] = None, knorm: Optional[torch.Tensor] = None
+            ) -> torch.Tensor:
     q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
+    kn = 0
+    if knorm is not None:
+        if (knorm.numel() != B * Hkv * fam_key_norm_parts(S) or knorm.dtype != torch.float32
+                or not knorm.is_contiguous()):
+            raise FamError(1, "knorm must be fam_key_norms' output for this k")
+        kn = knorm.data_ptr()
     _check(load().fam_lse(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv, S, d,
                           *q4.stride()[:3], *k4.stride()[:3], 0.0 if scale is None else scale,
-                          lse.data_ptr(), _stream(q4)))
+                          kn, lse.data_ptr(), _stream(q4)))
     return lse if q.dim() == 4 else lse[0]
 
 

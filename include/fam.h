@@ -58,6 +58,26 @@ const char* fam_status_string(fam_status status);
 const char* fam_last_error(void);
 
 /* ------------------------------------------------------------------------
+ * fam_key_norms -- partial maxima of the squared key norms.
+ *
+ * Not a quantity of the pages: an input of fam_lse's bounded form (below).
+ * Per (batch, KV head), the keys are split into P = fam_key_norm_parts(S)
+ * consecutive ranges of ceil(S / P) keys and
+ *
+ *   knorm[b, h, p] = max over keys j of range p of sum_e k[b,h,j,e]^2   (fp32)
+ *
+ * (0 for an empty range).
+ *
+ *   k      device, [B, Hkv, S, d] of `dtype`, strides (k_sb, k_sh, k_ss)
+ *   knorm  device out, [B, Hkv, P] fp32, contiguous, fully overwritten
+ * Requirements and errors as for fam_lse (for the k side).
+ * ---------------------------------------------------------------------- */
+int fam_key_norm_parts(int S);
+fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, int d,
+                         int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                         float* knorm, void* stream);
+
+/* ------------------------------------------------------------------------
  * fam_lse -- causal row log-sum-exp (first pass).
  *
  * [KVpop] "Delayed Memory Scoring": the normaliser of query i is the log of
@@ -71,6 +91,12 @@ const char* fam_last_error(void);
  *   q      device, [B, Hq, S, d] of `dtype`, strides (q_sb, q_sh, q_ss)
  *   k      device, [B, Hkv, S, d] of `dtype`, strides (k_sb, k_sh, k_ss)
  *   scale  softmax scale; a value <= 0 selects 1/sqrt(d)
+ *   knorm  device, [B, Hkv, fam_key_norm_parts(S)] fp32 from fam_key_norms
+ *          on this k, or NULL. With it, each row's exponentials are shifted
+ *          by the Cauchy-Schwarz bound scale * |q_i| * max_j |k_j| instead of
+ *          a running maximum (faster; a workgroup whose bound is too loose
+ *          repeats its rows with the running maximum). The result is the
+ *          same up to fp32 rounding.
  *   lse    device out, [B, Hq, S] fp32, contiguous, fully overwritten
  *
  * Requirements: B, Hq, Hkv, S >= 1; Hq % Hkv == 0; d in {64, 128};
@@ -83,7 +109,7 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype,
                    int B, int Hq, int Hkv, int S, int d,
                    int64_t q_sb, int64_t q_sh, int64_t q_ss,
                    int64_t k_sb, int64_t k_sh, int64_t k_ss,
-                   float scale, float* lse, void* stream);
+                   float scale, const float* knorm, float* lse, void* stream);
 
 /* ------------------------------------------------------------------------
  * fam_mass -- per-KV-head future-attention mass (second, key-major pass).
@@ -112,7 +138,9 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
                     int64_t k_sb, int64_t k_sh, int64_t k_ss,
                     int W, float scale, float* mass, void* stream);
 
-/* fam_compute -- fam_lse followed by fam_mass on the same stream. */
+/* fam_compute -- fam_key_norms, fam_lse (bounded form) and fam_mass on the
+ * same stream. The key-norm partial maxima are kept in the first entries of
+ * `mass` until the mass pass overwrites it, so no workspace is needed. */
 fam_status fam_compute(const void* q, const void* k, fam_dtype dtype,
                        int B, int Hq, int Hkv, int S, int d,
                        int64_t q_sb, int64_t q_sh, int64_t q_ss,

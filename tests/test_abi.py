@@ -74,7 +74,7 @@ FAKE = 1 << 20  # aligned, never dereferenced: every call below fails validation
 
 def lse_call(**over):
     a = dict(q=FAKE, k=FAKE, dtype=0, B=1, Hq=4, Hkv=2, S=64, d=128, q_sb=0, q_sh=64 * 128,
-             q_ss=128, k_sb=0, k_sh=64 * 128, k_ss=128, scale=0.0, lse=FAKE, stream=None)
+             q_ss=128, k_sb=0, k_sh=64 * 128, k_ss=128, scale=0.0, knorm=None, lse=FAKE, stream=None)
     a.update(over)
     return fam.load().fam_lse(*a.values())
 
@@ -88,6 +88,18 @@ def lse_call(**over):
 def test_fam_lse_validation(over, status):
     assert lse_call(**over) == status
     assert fam.load().fam_last_error() != b""
+
+
+def test_key_norm_parts_and_validation():
+    lib = fam.load()
+    assert [lib.fam_key_norm_parts(S) for S in (0, 1, 63, 64, 131072)] == [0, 1, 63, 64, 64]
+    args = [FAKE, 0, 1, 2, 100, 128, 0, 12800, 128, FAKE, None]
+    bad = list(args); bad[9] = None
+    assert lib.fam_key_norms(*bad) == INVALID
+    bad = list(args); bad[5] = 96
+    assert lib.fam_key_norms(*bad) == UNSUPPORTED
+    bad = list(args); bad[8] = 132
+    assert lib.fam_key_norms(*bad) == INVALID
 
 
 def test_fam_mass_and_compute_validation():

@@ -232,10 +232,93 @@ def test_deterministic_bitwise():
 
 
 def test_separate_passes_match_compute():
-    say("fam_lse + fam_mass == fam_compute")
+    """fam_compute shifts the exponentials by a key-norm bound, fam_lse by the
+    running maximum; both must meet the oracle and agree to fp32 rounding."""
+    say("fam_lse + fam_mass vs fam_compute")
     q, k = rand_inputs(22, 1, 4, 1, 999, 64, torch.bfloat16)
-    q, k = q.to(DEV), k.to(DEV)
-    lse = fam.fam_lse(q, k)
-    mass = fam.fam_mass(q, k, lse, 17)
-    lse2, mass2 = fam.fam_compute(q, k, 17)
-    assert torch.equal(lse, lse2) and torch.equal(mass, mass2)
+    qd, kd = q.to(DEV), k.to(DEV)
+    lse = fam.fam_lse(qd, kd)
+    mass = fam.fam_mass(qd, kd, lse, 17)
+    lse2, mass2 = fam.fam_compute(qd, kd, 17)
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), 17)
+    for l_, m_ in ((lse, mass), (lse2, mass2)):
+        check_lse(l_.cpu().numpy(), lse_ref)
+        check_mass(m_.cpu().numpy(), mass_ref, 999, 17)
+    assert (lse - lse2).abs().max().item() <= 1e-5
+    pos = mass2 > 0
+    assert ((mass - mass2).abs()[pos] / mass2[pos]).max().item() <= 1e-5
+
+
+def orthogonal_big_norm_inputs(S, d, big, seed):
+    """Queries and keys whose large components lie in different coordinates:
+    the logits stay O(1) while |q| * |k| is huge, so the Cauchy-Schwarz row
+    bound is far too high and every row's bounded sum underflows."""
+    g = torch.Generator().manual_seed(seed)
+    q = torch.randn(1, 2, S, d, generator=g)
+    k = torch.randn(1, 1, S, d, generator=g)
+    q[..., 0], q[..., 1] = big, 0.0       # query rows: large along axis 0
+    k[..., 0], k[..., 1] = 0.0, 0.0
+    k[0, 0, 0, 1] = big                   # one key: large along axis 1
+    return q.to(torch.bfloat16), k.to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("S,big", [(300, 200.0), (2049, 64.0)])
+def test_loose_bound_falls_back_to_running_max(S, big):
+    say(f"loose key-norm bound S={S} big={big}")
+    q, k = orthogonal_big_norm_inputs(S, 128, big, seed=S)
+    W = 9
+    lse, mass = fam.fam_compute(q.to(DEV), k.to(DEV), W)
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), W)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, S, W)
+
+
+def test_moderately_loose_bound_without_fallback():
+    """One key six times longer than the rest: the bound exceeds most rows'
+    maxima by tens of log2 units but the sums stay far above the fallback
+    threshold."""
+    say("moderately loose bound")
+    q, k = rand_inputs(23, 1, 8, 2, 1500, 128, torch.bfloat16)
+    k[0, :, 7] *= 6
+    lse, mass = fam.fam_compute(q.to(DEV), k.to(DEV), 20)
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), 20)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, 1500, 20)
+
+
+@pytest.mark.parametrize("B,H,S,d,dtype", [(1, 8, 131072, 128, torch.bfloat16), (2, 3, 100, 128, torch.bfloat16),
+                                           (1, 2, 5, 64, torch.float16), (1, 1, 4097, 64, torch.bfloat16)])
+def test_key_norms_against_float64(B, H, S, d, dtype):
+    say(f"key norms B={B} H={H} S={S} d={d} {dtype}")
+    g = torch.Generator().manual_seed(S)
+    k = (torch.randn(B, H, S, d, generator=g) * 3).to(dtype)
+    kn = fam.fam_key_norms(k.to(DEV)).cpu().double()
+    P = fam.fam_key_norm_parts(S)
+    chunk = -(-S // P)
+    sq = (k.double() ** 2).sum(-1)
+    padded = torch.zeros(B, H, P * chunk, dtype=torch.float64)
+    padded[..., :S] = sq
+    ref = padded.view(B, H, P, chunk).max(-1).values
+    assert kn.shape == (B, H, P)
+    assert ((kn - ref).abs() / ref.clamp_min(1e-30)).max().item() <= 1e-5
+
+
+@pytest.mark.parametrize("seed,S,d,W", [(24, 777, 128, 5), (25, 2050, 64, 300)])
+def test_lse_bounded_form_against_oracle(seed, S, d, W):
+    say(f"fam_lse with key norms S={S} d={d}")
+    q, k = rand_inputs(seed, 1, 8, 2, S, d, torch.bfloat16, spread=1.3)
+    qd, kd = q.to(DEV), k.to(DEV)
+    kn = fam.fam_key_norms(kd)
+    lse = fam.fam_lse(qd, kd, knorm=kn)
+    mass = fam.fam_mass(qd, kd, lse, W)
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), W)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, S, W)
+
+
+def test_lse_bounded_form_fallback():
+    say("fam_lse with key norms, loose bound")
+    q, k = orthogonal_big_norm_inputs(640, 128, 100.0, seed=7)
+    qd, kd = q.to(DEV), k.to(DEV)
+    lse = fam.fam_lse(qd, kd, knorm=fam.fam_key_norms(kd))
+    check_lse(lse.cpu().numpy()[0], fo.causal_lse(to64(q)[0], to64(k)[0]))
