@@ -155,19 +155,15 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
 
   // staging: a uniform tile pointer plus fixed per-thread 32-bit offsets; the
   // ragged last tile clamps its rows (keys >= S are masked in the update)
-  int off[CHUNKS];
-#pragma unroll
-  for (int c = 0; c < CHUNKS; ++c) {
-    const int id = tid + c * kThreads;
-    off[c] = (id / CPR) * (int)p.k_ss + (id % CPR) * 8;
-  }
+  const int off0 = (tid / CPR) * (int)p.k_ss + (tid % CPR) * 8;
+  const int pass_stride = (kThreads / CPR) * (int)p.k_ss;   // uniform: chunk c at off0 + c * pass_stride
   u32x4_t st[CHUNKS];
   auto load_tile = [&](int t) {
     const int r0 = t * kKeyTile;
     if (r0 + kKeyTile <= p.S) {
       const uint16_t* tile = kbase + (int64_t)r0 * p.k_ss;
 #pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off[c]);
+      for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off0 + c * pass_stride);
     } else {
 #pragma unroll
       for (int c = 0; c < CHUNKS; ++c) {
@@ -177,13 +173,10 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
       }
     }
   };
+  const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
   auto store_tile = [&](int buf) {
 #pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-      const int id = tid + c * kThreads;
-      const int r = id / CPR, ch = id % CPR;
-      store16(&sk[buf][r * PITCH + ch * 8], st[c]);
-    }
+    for (int c = 0; c < CHUNKS; ++c) store16(&sk[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
   };
 
   float* lse_row = p.lse + ((int64_t)b * p.Hq + qh) * p.S + q0;

@@ -19,7 +19,8 @@
 //     run at the same time read the same Q tiles (the L2 absorbs most of the
 //     re-reads). Each (tile, head) step stages 64 query rows and their
 //     normalisers (in base-2 units) through double-buffered LDS; the tile
-//     base is a uniform pointer and each thread keeps fixed 32-bit offsets.
+//     base is a uniform pointer and a thread's chunks sit at one 32-bit
+//     offset plus multiples of a uniform stride (no per-chunk registers).
 //   * Only band steps (those that contain some i < j + W) evaluate the window
 //     predicate. Keys that no query can reach (j > S - 1 - W) get exactly 0.
 //   * Per-step partial sums are added into a mid-level accumulator that is
@@ -103,14 +104,10 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const int t_full = (j0 + kKeysPerWG - 1 + p.W + kQTile - 1) / kQTile;
     const int nfull = max(0, t1 - max(t_full, t0)) * g;
 
-    // per-thread staging offsets (elements) inside a tile, fixed for the whole loop
-    // (the host guarantees kQTile * q_ss < 2^31, so tile offsets fit in 32 bits)
-    int off[CHUNKS];
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) {
-      const int id = tid + c * kThreads;
-      off[c] = (id / CPR) * (int)p.q_ss + (id % CPR) * 8;
-    }
+    // staging offsets (elements) inside a tile: chunk c of this thread is
+    // off0 + c * pass_stride (the host guarantees kQTile * q_ss < 2^31)
+    const int off0 = (tid / CPR) * (int)p.q_ss + (tid % CPR) * 8;
+    const int pass_stride = (kThreads / CPR) * (int)p.q_ss;   // uniform
     const uint16_t* qgroup = p.q + b * p.q_sb + (int64_t)(h * g) * p.q_sh;
     const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.S;
     u32x4_t st[CHUNKS];
@@ -122,7 +119,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       const uint16_t* tile = qgroup + gi * p.q_sh + (int64_t)r0 * p.q_ss;   // uniform
       if (r0 + kQTile <= p.S) {
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off[c]);
+        for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off0 + c * pass_stride);
       } else {  // ragged last tile: clamp rows (their normaliser is +inf)
 #pragma unroll
         for (int c = 0; c < CHUNKS; ++c) {
@@ -137,12 +134,10 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         lst = row < p.S ? x : kInf;
       }
     };
+    const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
     auto store_step = [&](int buf) {
 #pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int id = tid + c * kThreads;
-        store16(&sq[buf][(id / CPR) * PITCH + (id % CPR) * 8], st[c]);
-      }
+      for (int c = 0; c < CHUNKS; ++c) store16(&sq[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
       if (tid < kQTile) sl[buf][tid] = lst * kLog2e;
     };
 
