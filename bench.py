@@ -113,6 +113,47 @@ def cpu_baseline(wl, prefix=32768):
                        f"({g} query heads) of {wl.name}; {pairs} causal pairs")}
 
 
+def kvpop_target_row(steps, q, k, lse, wl, work, stream):
+    """Time the widened row apart from the step: per-query-head mass (the
+    second pass writing [B, Hq, S]) and the KVpop epilogue (count
+    normalisation, log, max over the group)."""
+    B, Hq, Hkv, S = 1, wl.Hq, wl.Hkv, wl.S
+    mass_q = torch.empty((B, Hq, S), dtype=torch.float32, device=q.device)
+    target = torch.empty((B, Hkv, S), dtype=torch.float32, device=q.device)
+
+    def run(e=None):
+        if e:
+            e[0].record(stream)
+        fam.fam_mass_per_head(q, k, lse, wl.W, mass_q=mass_q)
+        if e:
+            e[1].record(stream)
+        fam.fam_kvpop_target(mass_q, Hkv, wl.W, eps=0.0, aggregate="max", target=target)
+        if e:
+            e[2].record(stream)
+
+    run()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e in ev:
+        run(e)
+    torch.cuda.synchronize()
+    mq_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in ev]))
+    tg_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in ev]))
+    tg_bytes = 4 * B * Hq * S + 4 * B * Hkv * S
+    mq_flops = work["mass_flops"] / (mq_ms * 1e-3)
+    tg_bw = tg_bytes / (tg_ms * 1e-3)
+    return {
+        "fam_mass_per_head": {"bound": "mfma", "achieved": round(mq_flops / 1e12, 3),
+                              "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                              "frac": round(mq_flops / PEAK_BF16_FLOPS, 4), "ms": round(mq_ms, 4)},
+        "fam_kvpop_target": {"bound": "hbm", "achieved": round(tg_bw / 1e9, 3),
+                             "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                             "frac": round(tg_bw / PEAK_HBM_BYTES, 4), "ms": round(tg_ms, 4),
+                             "bytes": tg_bytes},
+        "steps": steps,
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -120,6 +161,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="llama-128k", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--target-steps", type=int, default=2,
+                    help="timed runs of the KVpop target row (per-head mass + epilogue); 0 skips it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -233,6 +276,8 @@ def main():
         "roofline": dict(roof[dominant], kernel=dominant),
         "roofline_all": roof,
     }
+    if args.target_steps > 0:
+        out["kvpop_target"] = kvpop_target_row(args.target_steps, q, k, lse, wl, work, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

@@ -22,7 +22,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfam.so")
 ARCH = "gfx950"
 
-SOURCES = ["fam_api.cpp", "fam_lse.hip", "fam_mass.hip", "evict_select.hip", "kv_compact.hip"]
+SOURCES = ["fam_api.cpp", "fam_lse.hip", "fam_mass.hip", "kvpop_target.hip", "evict_select.hip",
+           "kv_compact.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

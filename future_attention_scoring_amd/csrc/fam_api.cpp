@@ -158,6 +158,39 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
   return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_mass launch");
 }
 
+fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype, int B,
+                             int Hq, int Hkv, int S, int d, int64_t q_sb, int64_t q_sh,
+                             int64_t q_ss, int64_t k_sb, int64_t k_sh, int64_t k_ss, int W,
+                             float scale, float* mass_q, void* stream) {
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  fam_status st = check_scores(q, k, dtype, s);
+  if (st != FAM_OK) return st;
+  if (!lse || !mass_q) return fail(FAM_ERR_INVALID_ARG, "lse and mass_q must be non-null");
+  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  fam::MassArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, nullptr,
+                  q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
+                  W < S ? W : S, resolve_scale(scale, d), mass_q};
+  return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
+                    "fam_mass_per_head launch");
+}
+
+fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, int W, float eps,
+                            fam_aggregate aggregate, float* target, void* stream) {
+  if (!mass_q || !target) return fail(FAM_ERR_INVALID_ARG, "mass_q and target must be non-null");
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1)
+    return fail(FAM_ERR_INVALID_ARG, "B, Hq, Hkv and S must be >= 1 (got %d, %d, %d, %d)", B, Hq, Hkv, S);
+  if (Hq % Hkv != 0) return fail(FAM_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", Hq, Hkv);
+  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FAM_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (aggregate != FAM_AGG_MAX && aggregate != FAM_AGG_MEAN)
+    return fail(FAM_ERR_INVALID_ARG, "aggregate %d is not FAM_AGG_MAX or FAM_AGG_MEAN", (int)aggregate);
+  if ((reinterpret_cast<uintptr_t>(mass_q) | reinterpret_cast<uintptr_t>(target)) & 3u)
+    return fail(FAM_ERR_INVALID_ARG, "mass_q and target must be 4-byte aligned");
+  const fam::TargetArgs a{mass_q, target, B, Hq, Hkv, S, W, eps, aggregate == FAM_AGG_MEAN ? 1 : 0};
+  return hip_status(fam::launch_target(a, static_cast<hipStream_t>(stream)), "fam_kvpop_target launch");
+}
+
 fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
                        int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
                        int64_t k_ss, int W, float scale, float* lse, float* mass, void* stream) {

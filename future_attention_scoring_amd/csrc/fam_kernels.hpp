@@ -37,8 +37,19 @@ struct MassArgs {
   int64_t k_sb, k_sh, k_ss;
   int B, Hq, Hkv, S, d, g, W;
   float c;  // scale * log2(e)
+  float* mass_q;  // non-null: per-query-head mass [B, Hq, S] instead of `mass`
 };
 hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s);
+
+// KVpop supervision target from per-query-head mass.
+struct TargetArgs {
+  const float* mass_q;  // [B, Hq, S]
+  float* target;        // [B, Hkv, S]
+  int B, Hq, Hkv, S, W;
+  float eps;
+  int mean;             // 0: max over the group of the logs; 1: log of the group mean
+};
+hipError_t launch_target(const TargetArgs& a, hipStream_t s);
 
 // Per-head selection. Heads are launched in batches of up to kSelectBatch
 // whose plan travels in the kernel arguments; each head's candidates are

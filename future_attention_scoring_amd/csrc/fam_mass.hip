@@ -63,7 +63,11 @@ __device__ __forceinline__ float block_sum_band(const f32x16_t& acc, const float
   return sum16(e);
 }
 
-template <int D, typename T>
+// PER_HEAD: the steps run head-major (all tiles of one query head, then the
+// next) and each query head's column sums go to mass_q [B, Hq, S] when its
+// last tile is done; otherwise the steps interleave the heads tile by tile
+// and the group sum goes to mass [B, Hkv, S].
+template <int D, typename T, bool PER_HEAD>
 __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   constexpr int PITCH = D + 8;
   constexpr int KS = D / 16;
@@ -94,15 +98,30 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   }
 
   float top[2] = {0.f, 0.f}, mid[2] = {0.f, 0.f};
+  // this wave's column sums (the two half-waves added) into dst[key]
+  auto write_cols = [&](float* dst) {
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      float tot = top[blk] + mid[blk];
+      tot += __shfl_xor(tot, 32);
+      const int key = jw + 32 * blk + col;
+      if (half == 0 && key < p.S) dst[key] = tot;
+    }
+  };
   const int i_first = j0 + p.W;
   if (i_first < p.S) {
     const int g = p.g;
     const int t0 = i_first / kQTile;
     const int t1 = (p.S + kQTile - 1) / kQTile;
-    const int nsteps = (t1 - t0) * g;
+    const int ntiles = t1 - t0;
+    const int nsteps = ntiles * g;
     // tiles t >= t_full have every row i >= j0 + 255 + W: no predicate needed
     const int t_full = (j0 + kKeysPerWG - 1 + p.W + kQTile - 1) / kQTile;
-    const int nfull = max(0, t1 - max(t_full, t0)) * g;
+    const int nfull_h = max(0, t1 - max(t_full, t0));   // per query head
+    // step u -> (tile, query head of the group); the latest tiles come first
+    auto tile_of = [&](int u) { return PER_HEAD ? t1 - 1 - u % ntiles : t1 - 1 - u / g; };
+    auto head_of = [&](int u) { return PER_HEAD ? u / ntiles : u % g; };
+    auto is_full = [&](int u) { return PER_HEAD ? u % ntiles < nfull_h : u < nfull_h * g; };
 
     // staging offsets (elements) inside a tile: chunk c of this thread is
     // off0 + c * pass_stride (the host guarantees kQTile * q_ss < 2^31)
@@ -113,8 +132,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     u32x4_t st[CHUNKS];
     float lst = 0.f;
     auto load_step = [&](int u) {
-      const int t = t1 - 1 - u / g;
-      const int gi = u % g;
+      const int t = tile_of(u);
+      const int gi = head_of(u);
       const int r0 = t * kQTile;
       const uint16_t* tile = qgroup + gi * p.q_sh + (int64_t)r0 * p.q_ss;   // uniform
       if (r0 + kQTile <= p.S) {
@@ -148,8 +167,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       const bool more = u + 1 < nsteps;
       if (more) load_step(u + 1);
       const int buf = u & 1;
-      const int i0t = (t1 - 1 - u / g) * kQTile;
-      const bool full = u < nfull;
+      const int i0t = tile_of(u) * kQTile;
+      const bool full = is_full(u);
 #pragma unroll
       for (int rb = 0; rb < kQTile / 32; ++rb) {
         const int i0 = i0t + 32 * rb;
@@ -185,17 +204,19 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         mid[0] = 0.f;
         mid[1] = 0.f;
       }
+      if (PER_HEAD && u % ntiles == ntiles - 1) {  // this query head is complete
+        write_cols(p.mass_q + ((int64_t)b * p.Hq + h * g + head_of(u)) * p.S);
+        top[0] = top[1] = mid[0] = mid[1] = 0.f;
+      }
       if (more) store_step((u + 1) & 1);
       __syncthreads();
     }
   }
 
-#pragma unroll
-  for (int blk = 0; blk < 2; ++blk) {
-    float tot = top[blk] + mid[blk];
-    tot += __shfl_xor(tot, 32);
-    const int key = jw + 32 * blk + col;
-    if (half == 0 && key < p.S) p.mass[((int64_t)b * p.Hkv + h) * p.S + key] = tot;
+  if (!PER_HEAD) {
+    write_cols(p.mass + ((int64_t)b * p.Hkv + h) * p.S);
+  } else if (i_first >= p.S) {  // no future query: every head's mass is 0
+    for (int gi = 0; gi < p.g; ++gi) write_cols(p.mass_q + ((int64_t)b * p.Hq + h * p.g + gi) * p.S);
   }
 }
 
@@ -204,7 +225,10 @@ hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   const int nkb = (a.S + kKeysPerWG - 1) / kKeysPerWG;
   const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  hipLaunchKernelGGL((mass_kernel<D, T>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  if (a.mass_q)
+    hipLaunchKernelGGL((mass_kernel<D, T, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  else
+    hipLaunchKernelGGL((mass_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -32,6 +32,9 @@ _SIGNATURES = {
                      _p]),
     "fam_mass": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
                       _i, _f, _p, _p]),
+    "fam_mass_per_head": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
+                               _i64, _i, _f, _p, _p]),
+    "fam_kvpop_target": (_i, [_p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "fam_compute": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
                          _i, _f, _p, _p, _p]),
     "evict_plan": (_i, [_i, _i, _p, _i, _i, _p, _p]),
@@ -159,6 +162,42 @@ def fam_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
                            Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
                            0.0 if scale is None else scale, mass.data_ptr(), _stream(q4)))
     return mass if q.dim() == 4 else mass[0]
+
+
+def fam_mass_per_head(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
+                      scale: Optional[float] = None, mass_q: Optional[torch.Tensor] = None
+                      ) -> torch.Tensor:
+    q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
+    lse = lse.contiguous()
+    if lse.numel() != B * Hq * S or lse.dtype != torch.float32:
+        raise FamError(1, "lse must be fp32 [B, Hq, S]")
+    if mass_q is None:
+        mass_q = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
+    _check(load().fam_mass_per_head(q4.data_ptr(), k4.data_ptr(), lse.data_ptr(), _dtype_code(q4),
+                                    B, Hq, Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
+                                    0.0 if scale is None else scale, mass_q.data_ptr(),
+                                    _stream(q4)))
+    return mass_q if q.dim() == 4 else mass_q[0]
+
+
+FAM_AGG = {"max": 0, "mean": 1}
+
+
+def fam_kvpop_target(mass_q: torch.Tensor, Hkv: int, W: int, eps: float = 0.0,
+                     aggregate: str = "max", target: Optional[torch.Tensor] = None
+                     ) -> torch.Tensor:
+    """KVpop target [B, Hkv, S] (or [Hkv, S]) from per-query-head mass [B, Hq, S]."""
+    m = mass_q if mass_q.dim() == 3 else mass_q.unsqueeze(0)
+    if m.dim() != 3 or m.dtype != torch.float32 or not m.is_cuda or not m.is_contiguous():
+        raise FamError(1, "mass_q must be a contiguous device fp32 [B, Hq, S] tensor")
+    if aggregate not in FAM_AGG:
+        raise FamError(1, f"aggregate must be one of {sorted(FAM_AGG)}")
+    B, Hq, S = m.shape
+    if target is None:
+        target = torch.empty((B, int(Hkv), S), dtype=torch.float32, device=m.device)
+    _check(load().fam_kvpop_target(m.data_ptr(), B, Hq, int(Hkv), S, int(W), float(eps),
+                                   FAM_AGG[aggregate], target.data_ptr(), _stream(m)))
+    return target if mass_q.dim() == 3 else target[0]
 
 
 def fam_compute(q: torch.Tensor, k: torch.Tensor, W: int, scale: Optional[float] = None,

@@ -138,6 +138,51 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
                     int64_t k_sb, int64_t k_sh, int64_t k_ss,
                     int W, float scale, float* mass, void* stream);
 
+/* ------------------------------------------------------------------------
+ * fam_mass_per_head -- the future-attention mass of each query head.
+ *
+ * [KVpop] "Defining Future Attention Utility" (worked example: the future
+ * attention of each query head is kept separately before aggregation) and
+ * the appendix on the transposed pass:
+ *
+ *   mass_q[b, qh, j] = sum_{i = j + W}^{S - 1}
+ *                      exp(scale * <q[b,qh,i,:], k[b,qh/g,j,:]> - lse[b,qh,i])
+ *
+ * so that fam_mass's output is the sum of mass_q over each group. Keys
+ * j > S - 1 - W get exactly 0.
+ *
+ *   mass_q  device out, [B, Hq, S] fp32, contiguous, fully overwritten
+ *   other arguments, requirements and errors as for fam_mass.
+ * ---------------------------------------------------------------------- */
+fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype,
+                             int B, int Hq, int Hkv, int S, int d,
+                             int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                             int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                             int W, float scale, float* mass_q, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fam_kvpop_target -- KVpop's supervision target from per-head mass.
+ *
+ * [KVpop] "Defining Future Attention Utility" (count normalisation and the
+ * log of the mean future mass, max over the query heads of a KV head) and
+ * the appendix "Alternative Aggregation Methods" (mean in probability space
+ * before the log). With N_j = max(1, S - (j + W)) and g = Hq / Hkv:
+ *
+ *   FAM_AGG_MAX:  target[b,h,j] = max_{qh in group h} log(eps + mass_q[b,qh,j] / N_j)
+ *   FAM_AGG_MEAN: target[b,h,j] = log(eps + (sum_{qh in group h} mass_q[b,qh,j]) / (g N_j))
+ *
+ * With eps = 0 a key with zero mass gets -inf.
+ *
+ *   mass_q  device, [B, Hq, S] fp32 contiguous (normally fam_mass_per_head's)
+ *   W       protected window (>= 0), as used for mass_q
+ *   eps     >= 0, finite
+ *   target  device out, [B, Hkv, S] fp32, contiguous, fully overwritten
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+typedef enum { FAM_AGG_MAX = 0, FAM_AGG_MEAN = 1 } fam_aggregate;
+fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, int W, float eps,
+                            fam_aggregate aggregate, float* target, void* stream);
+
 /* fam_compute -- fam_key_norms, fam_lse (bounded form) and fam_mass on the
  * same stream. The key-norm partial maxima are kept in the first entries of
  * `mass` until the mass pass overwrites it, so no workspace is needed. */

@@ -102,6 +102,30 @@ def test_key_norm_parts_and_validation():
     assert lib.fam_key_norms(*bad) == INVALID
 
 
+def test_kvpop_target_validation():
+    lib = fam.load()
+    ok = [FAKE, 1, 4, 2, 100, 8, 0.0, 0, FAKE, None]
+    for i, v in ((0, None), (8, None), (2, 3), (3, 0), (4, 0), (5, -1), (6, -1.0), (6, float("nan")),
+                 (6, float("inf")), (7, 2), (0, FAKE + 2)):
+        bad = list(ok)
+        bad[i] = v
+        assert lib.fam_kvpop_target(*bad) == INVALID, (i, v)
+        assert lib.fam_last_error() != b""
+
+
+def test_mass_per_head_validation():
+    lib = fam.load()
+    args = [FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE, None]
+    bad = list(args); bad[17] = None
+    assert lib.fam_mass_per_head(*bad) == INVALID
+    bad = list(args); bad[15] = -1
+    assert lib.fam_mass_per_head(*bad) == INVALID
+    bad = list(args); bad[5] = 3
+    assert lib.fam_mass_per_head(*bad) == INVALID
+    bad = list(args); bad[8] = 96
+    assert lib.fam_mass_per_head(*bad) == UNSUPPORTED
+
+
 def test_fam_mass_and_compute_validation():
     lib = fam.load()
     st = lib.fam_mass(FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, -1, 0.0, FAKE, None)
