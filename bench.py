@@ -202,6 +202,7 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     knorm = torch.empty((B, Hkv, fam.fam_key_norm_parts(S)), dtype=torch.float32, device=dev)
+    mass_ws = torch.empty(fam.fam_mass_workspace_size(B, Hq, Hkv, S), dtype=torch.uint8, device=dev)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
 
     def step(events=None):
@@ -211,7 +212,7 @@ def main():
         fam.fam_lse(q, k, lse=lse, knorm=knorm)
         if events:
             events[1].record(stream)
-        fam.fam_mass(q, k, lse, wl.W, mass=mass)
+        fam.fam_mass(q, k, lse, wl.W, mass=mass, workspace=mass_ws)
         if events:
             events[2].record(stream)
         fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets,

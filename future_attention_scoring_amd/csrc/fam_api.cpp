@@ -86,6 +86,14 @@ fam::LseArgs lse_args(const void* q, const void* k, const ScoreShape& s, float s
   return a;
 }
 
+// Splits of the mass pass: aim at >= 3072 workgroups (three per CU on 256
+// CUs, with room for the uneven column lengths), at most 16.
+int mass_splits(int B, int Hkv, int S) {
+  const int64_t wgs = (int64_t)((S + fam::kMassKeysPerWG - 1) / fam::kMassKeysPerWG) * B * Hkv;
+  const int64_t n = (3072 + wgs - 1) / wgs;
+  return (int)(n < 1 ? 1 : (n > 16 ? 16 : n));
+}
+
 fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
 
 // Forced set and candidate range for a head of length S.
@@ -143,18 +151,34 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq,
   return hip_status(fam::launch_lse(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_lse launch");
 }
 
+size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0) return 0;
+  const int n = mass_splits(B, Hkv, S);
+  return n > 1 ? (size_t)n * B * Hkv * S * sizeof(float) : 0;
+}
+
 fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype, int B, int Hq,
                     int Hkv, int S, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb,
-                    int64_t k_sh, int64_t k_ss, int W, float scale, float* mass, void* stream) {
+                    int64_t k_sh, int64_t k_ss, int W, float scale, float* mass, void* workspace,
+                    size_t workspace_bytes, void* stream) {
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  if (workspace && !aligned16(workspace))
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  // as many splits as wanted and as the workspace holds (none without one)
+  const size_t per_split = (size_t)B * Hkv * S * sizeof(float);
+  int nsplit = mass_splits(B, Hkv, S);
+  if (!workspace) nsplit = 1;
+  if ((size_t)nsplit * per_split > workspace_bytes) nsplit = (int)(workspace_bytes / per_split);
+  if (nsplit < 2) nsplit = 1;
   fam::MassArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, mass,
                   q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
-                  W < S ? W : S, resolve_scale(scale, d)};
+                  W < S ? W : S, resolve_scale(scale, d), nullptr,
+                  nsplit > 1 ? static_cast<float*>(workspace) : nullptr, nsplit};
   return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_mass launch");
 }
 
@@ -170,7 +194,7 @@ fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
   fam::MassArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, nullptr,
                   q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
-                  W < S ? W : S, resolve_scale(scale, d), mass_q};
+                  W < S ? W : S, resolve_scale(scale, d), mass_q, nullptr, 1};
   return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
                     "fam_mass_per_head launch");
 }
@@ -193,7 +217,8 @@ fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, 
 
 fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
                        int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
-                       int64_t k_ss, int W, float scale, float* lse, float* mass, void* stream) {
+                       int64_t k_ss, int W, float scale, float* lse, float* mass,
+                       void* workspace, size_t workspace_bytes, void* stream) {
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
@@ -209,7 +234,7 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int
   e = fam::launch_lse(a, elem_of(dtype), hs);
   if (e != hipSuccess) return hip_status(e, "fam_compute lse launch");
   return fam_mass(q, k, lse, dtype, B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, W, scale,
-                  mass, stream);
+                  mass, workspace, workspace_bytes, stream);
 }
 
 fam_status evict_plan(int H, int S, const int64_t* budgets, int sinks, int recent, int64_t* kept,

@@ -38,7 +38,13 @@ struct MassArgs {
   int B, Hq, Hkv, S, d, g, W;
   float c;  // scale * log2(e)
   float* mass_q;  // non-null: per-query-head mass [B, Hq, S] instead of `mass`
+  // Split of each key block's query tiles over nsplit workgroups (group-sum
+  // mode only): with nsplit > 1 the partial sums go to part [nsplit, B*Hkv*S]
+  // and a reduction adds them into `mass` in a fixed order.
+  float* part;
+  int nsplit;
 };
+constexpr int kMassKeysPerWG = 256;   // keys owned by one mass-pass workgroup
 hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s);
 
 // KVpop supervision target from per-query-head mass.

@@ -29,6 +29,10 @@
 //   * Workgroups are numbered earliest-key-first (the longest columns start
 //     first) with the (batch, KV head) index fastest, so with eight KV heads
 //     every XCD works on one head.
+//   * Short sequences give too few (and very unequal) key blocks to fill the
+//     chip, so the host may split each key block's steps over nsplit
+//     workgroups; their partial sums go to a caller workspace and a second
+//     launch adds them in split order (deterministic).
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -39,6 +43,7 @@ constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWG = kKeysPerWave * kWaves;
+static_assert(kKeysPerWG == kMassKeysPerWG, "host and kernel key-block size");
 constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
 
 // Sum of exp2(c*s - L) over one 32x32 block, no window predicate.
@@ -78,7 +83,9 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
 
   const int nbh = p.B * p.Hkv;
   const int bh = blockIdx.x % nbh;
-  const int kbi = blockIdx.x / nbh;
+  const int rest = blockIdx.x / nbh;
+  const int split = PER_HEAD ? 0 : rest % p.nsplit;
+  const int kbi = PER_HEAD ? rest : rest / p.nsplit;
   const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -160,11 +167,16 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       if (tid < kQTile) sl[buf][tid] = lst * kLog2e;
     };
 
-    load_step(0);
-    store_step(0);
-    __syncthreads();
-    for (int u = 0; u < nsteps; ++u) {
-      const bool more = u + 1 < nsteps;
+    // this workgroup's share of the key block's steps
+    const int u_begin = PER_HEAD ? 0 : (int)((int64_t)nsteps * split / p.nsplit);
+    const int u_end = PER_HEAD ? nsteps : (int)((int64_t)nsteps * (split + 1) / p.nsplit);
+    if (u_begin < u_end) {
+      load_step(u_begin);
+      store_step(u_begin & 1);
+      __syncthreads();
+    }
+    for (int u = u_begin; u < u_end; ++u) {
+      const bool more = u + 1 < u_end;
       if (more) load_step(u + 1);
       const int buf = u & 1;
       const int i0t = tile_of(u) * kQTile;
@@ -214,21 +226,41 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   }
 
   if (!PER_HEAD) {
-    write_cols(p.mass + ((int64_t)b * p.Hkv + h) * p.S);
+    write_cols(p.nsplit > 1 ? p.part + ((int64_t)split * nbh + bh) * p.S
+                            : p.mass + ((int64_t)b * p.Hkv + h) * p.S);
   } else if (i_first >= p.S) {  // no future query: every head's mass is 0
     for (int gi = 0; gi < p.g; ++gi) write_cols(p.mass_q + ((int64_t)b * p.Hq + h * p.g + gi) * p.S);
+  }
+}
+
+// mass = sum over the splits of the partial column sums, in split order.
+__global__ __launch_bounds__(kThreads) void mass_reduce_kernel(const float* part, float* mass,
+                                                               int64_t n, int nsplit) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
+    float acc = part[e];
+    for (int k = 1; k < nsplit; ++k) acc += part[(int64_t)k * n + e];
+    mass[e] = acc;
   }
 }
 
 template <int D, typename T>
 hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   const int nkb = (a.S + kKeysPerWG - 1) / kKeysPerWG;
-  const int64_t grid = (int64_t)nkb * a.B * a.Hkv;
+  const int nsplit = a.mass_q ? 1 : a.nsplit;
+  const int64_t grid = (int64_t)nkb * nsplit * a.B * a.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.mass_q)
+  if (a.mass_q) {
     hipLaunchKernelGGL((mass_kernel<D, T, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  else
+  } else {
     hipLaunchKernelGGL((mass_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+    if (nsplit > 1) {
+      const int64_t n = (int64_t)a.B * a.Hkv * a.S;
+      const int64_t blocks = (n + kThreads - 1) / kThreads;
+      hipLaunchKernelGGL(mass_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                         dim3(kThreads), 0, s, a.part, a.mass, n, nsplit);
+    }
+  }
   return hipGetLastError();
 }
 

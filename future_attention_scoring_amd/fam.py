@@ -31,12 +31,13 @@ _SIGNATURES = {
     "fam_lse": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64, _f, _p, _p,
                      _p]),
     "fam_mass": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
-                      _i, _f, _p, _p]),
+                      _i, _f, _p, _p, ctypes.c_size_t, _p]),
+    "fam_mass_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fam_mass_per_head": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
                                _i64, _i, _f, _p, _p]),
     "fam_kvpop_target": (_i, [_p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "fam_compute": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
-                         _i, _f, _p, _p, _p]),
+                         _i, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "evict_plan": (_i, [_i, _i, _p, _i, _i, _p, _p]),
     "fam_budgets_from_ratios": (_i, [_i, _p, _i64, _p]),
     "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
@@ -150,17 +151,36 @@ def fam_lse(q: torch.Tensor, k: torch.Tensor, scale: Optional[float] = None,
     return lse if q.dim() == 4 else lse[0]
 
 
+def fam_mass_workspace_size(B: int, Hq: int, Hkv: int, S: int) -> int:
+    return int(load().fam_mass_workspace_size(int(B), int(Hq), int(Hkv), int(S)))
+
+
+def _mass_workspace(workspace, B, Hq, Hkv, S, device):
+    """The caller's workspace, or one of the recommended size (None if 0)."""
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    n = fam_mass_workspace_size(B, Hq, Hkv, S)
+    if n == 0:
+        return None, 0
+    # freed on return: torch's allocator reuses it only in stream order
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), n
+
+
 def fam_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
-             scale: Optional[float] = None, mass: Optional[torch.Tensor] = None) -> torch.Tensor:
+             scale: Optional[float] = None, mass: Optional[torch.Tensor] = None,
+             workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
     lse = lse.contiguous()
     if lse.numel() != B * Hq * S or lse.dtype != torch.float32:
         raise FamError(1, "lse must be fp32 [B, Hq, S]")
     if mass is None:
         mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
+    ws, nbytes = _mass_workspace(workspace, B, Hq, Hkv, S, q4.device)
     _check(load().fam_mass(q4.data_ptr(), k4.data_ptr(), lse.data_ptr(), _dtype_code(q4), B, Hq,
                            Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
-                           0.0 if scale is None else scale, mass.data_ptr(), _stream(q4)))
+                           0.0 if scale is None else scale, mass.data_ptr(), ws, nbytes,
+                           _stream(q4)))
     return mass if q.dim() == 4 else mass[0]
 
 
@@ -201,17 +221,18 @@ def fam_kvpop_target(mass_q: torch.Tensor, Hkv: int, W: int, eps: float = 0.0,
 
 
 def fam_compute(q: torch.Tensor, k: torch.Tensor, W: int, scale: Optional[float] = None,
-                lse: Optional[torch.Tensor] = None, mass: Optional[torch.Tensor] = None
-                ) -> Tuple[torch.Tensor, torch.Tensor]:
+                lse: Optional[torch.Tensor] = None, mass: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
     if lse is None:
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
     if mass is None:
         mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
+    ws, nbytes = _mass_workspace(workspace, B, Hq, Hkv, S, q4.device)
     _check(load().fam_compute(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv, S, d,
                               *q4.stride()[:3], *k4.stride()[:3], int(W),
                               0.0 if scale is None else scale, lse.data_ptr(), mass.data_ptr(),
-                              _stream(q4)))
+                              ws, nbytes, _stream(q4)))
     if q.dim() == 3:
         return lse.view(Hq, S), mass.view(Hkv, S)
     return lse, mass

@@ -130,13 +130,26 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype,
  *   lse    device, [B, Hq, S] fp32 contiguous (normally fam_lse's output)
  *   W      protected recent window, W >= 0 (W >= S makes every mass 0)
  *   mass   device out, [B, Hkv, S] fp32, contiguous, fully overwritten
+ *   workspace, workspace_bytes
+ *          optional device scratch (16-byte aligned, owned by the caller,
+ *          contents irrelevant on entry and unspecified on return). With
+ *          fam_mass_workspace_size(B, Hq, Hkv, S) bytes, short sequences
+ *          split each key block's queries over several workgroups and add
+ *          the parts in a fixed order (same result up to fp32 rounding;
+ *          deterministic). NULL or fewer bytes: fewer or no splits. Calls
+ *          sharing a workspace must be ordered on one stream.
  *   other arguments and requirements as for fam_lse.
  * ---------------------------------------------------------------------- */
 fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype,
                     int B, int Hq, int Hkv, int S, int d,
                     int64_t q_sb, int64_t q_sh, int64_t q_ss,
                     int64_t k_sb, int64_t k_sh, int64_t k_ss,
-                    int W, float scale, float* mass, void* stream);
+                    int W, float scale, float* mass,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fam_mass and fam_compute use for these sizes (0 when
+ * the sequence fills the chip without splitting, or for invalid sizes). */
+size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S);
 
 /* ------------------------------------------------------------------------
  * fam_mass_per_head -- the future-attention mass of each query head.
@@ -185,12 +198,13 @@ fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, 
 
 /* fam_compute -- fam_key_norms, fam_lse (bounded form) and fam_mass on the
  * same stream. The key-norm partial maxima are kept in the first entries of
- * `mass` until the mass pass overwrites it, so no workspace is needed. */
+ * `mass` until the mass pass overwrites it; the workspace is fam_mass's. */
 fam_status fam_compute(const void* q, const void* k, fam_dtype dtype,
                        int B, int Hq, int Hkv, int S, int d,
                        int64_t q_sb, int64_t q_sh, int64_t q_ss,
                        int64_t k_sb, int64_t k_sh, int64_t k_ss,
-                       int W, float scale, float* lse, float* mass, void* stream);
+                       int W, float scale, float* lse, float* mass,
+                       void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * evict_plan -- host-only budget plan (no device work).

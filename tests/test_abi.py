@@ -128,10 +128,24 @@ def test_mass_per_head_validation():
 
 def test_fam_mass_and_compute_validation():
     lib = fam.load()
-    st = lib.fam_mass(FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, -1, 0.0, FAKE, None)
+    st = lib.fam_mass(FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, -1, 0.0, FAKE,
+                      None, 0, None)
     assert st == INVALID
-    st = lib.fam_compute(FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE, None, None)
+    st = lib.fam_mass(FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE,
+                      FAKE + 4, 1 << 20, None)
+    assert st == INVALID  # misaligned workspace
+    st = lib.fam_compute(FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE, None,
+                         None, 0, None)
     assert st == INVALID
+
+
+def test_mass_workspace_size():
+    lib = fam.load()
+    assert lib.fam_mass_workspace_size(1, 32, 8, 131072) == 0          # fills the chip unsplit
+    n8k = lib.fam_mass_workspace_size(1, 32, 8, 8192)
+    assert n8k > 0 and n8k % (8 * 8192 * 4) == 0 and n8k // (8 * 8192 * 4) <= 16
+    assert lib.fam_mass_workspace_size(1, 3, 2, 100) == 0                # Hq % Hkv != 0
+    assert lib.fam_mass_workspace_size(0, 4, 2, 100) == 0
 
 
 WORKSPACE = 3

@@ -322,3 +322,25 @@ def test_lse_bounded_form_fallback():
     qd, kd = q.to(DEV), k.to(DEV)
     lse = fam.fam_lse(qd, kd, knorm=fam.fam_key_norms(kd))
     check_lse(lse.cpu().numpy()[0], fo.causal_lse(to64(q)[0], to64(k)[0]))
+
+
+@pytest.mark.parametrize("seed,Hq,Hkv,S,d,W", [(41, 8, 2, 3000, 128, 100), (42, 4, 4, 700, 64, 0),
+                                             (43, 32, 8, 8192, 128, 128)])
+def test_split_mass_matches_unsplit_and_oracle(seed, Hq, Hkv, S, d, W):
+    """Short sequences split each key block's queries over several workgroups
+    (workspace of fam_mass_workspace_size bytes); without a workspace the pass
+    runs unsplit. Both meet the oracle and agree to fp32 rounding."""
+    say(f"split mass Hq={Hq} Hkv={Hkv} S={S} W={W}")
+    assert fam.fam_mass_workspace_size(1, Hq, Hkv, S) > 0
+    q, k = rand_inputs(seed, 1, Hq, Hkv, S, d, torch.bfloat16)
+    qd, kd = q.to(DEV), k.to(DEV)
+    lse = fam.fam_lse(qd, kd, knorm=fam.fam_key_norms(kd))
+    split = fam.fam_mass(qd, kd, lse, W)
+    whole = fam.fam_mass(qd, kd, lse, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    pos = whole > 0
+    assert torch.equal(split[~pos], whole[~pos])
+    assert ((split - whole).abs()[pos] / whole[pos]).max().item() <= 1e-5
+    if S <= 3000:
+        lse_ref, mass_ref = fo.fam(to64(q), to64(k), W)
+        check_mass(split.cpu().numpy(), mass_ref, S, W)
+        check_mass(whole.cpu().numpy(), mass_ref, S, W)
