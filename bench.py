@@ -45,6 +45,8 @@ KERNEL_SOURCES = {
     "fam_mass": ["fam_mass.hip", "fam_device.hpp", "fam_kernels.hpp"],
     "evict_select": ["evict_select.hip", "fam_device.hpp", "fam_kernels.hpp"],
     "kv_compact": ["kv_compact.hip", "fam_device.hpp", "fam_kernels.hpp"],
+    "fam_mass_per_head": ["fam_mass.hip", "fam_device.hpp", "fam_kernels.hpp"],
+    "fam_kvpop_target": ["kvpop_target.hip", "fam_device.hpp", "fam_kernels.hpp"],
 }
 
 
@@ -279,6 +281,8 @@ def main():
     }
     if args.target_steps > 0:
         out["kvpop_target"] = kvpop_target_row(args.target_steps, q, k, lse, wl, work, stream)
+        for n in ("fam_mass_per_head", "fam_kvpop_target"):
+            out["kvpop_target"][n]["traffic"] = traffic.get(n)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
