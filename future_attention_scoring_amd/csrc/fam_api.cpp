@@ -40,9 +40,12 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 constexpr int kMaxSeq = 1 << 28;
 constexpr int64_t kMaxRowStride = (int64_t)1 << 24;
 
+// S keys; Sq query rows at the last Sq positions (Sq = 0 stands for Sq = S).
 struct ScoreShape {
   int B, Hq, Hkv, S, d;
   int64_t q_sb, q_sh, q_ss, k_sb, k_sh, k_ss;
+  int Sq;
+  int rows() const { return Sq > 0 ? Sq : S; }
 };
 
 fam_status check_scores(const void* q, const void* k, fam_dtype dtype, const ScoreShape& s) {
@@ -53,6 +56,8 @@ fam_status check_scores(const void* q, const void* k, fam_dtype dtype, const Sco
     return fail(FAM_ERR_INVALID_ARG, "B, Hq, Hkv and S must be >= 1 (got %d, %d, %d, %d)",
                 s.B, s.Hq, s.Hkv, s.S);
   if (s.S > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "S = %d exceeds %d", s.S, kMaxSeq);
+  if (s.Sq < 0 || s.Sq > s.S)
+    return fail(FAM_ERR_INVALID_ARG, "query rows Sq = %d must be in [1, Sk = %d]", s.Sq, s.S);
   if (s.Hq % s.Hkv != 0)
     return fail(FAM_ERR_INVALID_ARG, "Hq (%d) must be a multiple of Hkv (%d)", s.Hq, s.Hkv);
   if (s.d != 64 && s.d != 128) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64 or 128)", s.d);
@@ -79,10 +84,38 @@ float resolve_scale(float scale, int d) {
 // maxima stored there ([B * Hkv][nkn] floats).
 fam::LseArgs lse_args(const void* q, const void* k, const ScoreShape& s, float scale, float* lse,
                       float* knorm) {
-  fam::LseArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse,
-                 s.q_sb, s.q_sh, s.q_ss, s.k_sb, s.k_sh, s.k_ss, s.B, s.Hq, s.Hkv, s.S, s.d,
-                 s.Hq / s.Hkv, resolve_scale(scale, s.d), knorm,
-                 knorm ? fam_key_norm_parts(s.S) : 0};
+  fam::LseArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.lse = lse;
+  a.q_sb = s.q_sb, a.q_sh = s.q_sh, a.q_ss = s.q_ss;
+  a.k_sb = s.k_sb, a.k_sh = s.k_sh, a.k_ss = s.k_ss;
+  a.B = s.B, a.Hq = s.Hq, a.Hkv = s.Hkv, a.S = s.S, a.d = s.d, a.g = s.Hq / s.Hkv;
+  a.Sq = s.rows();
+  a.c = resolve_scale(scale, s.d);
+  a.knorm = knorm;
+  a.nkn = knorm ? fam_key_norm_parts(s.S) : 0;
+  return a;
+}
+
+// Arguments of the mass pass (group sum into `mass` with nsplit splits, or
+// per query head into `mass_q`).
+fam::MassArgs mass_args(const void* q, const void* k, const float* lse, const ScoreShape& s, int W,
+                        float scale, float* mass, float* mass_q, float* part, int nsplit) {
+  fam::MassArgs a{};
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.lse = lse;
+  a.mass = mass;
+  a.q_sb = s.q_sb, a.q_sh = s.q_sh, a.q_ss = s.q_ss;
+  a.k_sb = s.k_sb, a.k_sh = s.k_sh, a.k_ss = s.k_ss;
+  a.B = s.B, a.Hq = s.Hq, a.Hkv = s.Hkv, a.S = s.S, a.d = s.d, a.g = s.Hq / s.Hkv;
+  a.W = W < s.S ? W : s.S;
+  a.Sq = s.rows();
+  a.c = resolve_scale(scale, s.d);
+  a.mass_q = mass_q;
+  a.part = part;
+  a.nsplit = nsplit;
   return a;
 }
 
@@ -95,6 +128,48 @@ int mass_splits(int B, int Hkv, int S) {
 }
 
 fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
+
+// Group-sum mass pass on a validated shape: as many splits as wanted and as
+// the workspace holds (none without one).
+fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype dtype,
+                      const ScoreShape& s, int W, float scale, float* mass, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, const char* what) {
+  if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
+  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  if (workspace && !aligned16(workspace))
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const size_t per_split = (size_t)s.B * s.Hkv * s.S * sizeof(float);
+  int nsplit = mass_splits(s.B, s.Hkv, s.S);
+  if (!workspace) nsplit = 1;
+  if ((size_t)nsplit * per_split > workspace_bytes) nsplit = (int)(workspace_bytes / per_split);
+  if (nsplit < 2) nsplit = 1;
+  const fam::MassArgs a = mass_args(q, k, lse, s, W, scale, mass, nullptr,
+                                    nsplit > 1 ? static_cast<float*>(workspace) : nullptr, nsplit);
+  return hip_status(fam::launch_mass(a, elem_of(dtype), stream), what);
+}
+
+// Key norms, the bounded first pass and the group-sum mass pass. The
+// key-norm partial maxima ([B * Hkv][P] floats, P <= S) occupy the start of
+// `mass` until the mass pass overwrites it.
+fam_status compute_all(const void* q, const void* k, fam_dtype dtype, const ScoreShape& s, int W,
+                       float scale, float* lse, float* mass, void* workspace,
+                       size_t workspace_bytes, hipStream_t hs, const char* who) {
+  if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
+  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  if (workspace && !aligned16(workspace))
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  const fam::LseArgs a = lse_args(q, k, s, scale, lse, mass);
+  std::string what = std::string(who) + " key-norm launch";
+  hipError_t e = fam::launch_knorm(a, elem_of(dtype), hs);
+  if (e != hipSuccess) return hip_status(e, what.c_str());
+  e = fam::launch_lse(a, elem_of(dtype), hs);
+  what = std::string(who) + " lse launch";
+  if (e != hipSuccess) return hip_status(e, what.c_str());
+  what = std::string(who) + " mass launch";
+  return mass_group(q, k, lse, dtype, s, W, scale, mass, workspace, workspace_bytes, hs, what.c_str());
+}
 
 // Forced set and candidate range for a head of length S.
 struct Plan {
@@ -164,22 +239,8 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
-  if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
-  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
-  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
-  if (workspace && !aligned16(workspace))
-    return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  // as many splits as wanted and as the workspace holds (none without one)
-  const size_t per_split = (size_t)B * Hkv * S * sizeof(float);
-  int nsplit = mass_splits(B, Hkv, S);
-  if (!workspace) nsplit = 1;
-  if ((size_t)nsplit * per_split > workspace_bytes) nsplit = (int)(workspace_bytes / per_split);
-  if (nsplit < 2) nsplit = 1;
-  fam::MassArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, mass,
-                  q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
-                  W < S ? W : S, resolve_scale(scale, d), nullptr,
-                  nsplit > 1 ? static_cast<float*>(workspace) : nullptr, nsplit};
-  return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_mass launch");
+  return mass_group(q, k, lse, dtype, s, W, scale, mass, workspace, workspace_bytes,
+                    static_cast<hipStream_t>(stream), "fam_mass launch");
 }
 
 fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype, int B,
@@ -192,9 +253,7 @@ fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam
   if (!lse || !mass_q) return fail(FAM_ERR_INVALID_ARG, "lse and mass_q must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
-  fam::MassArgs a{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), lse, nullptr,
-                  q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, B, Hq, Hkv, S, d, Hq / Hkv,
-                  W < S ? W : S, resolve_scale(scale, d), mass_q, nullptr, 1};
+  const fam::MassArgs a = mass_args(q, k, lse, s, W, scale, nullptr, mass_q, nullptr, 1);
   return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
                     "fam_mass_per_head launch");
 }
@@ -222,19 +281,22 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
-  if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
-  if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
-  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
-  // The key-norm partial maxima ([B * Hkv][P] floats, P <= S) occupy the
-  // start of `mass` until the mass pass overwrites it.
-  const fam::LseArgs a = lse_args(q, k, s, scale, lse, mass);
-  const hipStream_t hs = static_cast<hipStream_t>(stream);
-  hipError_t e = fam::launch_knorm(a, elem_of(dtype), hs);
-  if (e != hipSuccess) return hip_status(e, "fam_compute key-norm launch");
-  e = fam::launch_lse(a, elem_of(dtype), hs);
-  if (e != hipSuccess) return hip_status(e, "fam_compute lse launch");
-  return fam_mass(q, k, lse, dtype, B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, W, scale,
-                  mass, workspace, workspace_bytes, stream);
+  return compute_all(q, k, dtype, s, W, scale, lse, mass, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream), "fam_compute");
+}
+
+fam_status fam_compute_chunk(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv,
+                             int Sq, int Sk, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                             int64_t k_sb, int64_t k_sh, int64_t k_ss, int W, float scale,
+                             float* lse, float* mass, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (Sq < 1 || Sq > Sk)
+    return fail(FAM_ERR_INVALID_ARG, "query rows Sq = %d must be in [1, Sk = %d]", Sq, Sk);
+  const ScoreShape s{B, Hq, Hkv, Sk, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, Sq};
+  fam_status st = check_scores(q, k, dtype, s);
+  if (st != FAM_OK) return st;
+  return compute_all(q, k, dtype, s, W, scale, lse, mass, workspace, workspace_bytes,
+                     static_cast<hipStream_t>(stream), "fam_compute_chunk");
 }
 
 fam_status evict_plan(int H, int S, const int64_t* budgets, int sinks, int recent, int64_t* kept,
@@ -366,6 +428,75 @@ fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S
                      v_sh, v_ss, idx, offsets_dev, total_rows, static_cast<uint16_t*>(k_new),
                      static_cast<uint16_t*>(v_new), H, S, d};
   return hip_status(fam::launch_compact(a, static_cast<hipStream_t>(stream)), "kv_compact launch");
+}
+
+
+fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H, int n, int d,
+                     int64_t ks_sh, int64_t ks_ss, int64_t vs_sh, int64_t vs_ss, void* k_cache,
+                     void* v_cache, int64_t kc_sh, int64_t kc_ss, int64_t vc_sh, int64_t vc_ss,
+                     int capacity, int row0, int32_t* pos, int64_t pos_sh, int pos0, void* stream) {
+  if (elem_bytes != 2) return fail(FAM_ERR_UNSUPPORTED, "elem_bytes %d (need 2)", elem_bytes);
+  if (d != 64 && d != 128 && d != 256) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64, 128 or 256)", d);
+  if (H < 0 || n < 0 || capacity < 0 || row0 < 0)
+    return fail(FAM_ERR_INVALID_ARG, "H, n, capacity and row0 must be >= 0");
+  if ((int64_t)row0 + n > capacity)
+    return fail(FAM_ERR_INVALID_ARG, "rows %d .. %lld exceed the capacity %d", row0,
+                (long long)row0 + n - 1, capacity);
+  if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
+  if (H == 0 || n == 0) return ok();
+  if (!k_src || !v_src || !k_cache || !v_cache)
+    return fail(FAM_ERR_INVALID_ARG, "pointers must be non-null");
+  const int64_t st[8] = {ks_sh, ks_ss, vs_sh, vs_ss, kc_sh, kc_ss, vc_sh, vc_ss};
+  for (int i = 0; i < 8; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0)
+      return fail(FAM_ERR_INVALID_ARG, "strides must be >= 0 and multiples of 8 elements");
+  if (!aligned16(k_src) || !aligned16(v_src) || !aligned16(k_cache) || !aligned16(v_cache))
+    return fail(FAM_ERR_INVALID_ARG, "k_src, v_src, k_cache and v_cache must be 16-byte aligned");
+  if (pos && (pos_sh < capacity || (reinterpret_cast<uintptr_t>(pos) & 3u)))
+    return fail(FAM_ERR_INVALID_ARG, "pos needs a head stride >= capacity and 4-byte alignment");
+  if (pos && (int64_t)pos0 + n - 1 > 0x7fffffffLL)
+    return fail(FAM_ERR_INVALID_ARG, "positions overflow int32");
+  fam::AppendArgs a{};
+  a.k_src = static_cast<const uint16_t*>(k_src);
+  a.v_src = static_cast<const uint16_t*>(v_src);
+  a.ks_sh = ks_sh, a.ks_ss = ks_ss, a.vs_sh = vs_sh, a.vs_ss = vs_ss;
+  a.k = static_cast<uint16_t*>(k_cache);
+  a.v = static_cast<uint16_t*>(v_cache);
+  a.k_sh = kc_sh, a.k_ss = kc_ss, a.v_sh = vc_sh, a.v_ss = vc_ss;
+  a.pos = pos;
+  a.pos_sh = pos_sh;
+  a.H = H, a.n = n, a.d = d, a.row0 = row0, a.pos0 = pos0;
+  return hip_status(fam::launch_append(a, static_cast<hipStream_t>(stream)), "kv_append launch");
+}
+
+fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, int d, int64_t k_sh,
+                              int64_t k_ss, int64_t v_sh, int64_t v_ss, const int32_t* idx,
+                              const int64_t* offsets_dev, int32_t* pos, int64_t pos_sh,
+                              void* stream) {
+  if (elem_bytes != 2) return fail(FAM_ERR_UNSUPPORTED, "elem_bytes %d (need 2)", elem_bytes);
+  if (d != 64 && d != 128 && d != 256) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64, 128 or 256)", d);
+  if (H < 0 || S < 1) return fail(FAM_ERR_INVALID_ARG, "need H >= 0 and S >= 1");
+  if (H > 0x7fffffff - 1) return fail(FAM_ERR_UNSUPPORTED, "too many heads");
+  if (H == 0) return ok();
+  if (!k || !v || !idx || !offsets_dev) return fail(FAM_ERR_INVALID_ARG, "pointers must be non-null");
+  const int64_t st[4] = {k_sh, k_ss, v_sh, v_ss};
+  for (int i = 0; i < 4; ++i)
+    if (st[i] < 0 || st[i] % 8 != 0)
+      return fail(FAM_ERR_INVALID_ARG, "strides must be >= 0 and multiples of 8 elements");
+  if (!aligned16(k) || !aligned16(v)) return fail(FAM_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
+  if (pos && (pos_sh < S || (reinterpret_cast<uintptr_t>(pos) & 3u)))
+    return fail(FAM_ERR_INVALID_ARG, "pos needs a head stride >= S and 4-byte alignment");
+  fam::InplaceArgs a{};
+  a.k = static_cast<uint16_t*>(k);
+  a.v = static_cast<uint16_t*>(v);
+  a.k_sh = k_sh, a.k_ss = k_ss, a.v_sh = v_sh, a.v_ss = v_ss;
+  a.idx = idx;
+  a.offsets = offsets_dev;
+  a.pos = pos;
+  a.pos_sh = pos_sh;
+  a.H = H, a.S = S, a.d = d;
+  return hip_status(fam::launch_compact_inplace(a, static_cast<hipStream_t>(stream)),
+                    "kv_compact_inplace launch");
 }
 
 }  // extern "C"

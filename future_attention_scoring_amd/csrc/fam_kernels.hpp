@@ -8,14 +8,19 @@ namespace fam {
 
 enum class Elem { kBf16, kFp16 };
 
+// Query rows and key rows. The S keys sit at positions 0 .. S-1 and the Sq
+// query rows (Sq <= S) at positions S - Sq .. S - 1 (the queries of the last
+// Sq positions; Sq = S is the full causal square).
+
 // Causal row log-sum-exp (first pass).
 struct LseArgs {
   const uint16_t* q;
   const uint16_t* k;
-  float* lse;
+  float* lse;  // [B, Hq, Sq]
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int B, Hq, Hkv, S, d, g;
+  int Sq;
   float c;  // scale * log2(e)
   // Key-norm bound: knorm[(b * Hkv + h) * nkn + p] is the largest |k_j|^2
   // over key range p of that KV head (written by launch_knorm). Null selects
@@ -31,11 +36,12 @@ hipError_t launch_lse(const LseArgs& a, Elem e, hipStream_t s);
 struct MassArgs {
   const uint16_t* q;
   const uint16_t* k;
-  const float* lse;
-  float* mass;
+  const float* lse;  // [B, Hq, Sq]
+  float* mass;       // [B, Hkv, S]
   int64_t q_sb, q_sh, q_ss;
   int64_t k_sb, k_sh, k_ss;
   int B, Hq, Hkv, S, d, g, W;
+  int Sq;
   float c;  // scale * log2(e)
   float* mass_q;  // non-null: per-query-head mass [B, Hq, S] instead of `mass`
   // Split of each key block's query tiles over nsplit workgroups (group-sum
@@ -93,5 +99,32 @@ struct CompactArgs {
   int H, S, d;
 };
 hipError_t launch_compact(const CompactArgs& a, hipStream_t s);
+
+// Per-head cache regions (H regions with a head stride, rows of d elements):
+// append rows at row0, or move rows idx[offsets[h] + r] to row r in place.
+struct AppendArgs {
+  const uint16_t* k_src;
+  const uint16_t* v_src;
+  int64_t ks_sh, ks_ss, vs_sh, vs_ss;
+  uint16_t* k;
+  uint16_t* v;
+  int64_t k_sh, k_ss, v_sh, v_ss;
+  int32_t* pos;  // optional [H] rows of pos_sh: pos[row0 + r] = pos0 + r
+  int64_t pos_sh;
+  int H, n, d, row0, pos0;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
+struct InplaceArgs {
+  uint16_t* k;
+  uint16_t* v;
+  int64_t k_sh, k_ss, v_sh, v_ss;
+  const int32_t* idx;
+  const int64_t* offsets;
+  int32_t* pos;  // optional, moved with the rows
+  int64_t pos_sh;
+  int H, S, d;   // S: rows per head region
+};
+hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s);
 
 }  // namespace fam

@@ -2,7 +2,10 @@
 //
 // KVpop ("Delayed Memory Scoring"): the normaliser of query i sums exp(logit)
 // over the keys j <= i. Here each query's normaliser is formed over key tiles,
-// in base 2 internally, and stored as a natural log.
+// in base 2 internally, and stored as a natural log. The Sq query rows are the
+// last Sq of the S key positions (row r at position S - Sq + r): Sq = S is the
+// full causal square, Sq < S the queries of a chunk over a cache that holds
+// the earlier keys.
 //
 // Work decomposition
 //   * A "row unit" is 64 consecutive query positions of one query head. The
@@ -133,11 +136,13 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
   const bool active = unit < npb * p.g;
   const int pb = npb - 1 - (active ? unit / p.g : 0);
   const int qh = h * p.g + (active ? unit % p.g : 0);
-  const int q0 = pb * kRowsPerWave;
+  const int q0 = pb * kRowsPerWave;   // first query row of this wave
+  const int off = p.S - p.Sq;         // position of query row 0
+  const int qp0 = off + q0;           // position of the wave's first query row
 
   // the workgroup's first unit holds its latest positions
   const int pb_top = npb - 1 - (slot * kWaves) / p.g;
-  const int kend = min(p.S, (pb_top + 1) * kRowsPerWave);
+  const int kend = min(p.S, off + (pb_top + 1) * kRowsPerWave);
   const int ntiles = (kend + kKeyTile - 1) / kKeyTile;
 
   const uint16_t* qbase = p.q + b * p.q_sb + qh * p.q_sh;
@@ -147,7 +152,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int row = q0 + 32 * blk + col;
-    const bool ok = active && row < p.S;
+    const bool ok = active && row < p.Sq;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       qf[blk][ks] = ok ? load16(qbase + (int64_t)row * p.q_ss + ks * 16 + half * 8) : zero16();
@@ -179,7 +184,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
     for (int c = 0; c < CHUNKS; ++c) store16(&sk[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
   };
 
-  float* lse_row = p.lse + ((int64_t)b * p.Hq + qh) * p.S + q0;
+  float* lse_row = p.lse + ((int64_t)b * p.Hq + qh) * p.Sq + q0;
   bool done = false;
 
   if constexpr (BOUND) {
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
 #pragma unroll
       for (int kk2 = 0; kk2 < kKeyTile / 32; ++kk2) {
         const int kb = t * kKeyTile + 32 * kk2;
-        if (active && kb <= q0 + 63 && kb < p.S) {
+        if (active && kb <= qp0 + 63 && kb < p.S) {
           f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
@@ -215,8 +220,8 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
             acc0 = Mma<T>::run(a, qf[0][ks], acc0);
             acc1 = Mma<T>::run(a, qf[1][ks], acc1);
           }
-          bound_update(acc0, kb, q0, p.S, lane, p.c, M[0], l[0]);
-          bound_update(acc1, kb, q0 + 32, p.S, lane, p.c, M[1], l[1]);
+          bound_update(acc0, kb, qp0, p.S, lane, p.c, M[0], l[0]);
+          bound_update(acc1, kb, qp0 + 32, p.S, lane, p.c, M[1], l[1]);
         }
       }
       if (more) store_tile((t + 1) & 1);
@@ -228,13 +233,13 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
     for (int blk = 0; blk < 2; ++blk) {
       L[blk] = l[blk] + __shfl_xor(l[blk], 32);
       const int row = q0 + 32 * blk + col;
-      if (active && row < p.S && L[blk] < kMinBoundSum) loose = 1;
+      if (active && row < p.Sq && L[blk] < kMinBoundSum) loose = 1;
     }
     if (!__syncthreads_or(loose)) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const int row = q0 + 32 * blk + col;
-        if (active && half == 0 && row < p.S)
+        if (active && half == 0 && row < p.Sq)
           lse_row[32 * blk + col] = (M[blk] + fast_log2(L[blk])) * kLn2;
       }
       done = true;
@@ -254,7 +259,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
 #pragma unroll
     for (int kk = 0; kk < kKeyTile / 32; ++kk) {
       const int kb = t * kKeyTile + 32 * kk;
-      if (active && kb <= q0 + 63 && kb < p.S) {
+      if (active && kb <= qp0 + 63 && kb < p.S) {
         f32x16_t acc0 = {}, acc1 = {};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -263,8 +268,8 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
           acc0 = Mma<T>::run(a, qf[0][ks], acc0);
           acc1 = Mma<T>::run(a, qf[1][ks], acc1);
         }
-        online_update(acc0, kb, q0, p.S, lane, p.c, m[0], l[0]);
-        online_update(acc1, kb, q0 + 32, p.S, lane, p.c, m[1], l[1]);
+        online_update(acc0, kb, qp0, p.S, lane, p.c, m[0], l[0]);
+        online_update(acc1, kb, qp0 + 32, p.S, lane, p.c, m[1], l[1]);
       }
     }
     if (more) store_tile((t + 1) & 1);
@@ -279,13 +284,13 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
     const float Mu = Mx == -kInf ? 0.f : Mx;
     const float L = l[blk] * fast_exp2(m[blk] - Mu) + lo * fast_exp2(mo - Mu);
     const int row = q0 + 32 * blk + col;
-    if (active && half == 0 && row < p.S) lse_row[32 * blk + col] = (Mx + fast_log2(L)) * kLn2;
+    if (active && half == 0 && row < p.Sq) lse_row[32 * blk + col] = (Mx + fast_log2(L)) * kLn2;
   }
 }
 
 template <int D, typename T>
 hipError_t launch_lse_t(const LseArgs& a, hipStream_t s) {
-  const int npb = (a.S + kRowsPerWave - 1) / kRowsPerWave;
+  const int npb = (a.Sq + kRowsPerWave - 1) / kRowsPerWave;
   const int slots = (npb * a.g + kWaves - 1) / kWaves;
   const int64_t grid = (int64_t)slots * a.B * a.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;

@@ -6,7 +6,9 @@
 // of exp(logit_ij - LSE_i). The page obtains it by swapping the roles of
 // queries and keys in an attention call; here the same sum is formed directly
 // as register column sums, which needs no running maximum because every term
-// exp(logit - LSE) is at most one.
+// exp(logit - LSE) is at most one. The Sq query rows are the last Sq of the S
+// key positions (row r at position S - Sq + r), so a chunk's queries can score
+// the keys of a cache that also holds earlier positions.
 //
 // Work decomposition
 //   * A workgroup owns 256 consecutive keys of one (batch, KV head); each of
@@ -115,15 +117,17 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       if (half == 0 && key < p.S) dst[key] = tot;
     }
   };
-  const int i_first = j0 + p.W;
-  if (i_first < p.S) {
+  // query row r (position off + r) sees key j iff r >= j + Wr
+  const int Wr = p.W - (p.S - p.Sq);
+  const int i_first = max(0, j0 + Wr);
+  if (i_first < p.Sq) {
     const int g = p.g;
     const int t0 = i_first / kQTile;
-    const int t1 = (p.S + kQTile - 1) / kQTile;
+    const int t1 = (p.Sq + kQTile - 1) / kQTile;
     const int ntiles = t1 - t0;
     const int nsteps = ntiles * g;
-    // tiles t >= t_full have every row i >= j0 + 255 + W: no predicate needed
-    const int t_full = (j0 + kKeysPerWG - 1 + p.W + kQTile - 1) / kQTile;
+    // tiles t >= t_full have every row r >= j0 + 255 + Wr: no predicate needed
+    const int t_full = (max(0, j0 + kKeysPerWG - 1 + Wr) + kQTile - 1) / kQTile;
     const int nfull_h = max(0, t1 - max(t_full, t0));   // per query head
     // step u -> (tile, query head of the group); the latest tiles come first
     auto tile_of = [&](int u) { return PER_HEAD ? t1 - 1 - u % ntiles : t1 - 1 - u / g; };
@@ -135,7 +139,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const int off0 = (tid / CPR) * (int)p.q_ss + (tid % CPR) * 8;
     const int pass_stride = (kThreads / CPR) * (int)p.q_ss;   // uniform
     const uint16_t* qgroup = p.q + b * p.q_sb + (int64_t)(h * g) * p.q_sh;
-    const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.S;
+    const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.Sq;
     u32x4_t st[CHUNKS];
     float lst = 0.f;
     auto load_step = [&](int u) {
@@ -143,21 +147,21 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       const int gi = head_of(u);
       const int r0 = t * kQTile;
       const uint16_t* tile = qgroup + gi * p.q_sh + (int64_t)r0 * p.q_ss;   // uniform
-      if (r0 + kQTile <= p.S) {
+      if (r0 + kQTile <= p.Sq) {
 #pragma unroll
         for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off0 + c * pass_stride);
       } else {  // ragged last tile: clamp rows (their normaliser is +inf)
 #pragma unroll
         for (int c = 0; c < CHUNKS; ++c) {
           const int id = tid + c * kThreads;
-          const int row = min(r0 + id / CPR, p.S - 1);
+          const int row = min(r0 + id / CPR, p.Sq - 1);
           st[c] = load16(qgroup + gi * p.q_sh + (int64_t)row * p.q_ss + (id % CPR) * 8);
         }
       }
       if (tid < kQTile) {
         const int row = r0 + tid;
-        const float x = lgroup[(int64_t)gi * p.S + min(row, p.S - 1)];
-        lst = row < p.S ? x : kInf;
+        const float x = lgroup[(int64_t)gi * p.Sq + min(row, p.Sq - 1)];
+        lst = row < p.Sq ? x : kInf;
       }
     };
     const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
@@ -184,7 +188,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
 #pragma unroll
       for (int rb = 0; rb < kQTile / 32; ++rb) {
         const int i0 = i0t + 32 * rb;
-        if (full || i0 + 31 >= jw + p.W) {
+        if (full || i0 + 31 >= jw + Wr) {
           float lv[16];
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
@@ -205,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
             mid[0] += block_sum_full(acc0, lv, p.c);
             mid[1] += block_sum_full(acc1, lv, p.c);
           } else {
-            mid[0] += block_sum_band(acc0, lv, i0, jw, p.W, lane, p.c);
-            mid[1] += block_sum_band(acc1, lv, i0, jw + 32, p.W, lane, p.c);
+            mid[0] += block_sum_band(acc0, lv, i0, jw, Wr, lane, p.c);
+            mid[1] += block_sum_band(acc1, lv, i0, jw + 32, Wr, lane, p.c);
           }
         }
       }
@@ -228,7 +232,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   if (!PER_HEAD) {
     write_cols(p.nsplit > 1 ? p.part + ((int64_t)split * nbh + bh) * p.S
                             : p.mass + ((int64_t)b * p.Hkv + h) * p.S);
-  } else if (i_first >= p.S) {  // no future query: every head's mass is 0
+  } else if (i_first >= p.Sq) {  // no future query: every head's mass is 0
     for (int gi = 0; gi < p.g; ++gi) write_cols(p.mass_q + ((int64_t)b * p.Hq + h * p.g + gi) * p.S);
   }
 }

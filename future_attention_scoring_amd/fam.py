@@ -43,6 +43,12 @@ _SIGNATURES = {
     "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
     "evict_select_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
+    "fam_compute_chunk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
+                               _i64, _i, _f, _p, _p, _p, ctypes.c_size_t, _p]),
+    "kv_append": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64,
+                       _i64, _i, _i, _p, _i64, _i, _p]),
+    "kv_compact_inplace": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _p, _i64,
+                                _p]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -308,3 +314,164 @@ def kv_compact(k: torch.Tensor, v: torch.Tensor, idx: torch.Tensor, offsets: tor
                              v.stride(0), v.stride(1), idx.data_ptr(), offsets.data_ptr(), rows,
                              k_new.data_ptr(), v_new.data_ptr(), _stream(k)))
     return k_new, v_new
+
+
+def fam_compute_chunk(q: torch.Tensor, k: torch.Tensor, W: int, scale: Optional[float] = None,
+                      lse: Optional[torch.Tensor] = None, mass: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None
+                      ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """Scores of a chunk's Sq queries over Sk cache rows (the chunk's own keys
+    last): lse [B, Hq, Sq] and mass [B, Hkv, Sk] (3-D inputs give 2-D outputs)."""
+    q4, k4 = _as4(q), _as4(k)
+    if not (q4.is_cuda and k4.is_cuda) or q4.dtype != k4.dtype:
+        raise FamError(1, "q and k must be device tensors of one dtype")
+    if q4.stride(3) != 1 or k4.stride(3) != 1:
+        raise FamError(1, "the head dimension must be contiguous")
+    B, Hq, Sq, d = q4.shape
+    if k4.shape[0] != B or k4.shape[3] != d:
+        raise FamError(1, f"k shape {tuple(k4.shape)} does not match q {tuple(q4.shape)}")
+    Hkv, Sk = k4.shape[1], k4.shape[2]
+    if lse is None:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q4.device)
+    if mass is None:
+        mass = torch.empty((B, Hkv, Sk), dtype=torch.float32, device=q4.device)
+    ws, nbytes = _mass_workspace(workspace, B, Hq, Hkv, Sk, q4.device)
+    _check(load().fam_compute_chunk(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv,
+                                    Sq, Sk, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
+                                    0.0 if scale is None else scale, lse.data_ptr(),
+                                    mass.data_ptr(), ws, nbytes, _stream(q4)))
+    if q.dim() == 3:
+        return lse.view(Hq, Sq), mass.view(Hkv, Sk)
+    return lse, mass
+
+
+def _cache_args(k: torch.Tensor, v: torch.Tensor, what: str):
+    if k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.dtype != v.dtype:
+        raise FamError(1, f"{what}: k and v must be [H, rows, d] tensors of one shape and dtype")
+    if k.element_size() != 2 or k.stride(2) != 1 or v.stride(2) != 1 or not k.is_cuda:
+        raise FamError(1, f"{what}: device tensors with 2-byte elements and a contiguous last axis")
+    return k.shape
+
+
+def kv_append(k_src: torch.Tensor, v_src: torch.Tensor, k_cache: torch.Tensor,
+              v_cache: torch.Tensor, row0: int, pos: Optional[torch.Tensor] = None,
+              pos0: int = 0) -> None:
+    """Copy [H, n, d] rows into cache rows row0 .. row0+n-1 (and their positions)."""
+    H, n, d = _cache_args(k_src, v_src, "kv_append source")
+    Hc, cap, dc = _cache_args(k_cache, v_cache, "kv_append cache")
+    if Hc != H or dc != d:
+        raise FamError(1, f"cache {tuple(k_cache.shape)} does not match rows {tuple(k_src.shape)}")
+    pp, psh = 0, 0
+    if pos is not None:
+        if (pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != H or pos.shape[1] < cap
+                or pos.stride(1) != 1 or not pos.is_cuda):
+            raise FamError(1, "pos must be a device int32 [H, capacity] with contiguous rows")
+        pp, psh = pos.data_ptr(), pos.stride(0)
+    _check(load().kv_append(k_src.data_ptr(), v_src.data_ptr(), 2, H, n, d, k_src.stride(0),
+                            k_src.stride(1), v_src.stride(0), v_src.stride(1), k_cache.data_ptr(),
+                            v_cache.data_ptr(), k_cache.stride(0), k_cache.stride(1),
+                            v_cache.stride(0), v_cache.stride(1), cap, int(row0), pp, psh,
+                            int(pos0), _stream(k_cache)))
+
+
+def kv_compact_inplace(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
+                       offsets: torch.Tensor, pos: Optional[torch.Tensor] = None) -> None:
+    """Move each head's rows idx[offsets[h]:offsets[h+1]] to its first rows."""
+    H, S, d = _cache_args(k_cache, v_cache, "kv_compact_inplace")
+    if idx.dtype != torch.int32 or offsets.dtype != torch.int64 or offsets.numel() != H + 1:
+        raise FamError(1, "idx must be int32 and offsets int64 [H + 1]")
+    pp, psh = 0, 0
+    if pos is not None:
+        if (pos.dtype != torch.int32 or pos.dim() != 2 or pos.shape[0] != H or pos.shape[1] < S
+                or pos.stride(1) != 1 or not pos.is_cuda):
+            raise FamError(1, "pos must be a device int32 [H, S] with contiguous rows")
+        pp, psh = pos.data_ptr(), pos.stride(0)
+    _check(load().kv_compact_inplace(k_cache.data_ptr(), v_cache.data_ptr(), 2, H, S, d,
+                                     k_cache.stride(0), k_cache.stride(1), v_cache.stride(0),
+                                     v_cache.stride(1), idx.data_ptr(), offsets.data_ptr(), pp,
+                                     psh, _stream(k_cache)))
+
+
+class ChunkedCache:
+    """A static per-head cache driven by chunked prefill and compression.
+
+    KVP (section 4: long contexts are prefilled chunk by chunk and the cache
+    is compressed to the budget after each chunk, with physical compaction)
+    and the pruning blog (conclusion: a static cache keeps a fixed region per
+    head and overwrites old entries in place). Each chunk is appended after
+    the rows the cache holds, scored by the future-attention mass its own
+    queries give every cache row (with the normalisers of the attention over
+    the cache, i.e. over the retained keys), and then, if the cache exceeds
+    the budget, the best-scored rows are kept (sinks and the recent window
+    forced, ties to the earlier position) and compacted in place. The budget
+    is uniform over heads (a total per head, forced rows included), so every
+    head holds the same number of rows. All device work runs in libfam.
+    """
+
+    def __init__(self, B: int, Hq: int, Hkv: int, d: int, chunk: int, budget: int, sinks: int,
+                 window: int, dtype=torch.bfloat16, device="cuda", scale: Optional[float] = None):
+        if min(B, Hq, Hkv, d, chunk) < 1 or budget < 0 or sinks < 0 or window < 0:
+            raise FamError(1, "invalid cache sizes")
+        self.B, self.Hq, self.Hkv, self.d = B, Hq, Hkv, d
+        self.chunk, self.budget, self.sinks, self.window = chunk, budget, sinks, window
+        self.scale = scale
+        self.capacity = max(budget, sinks + window) + chunk
+        H = B * Hkv
+        self.k = torch.empty((H, self.capacity, d), dtype=dtype, device=device)
+        self.v = torch.empty_like(self.k)
+        self.pos = torch.full((H, self.capacity), -1, dtype=torch.int32, device=device)
+        self.n = 0          # rows held per head
+        self.next_pos = 0   # position of the next appended row
+        self.lse = None
+        self.mass = None
+
+    def append(self, k_chunk: torch.Tensor, v_chunk: torch.Tensor) -> None:
+        """k_chunk, v_chunk: [B, Hkv, n, d] (or [B*Hkv, n, d]), n <= chunk."""
+        kc = k_chunk.reshape(-1, *k_chunk.shape[-2:])
+        vc = v_chunk.reshape(-1, *v_chunk.shape[-2:])
+        n = kc.shape[1]
+        if n > self.chunk:
+            raise FamError(1, f"{n} rows exceed the chunk size {self.chunk}")
+        kv_append(kc, vc, self.k, self.v, self.n, self.pos, self.next_pos)
+        self.n += n
+        self.next_pos += n
+
+    def score(self, q_chunk: torch.Tensor, workspace: Optional[torch.Tensor] = None
+              ) -> Tuple[torch.Tensor, torch.Tensor]:
+        """Normalisers [B, Hq, Sq] of the chunk's queries (the last Sq appended
+        positions) and the mass [B, Hkv, n] of every cache row."""
+        k = self.k[:, :self.n].view(self.B, self.Hkv, self.n, self.d)
+        self.lse, self.mass = fam_compute_chunk(q_chunk, k, self.window, self.scale,
+                                                workspace=workspace)
+        return self.lse, self.mass
+
+    def compress(self) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+        """Keep the budget's best rows by the last mass; returns (idx, offsets)
+        or (None, None) if the cache is within the budget."""
+        if self.n <= self.budget:
+            return None, None
+        H = self.B * self.Hkv
+        scores = self.mass.view(H, self.n)
+        idx, offsets = evict_select(scores, [self.budget] * H, self.sinks, self.window)
+        kv_compact_inplace(self.k, self.v, idx, offsets, self.pos)
+        self.n = int(idx.numel()) // H
+        return idx, offsets
+
+
+def prefill_compress(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: int, budget: int,
+                     sinks: int, window: int, scale: Optional[float] = None) -> ChunkedCache:
+    """Chunked prefill with compression after every chunk over q [B, Hq, S, d],
+    k, v [B, Hkv, S, d]; returns the final cache (rows, positions, count)."""
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    cache = ChunkedCache(B, Hq, Hkv, d, chunk, budget, sinks, window, k.dtype, k.device, scale)
+    ws = None
+    for p0 in range(0, S, chunk):
+        p1 = min(S, p0 + chunk)
+        cache.append(k[:, :, p0:p1], v[:, :, p0:p1])
+        if ws is None or ws.numel() < fam_mass_workspace_size(B, Hq, Hkv, cache.n):
+            n = fam_mass_workspace_size(B, Hq, Hkv, cache.capacity)
+            ws = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
+        cache.score(q[:, :, p0:p1], workspace=ws)
+        cache.compress()
+    return cache

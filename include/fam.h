@@ -207,6 +207,50 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype,
                        void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
+ * fam_compute_chunk -- the scores of one chunk of a chunked prefill over a
+ * cache that already holds (a compacted subset of) the earlier keys.
+ *
+ * [KVP] section 4 ("Evaluation") and 4.1: long contexts are prefilled chunk
+ * by chunk and the cache is compressed after each chunk to the budget, with
+ * physical compaction. [KVpop] "Delayed Memory Scoring": the normalisers are
+ * those of the sparse (retained-key) attention the model actually runs, and
+ * the target is the mass a key receives from queries at least W positions
+ * later.
+ *
+ * The Sk keys k[b, h, 0 .. Sk-1] are the cache rows and the Sq queries are
+ * the last Sq of them: query row r sits at cache row Sk - Sq + r. Causality
+ * and the window are taken in that row order:
+ *
+ *   lse[b, qh, r]  = log sum_{j <= Sk - Sq + r} exp(scale <q[b,qh,r,:], k[b,qh/g,j,:]>)
+ *   mass[b, h, j]  = sum_{qh in group h} sum_{r : Sk - Sq + r >= j + W}
+ *                    exp(scale <q[b,qh,r,:], k[b,h,j,:]> - lse[b,qh,r])
+ *
+ * For a compacted cache this equals the same sums taken over original
+ * positions whenever the last W rows before the chunk hold the W positions
+ * just before it (the recent window that every compression keeps; any
+ * cache that was never compressed qualifies): the chunk's keys are its own
+ * last Sq rows, every earlier row lies before the chunk, and only the
+ * window rows can be less than W positions before a chunk query. With
+ * Sq == Sk this is fam_compute.
+ *
+ *   q     device, [B, Hq, Sq, d], strides (q_sb, q_sh, q_ss): the chunk's queries
+ *   k     device, [B, Hkv, Sk, d], strides (k_sb, k_sh, k_ss): the cache rows,
+ *         the chunk's own keys last
+ *   lse   device out, [B, Hq, Sq] fp32, contiguous, fully overwritten
+ *   mass  device out, [B, Hkv, Sk] fp32, contiguous, fully overwritten
+ *         (rows j > Sk - 1 - W get exactly 0)
+ *   workspace  as for fam_mass, sized fam_mass_workspace_size(B, Hq, Hkv, Sk)
+ * Requirements: 1 <= Sq <= Sk; otherwise as for fam_compute.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_compute_chunk(const void* q, const void* k, fam_dtype dtype,
+                             int B, int Hq, int Hkv, int Sq, int Sk, int d,
+                             int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                             int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                             int W, float scale, float* lse, float* mass,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
  * evict_plan -- host-only budget plan (no device work).
  *
  * [KVpop] "The KVpop Scoring Module" / Figure 1: the sinks and the recent
@@ -300,6 +344,65 @@ fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S
                       int64_t k_sh, int64_t k_ss, int64_t v_sh, int64_t v_ss,
                       const int32_t* idx, const int64_t* offsets_dev, int64_t total_rows,
                       void* k_new, void* v_new, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kv_append -- copy a chunk's K and V rows into per-head cache regions.
+ *
+ * [KVP] section 4 (chunked prefill) and [Blog] conclusion (a static cache
+ * reserves a fixed region per head): the chunk's rows follow the rows the
+ * cache already holds.
+ *
+ *   k_cache[h, row0 + r, :] = k_src[h, r, :],  v_cache likewise,
+ *   pos[h * pos_sh + row0 + r] = pos0 + r      (when pos is not NULL)
+ *   for 0 <= h < H, 0 <= r < n; a bit copy.
+ *
+ *   k_src, v_src      device, [H, n, d], strides (ks_sh, ks_ss), (vs_sh, vs_ss)
+ *   k_cache, v_cache  device in/out, [H, capacity, d], strides (kc_sh, kc_ss),
+ *                     (vc_sh, vc_ss); only rows row0 .. row0+n-1 are written
+ *   pos               optional device in/out int32, head stride pos_sh >= capacity
+ * Requirements: elem_bytes == 2; d in {64, 128, 256}; row0 + n <= capacity;
+ * H <= 65535; pointers 16-byte aligned (pos 4-byte); strides multiples of 8
+ * elements. Source and cache rows must not overlap.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H, int n, int d,
+                     int64_t ks_sh, int64_t ks_ss, int64_t vs_sh, int64_t vs_ss,
+                     void* k_cache, void* v_cache, int64_t kc_sh, int64_t kc_ss,
+                     int64_t vc_sh, int64_t vc_ss, int capacity, int row0,
+                     int32_t* pos, int64_t pos_sh, int pos0, void* stream);
+
+/* ------------------------------------------------------------------------
+ * kv_compact_inplace -- keep the selected rows of each head's cache region,
+ * moved to its first rows, without a second cache.
+ *
+ * [Blog] conclusion (a ring or static cache can overwrite old entries in
+ * place instead of copying into a new tensor) and [KVP] 4.1 (physical
+ * compaction).
+ *
+ *   for each head h and 0 <= r < n_h = offsets_dev[h + 1] - offsets_dev[h]:
+ *     row r of head h  <-  row idx[offsets_dev[h] + r] of head h (K, V, pos)
+ *
+ * Rows n_h and beyond keep stale contents. The rows of a head must be
+ * ascending (as evict_select writes them); then idx[...+r] >= r and the
+ * forward sweep never reads a row it has already overwritten. Unsorted
+ * indices give unspecified row contents (never an access out of bounds);
+ * an index outside [0, S) yields a zero row and position -1.
+ *
+ *   k, v         device in/out, [H, S, d], strides (k_sh, k_ss), (v_sh, v_ss)
+ *   idx          device, [offsets_dev[H]] int32 (evict_select's output)
+ *   offsets_dev  device, [H + 1] int64, n_h is clamped to [0, S]
+ *   pos          optional device in/out int32 [H, S] with head stride pos_sh,
+ *                moved with the rows
+ * Requirements: elem_bytes == 2; d in {64, 128, 256}; k, v 16-byte aligned;
+ * strides multiples of 8 elements; pos 4-byte aligned with pos_sh >= S.
+ * One workgroup sweeps each head in order, so a call with few heads is
+ * bound by latency rather than bandwidth.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, int d,
+                              int64_t k_sh, int64_t k_ss, int64_t v_sh, int64_t v_ss,
+                              const int32_t* idx, const int64_t* offsets_dev,
+                              int32_t* pos, int64_t pos_sh, void* stream);
 
 #ifdef __cplusplus
 }

@@ -10,8 +10,9 @@ Modules
   select_oracle   budget plan, sort-based top-k selection, compaction
   soft_topk       closed-form Soft-TopK and per-head budgets (LKV)
   kvpop_target    count-normalised log target and group aggregation (KVpop)
+  chunked         chunked prefill with compression after every chunk (KVP)
 
 Every function is pinned by the CPU tests in ``tests/test_oracle_*.py``
 against brute force, closed forms, invariants or the pages' worked example.
 """
-from . import fam_oracle, kvpop_target, select_oracle, soft_topk  # noqa: F401
+from . import chunked, fam_oracle, kvpop_target, select_oracle, soft_topk  # noqa: F401

@@ -192,3 +192,49 @@ def test_kv_compact_validation():
     bad = list(args)
     bad[12] = 0
     assert lib.kv_compact(*bad) == 0  # nothing to copy
+
+
+def test_compute_chunk_validation():
+    lib = fam.load()
+    # q [1, 4, Sq=32, 128], k [1, 2, Sk=64, 128]
+    args = [FAKE, FAKE, 0, 1, 4, 2, 32, 64, 128, 0, 32 * 128, 128, 0, 64 * 128, 128, 8, 0.0, FAKE, FAKE,
+            None, 0, None]
+    for sq in (0, 65, -1):
+        bad = list(args); bad[6] = sq
+        assert lib.fam_compute_chunk(*bad) == INVALID
+    bad = list(args); bad[15] = -1
+    assert lib.fam_compute_chunk(*bad) == INVALID                  # negative window
+    bad = list(args); bad[8] = 96
+    assert lib.fam_compute_chunk(*bad) == UNSUPPORTED              # head dim
+    bad = list(args); bad[18] = None
+    assert lib.fam_compute_chunk(*bad) == INVALID                  # no mass buffer
+    bad = list(args); bad[19] = FAKE + 8; bad[20] = 1 << 16
+    assert lib.fam_compute_chunk(*bad) == INVALID                  # misaligned workspace
+    bad = list(args); bad[5] = 3
+    assert lib.fam_compute_chunk(*bad) == INVALID                  # Hq % Hkv
+
+
+def test_kv_append_and_inplace_validation():
+    lib = fam.load()
+    # src [2, 16, 128], cache [2, 100, 128]
+    args = [FAKE, FAKE, 2, 2, 16, 128, 16 * 128, 128, 16 * 128, 128, FAKE, FAKE, 100 * 128, 128,
+            100 * 128, 128, 100, 84, None, 0, 0, None]
+    bad = list(args); bad[17] = 85
+    assert lib.kv_append(*bad) == INVALID                          # past the capacity
+    bad = list(args); bad[2] = 4
+    assert lib.kv_append(*bad) == UNSUPPORTED
+    bad = list(args); bad[18] = FAKE; bad[19] = 99
+    assert lib.kv_append(*bad) == INVALID                          # pos stride below capacity
+    bad = list(args); bad[10] = FAKE + 2
+    assert lib.kv_append(*bad) == INVALID                          # misaligned cache
+    bad = list(args); bad[4] = 0
+    assert lib.kv_append(*bad) == 0                                # nothing to copy
+    ip = [FAKE, FAKE, 2, 2, 100, 128, 100 * 128, 128, 100 * 128, 128, FAKE, FAKE, None, 0, None]
+    bad = list(ip); bad[10] = None
+    assert lib.kv_compact_inplace(*bad) == INVALID
+    bad = list(ip); bad[5] = 72
+    assert lib.kv_compact_inplace(*bad) == UNSUPPORTED
+    bad = list(ip); bad[12] = FAKE; bad[13] = 50
+    assert lib.kv_compact_inplace(*bad) == INVALID                 # pos stride below S
+    bad = list(ip); bad[3] = 0
+    assert lib.kv_compact_inplace(*bad) == 0                       # no heads
