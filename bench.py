@@ -13,7 +13,12 @@ launch over its mean HIP-event duration); `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline]
+                       [--no-cpu-baseline] [--target-steps N] [--chunked-runs N]
+
+Two widened rows are timed apart from the step and reported beside it: the
+KVpop target (per-query-head mass and its epilogue) and the chunked
+prefill-compress loop (chunks of 4096, a uniform budget of 16384 rows per
+head, compaction in place).
 """
 from __future__ import annotations
 
@@ -156,6 +161,72 @@ def kvpop_target_row(steps, q, k, lse, wl, work, stream):
     }
 
 
+def chunked_row(runs, q, k, v, wl, stream, chunk=4096, budget=16384):
+    """Time the chunked prefill-compress loop over the whole sequence apart
+    from the step: per chunk, kv_append of its K/V rows, fam_compute_chunk
+    (key norms, first pass and mass of the chunk's queries over the cache),
+    and, once the cache exceeds the budget, evict_select + in-place
+    compaction (ChunkedCache.compress). The budget is uniform per head."""
+    B, Hq, S, d = q.shape
+    Hkv = k.shape[1]
+    cap = max(budget, wl.sinks + wl.W) + chunk
+    ws_n = max([fam.fam_mass_workspace_size(B, Hq, Hkv, s) for s in range(chunk, cap + 1, chunk)] + [16])
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
+
+    def one(record):
+        cache = fam.ChunkedCache(B, Hq, Hkv, d, chunk, budget, wl.sinks, wl.W, k.dtype, q.device)
+        marks, sizes = [], []
+        for p0 in range(0, S, chunk):
+            p1 = min(S, p0 + chunk)
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+            if e:
+                e[0].record(stream)
+            n_old = cache.n
+            cache.append(k[:, :, p0:p1], v[:, :, p0:p1])
+            if e:
+                e[1].record(stream)
+            cache.score(q[:, :, p0:p1], workspace=ws)
+            if e:
+                e[2].record(stream)
+            cache.compress()
+            if e:
+                e[3].record(stream)
+            marks.append(e)
+            sizes.append((n_old, p1 - p0))
+        return marks, sizes
+
+    one(False)
+    torch.cuda.synchronize()
+    per_run = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        marks, sizes = one(True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        phases = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
+                           for e in marks]).sum(axis=0)
+        per_run.append((wall * 1e3, phases))
+    wall_ms = float(np.mean([r[0] for r in per_run]))
+    append_ms, score_ms, compress_ms = (float(x) for x in np.mean([r[1] for r in per_run], axis=0))
+    W = wl.W
+    lse_pairs = sum(Hq * (c * n + c * (c + 1) // 2) for n, c in sizes)
+    mass_pairs = sum(Hq * sum(max(0, n + i - W + 1) for i in range(c)) for n, c in sizes)
+    flops = 2 * d * (lse_pairs + mass_pairs)
+    return {
+        "workload": f"{wl.name} chunked prefill-compress",
+        "chunk": chunk, "budget_per_head": budget, "sinks": wl.sinks, "window": W,
+        "chunks": len(sizes), "runs": runs,
+        "pairs_per_s": lse_pairs / (wall_ms * 1e-3),
+        "causal_pairs": lse_pairs, "future_pairs": mass_pairs,
+        "ms_wall": round(wall_ms, 3),
+        "ms": {"kv_append": round(append_ms, 3), "fam_compute_chunk": round(score_ms, 3),
+               "select_compact_inplace": round(compress_ms, 3)},
+        "fam_compute_chunk": {"bound": "mfma", "achieved": round(flops / (score_ms * 1e-3) / 1e12, 3),
+                              "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                              "frac": round(flops / (score_ms * 1e-3) / PEAK_BF16_FLOPS, 4)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -165,6 +236,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--target-steps", type=int, default=2,
                     help="timed runs of the KVpop target row (per-head mass + epilogue); 0 skips it")
+    ap.add_argument("--chunked-runs", type=int, default=1,
+                    help="timed runs of the chunked prefill-compress loop; 0 skips it")
+    ap.add_argument("--chunked-only", action="store_true",
+                    help="run only the chunked prefill-compress row (for a kernel trace of it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -187,6 +262,11 @@ def main():
     t = wl.tensors()
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
     del t
+    stream = torch.cuda.current_stream(dev)
+    if args.chunked_only:
+        print(json.dumps({"chunked_prefill": chunked_row(max(1, args.chunked_runs), q, k, v, wl, stream)}),
+              flush=True)
+        return
     bi = wl.budget_inputs()
     budgets = (fam.fam_budgets_from_ratios(bi["ratios"], bi["t"]).tolist() if "ratios" in bi
                else [bi["uniform"]] * wl.Hkv)
@@ -201,7 +281,6 @@ def main():
                      dtype=torch.uint8, device=dev)
     k_new = torch.empty((total, d), dtype=k.dtype, device=dev)
     v_new = torch.empty((total, d), dtype=v.dtype, device=dev)
-    stream = torch.cuda.current_stream(dev)
 
     knorm = torch.empty((B, Hkv, fam.fam_key_norm_parts(S)), dtype=torch.float32, device=dev)
     mass_ws = torch.empty(fam.fam_mass_workspace_size(B, Hq, Hkv, S), dtype=torch.uint8, device=dev)
@@ -283,6 +362,8 @@ def main():
         out["kvpop_target"] = kvpop_target_row(args.target_steps, q, k, lse, wl, work, stream)
         for n in ("fam_mass_per_head", "fam_kvpop_target"):
             out["kvpop_target"][n]["traffic"] = traffic.get(n)
+    if args.chunked_runs > 0:
+        out["chunked_prefill"] = chunked_row(args.chunked_runs, q, k, v, wl, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)

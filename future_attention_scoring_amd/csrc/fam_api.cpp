@@ -471,13 +471,15 @@ fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H
 
 fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, int d, int64_t k_sh,
                               int64_t k_ss, int64_t v_sh, int64_t v_ss, const int32_t* idx,
-                              const int64_t* offsets_dev, int32_t* pos, int64_t pos_sh,
-                              void* stream) {
+                              const int64_t* offsets_dev, int64_t total_rows, int32_t* pos,
+                              int64_t pos_sh, void* stream) {
   if (elem_bytes != 2) return fail(FAM_ERR_UNSUPPORTED, "elem_bytes %d (need 2)", elem_bytes);
   if (d != 64 && d != 128 && d != 256) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64, 128 or 256)", d);
-  if (H < 0 || S < 1) return fail(FAM_ERR_INVALID_ARG, "need H >= 0 and S >= 1");
-  if (H > 0x7fffffff - 1) return fail(FAM_ERR_UNSUPPORTED, "too many heads");
-  if (H == 0) return ok();
+  if (H < 0 || S < 1 || total_rows < 0)
+    return fail(FAM_ERR_INVALID_ARG, "need H >= 0, S >= 1 and total_rows >= 0");
+  if (total_rows > (int64_t)H * S)
+    return fail(FAM_ERR_INVALID_ARG, "total_rows %lld exceeds H * S", (long long)total_rows);
+  if (H == 0 || total_rows == 0) return ok();
   if (!k || !v || !idx || !offsets_dev) return fail(FAM_ERR_INVALID_ARG, "pointers must be non-null");
   const int64_t st[4] = {k_sh, k_ss, v_sh, v_ss};
   for (int i = 0; i < 4; ++i)
@@ -494,6 +496,7 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
   a.offsets = offsets_dev;
   a.pos = pos;
   a.pos_sh = pos_sh;
+  a.total = total_rows;
   a.H = H, a.S = S, a.d = d;
   return hip_status(fam::launch_compact_inplace(a, static_cast<hipStream_t>(stream)),
                     "kv_compact_inplace launch");

@@ -123,6 +123,7 @@ struct InplaceArgs {
   const int64_t* offsets;
   int32_t* pos;  // optional, moved with the rows
   int64_t pos_sh;
+  int64_t total; // offsets[H]: kept rows over all heads
   int H, S, d;   // S: rows per head region
 };
 hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s);

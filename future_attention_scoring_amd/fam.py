@@ -47,8 +47,8 @@ _SIGNATURES = {
                                _i64, _i, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "kv_append": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64,
                        _i64, _i, _i, _p, _i64, _i, _p]),
-    "kv_compact_inplace": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _p, _i64,
-                                _p]),
+    "kv_compact_inplace": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p,
+                                _i64, _p]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -375,8 +375,10 @@ def kv_append(k_src: torch.Tensor, v_src: torch.Tensor, k_cache: torch.Tensor,
 
 
 def kv_compact_inplace(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
-                       offsets: torch.Tensor, pos: Optional[torch.Tensor] = None) -> None:
-    """Move each head's rows idx[offsets[h]:offsets[h+1]] to its first rows."""
+                       offsets: torch.Tensor, pos: Optional[torch.Tensor] = None,
+                       total_rows: Optional[int] = None) -> None:
+    """Move each head's rows idx[offsets[h]:offsets[h+1]] to its first rows
+    (total_rows = offsets[H], idx.numel() by default)."""
     H, S, d = _cache_args(k_cache, v_cache, "kv_compact_inplace")
     if idx.dtype != torch.int32 or offsets.dtype != torch.int64 or offsets.numel() != H + 1:
         raise FamError(1, "idx must be int32 and offsets int64 [H + 1]")
@@ -388,8 +390,9 @@ def kv_compact_inplace(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.
         pp, psh = pos.data_ptr(), pos.stride(0)
     _check(load().kv_compact_inplace(k_cache.data_ptr(), v_cache.data_ptr(), 2, H, S, d,
                                      k_cache.stride(0), k_cache.stride(1), v_cache.stride(0),
-                                     v_cache.stride(1), idx.data_ptr(), offsets.data_ptr(), pp,
-                                     psh, _stream(k_cache)))
+                                     v_cache.stride(1), idx.data_ptr(), offsets.data_ptr(),
+                                     int(idx.numel()) if total_rows is None else int(total_rows),
+                                     pp, psh, _stream(k_cache)))
 
 
 class ChunkedCache:

@@ -229,12 +229,18 @@ def test_kv_append_and_inplace_validation():
     assert lib.kv_append(*bad) == INVALID                          # misaligned cache
     bad = list(args); bad[4] = 0
     assert lib.kv_append(*bad) == 0                                # nothing to copy
-    ip = [FAKE, FAKE, 2, 2, 100, 128, 100 * 128, 128, 100 * 128, 128, FAKE, FAKE, None, 0, None]
+    ip = [FAKE, FAKE, 2, 2, 100, 128, 100 * 128, 128, 100 * 128, 128, FAKE, FAKE, 150, None, 0, None]
     bad = list(ip); bad[10] = None
     assert lib.kv_compact_inplace(*bad) == INVALID
     bad = list(ip); bad[5] = 72
     assert lib.kv_compact_inplace(*bad) == UNSUPPORTED
-    bad = list(ip); bad[12] = FAKE; bad[13] = 50
+    bad = list(ip); bad[13] = FAKE; bad[14] = 50
     assert lib.kv_compact_inplace(*bad) == INVALID                 # pos stride below S
+    bad = list(ip); bad[12] = 201
+    assert lib.kv_compact_inplace(*bad) == INVALID                 # more rows than H * S
     bad = list(ip); bad[3] = 0
+    assert lib.kv_compact_inplace(*bad) == INVALID                 # rows but no heads
+    bad[12] = 0
     assert lib.kv_compact_inplace(*bad) == 0                       # no heads
+    bad = list(ip); bad[12] = 0
+    assert lib.kv_compact_inplace(*bad) == 0                       # nothing kept
