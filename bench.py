@@ -175,10 +175,10 @@ def chunked_row(runs, q, k, v, wl, stream, chunk=4096, budget=16384):
 
     def one(record):
         cache = fam.ChunkedCache(B, Hq, Hkv, d, chunk, budget, wl.sinks, wl.W, k.dtype, q.device)
-        marks, sizes = [], []
+        marks, sizes, moved = [], [], []
         for p0 in range(0, S, chunk):
             p1 = min(S, p0 + chunk)
-            e = [torch.cuda.Event(enable_timing=True) for _ in range(4)] if record else None
+            e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
             if e:
                 e[0].record(stream)
             n_old = cache.n
@@ -188,26 +188,33 @@ def chunked_row(runs, q, k, v, wl, stream, chunk=4096, budget=16384):
             cache.score(q[:, :, p0:p1], workspace=ws)
             if e:
                 e[2].record(stream)
-            cache.compress()
+            idx, offsets = cache.select()
             if e:
                 e[3].record(stream)
+            if idx is not None:
+                if not record:   # rows that move (idx[r] != r), counted in the untimed run only
+                    rows = torch.arange(idx.numel() // (B * Hkv), device=idx.device, dtype=idx.dtype)
+                    moved.append(int((idx.view(B * Hkv, -1) != rows).sum()))
+                cache.compact(idx, offsets)
+            if e:
+                e[4].record(stream)
             marks.append(e)
             sizes.append((n_old, p1 - p0))
-        return marks, sizes
+        return marks, sizes, moved
 
-    one(False)
+    _, _, moved = one(False)
     torch.cuda.synchronize()
     per_run = []
     for _ in range(runs):
         t0 = time.perf_counter()
-        marks, sizes = one(True)
+        marks, sizes, _ = one(True)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        phases = np.array([[e[0].elapsed_time(e[1]), e[1].elapsed_time(e[2]), e[2].elapsed_time(e[3])]
-                           for e in marks]).sum(axis=0)
+        phases = np.array([[e[i].elapsed_time(e[i + 1]) for i in range(4)] for e in marks]).sum(axis=0)
         per_run.append((wall * 1e3, phases))
     wall_ms = float(np.mean([r[0] for r in per_run]))
-    append_ms, score_ms, compress_ms = (float(x) for x in np.mean([r[1] for r in per_run], axis=0))
+    append_ms, score_ms, select_ms, compact_ms = (float(x) for x in np.mean([r[1] for r in per_run], axis=0))
+    compact_bytes = 2 * 2 * sum(moved) * d * k.element_size()   # K and V rows, read + write
     W = wl.W
     lse_pairs = sum(Hq * (c * n + c * (c + 1) // 2) for n, c in sizes)
     mass_pairs = sum(Hq * sum(max(0, n + i - W + 1) for i in range(c)) for n, c in sizes)
@@ -220,10 +227,14 @@ def chunked_row(runs, q, k, v, wl, stream, chunk=4096, budget=16384):
         "causal_pairs": lse_pairs, "future_pairs": mass_pairs,
         "ms_wall": round(wall_ms, 3),
         "ms": {"kv_append": round(append_ms, 3), "fam_compute_chunk": round(score_ms, 3),
-               "select_compact_inplace": round(compress_ms, 3)},
+               "evict_select": round(select_ms, 3), "kv_compact_inplace": round(compact_ms, 3)},
         "fam_compute_chunk": {"bound": "mfma", "achieved": round(flops / (score_ms * 1e-3) / 1e12, 3),
                               "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
                               "frac": round(flops / (score_ms * 1e-3) / PEAK_BF16_FLOPS, 4)},
+        "kv_compact_inplace": {"bound": "hbm", "moved_rows": int(sum(moved)), "bytes": compact_bytes,
+                               "achieved": round(compact_bytes / (compact_ms * 1e-3) / 1e9, 3),
+                               "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                               "frac": round(compact_bytes / (compact_ms * 1e-3) / PEAK_HBM_BYTES, 4)},
     }
 
 

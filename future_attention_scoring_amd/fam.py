@@ -448,16 +448,24 @@ class ChunkedCache:
                                                 workspace=workspace)
         return self.lse, self.mass
 
-    def compress(self) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
-        """Keep the budget's best rows by the last mass; returns (idx, offsets)
+    def select(self) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+        """Rows each head keeps by the last mass (evict_select): (idx, offsets),
         or (None, None) if the cache is within the budget."""
         if self.n <= self.budget:
             return None, None
         H = self.B * self.Hkv
-        scores = self.mass.view(H, self.n)
-        idx, offsets = evict_select(scores, [self.budget] * H, self.sinks, self.window)
+        return evict_select(self.mass.view(H, self.n), [self.budget] * H, self.sinks, self.window)
+
+    def compact(self, idx: torch.Tensor, offsets: torch.Tensor) -> None:
+        """Move the kept rows to the front of every head's region, in place."""
         kv_compact_inplace(self.k, self.v, idx, offsets, self.pos)
-        self.n = int(idx.numel()) // H
+        self.n = int(idx.numel()) // (self.B * self.Hkv)
+
+    def compress(self) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:
+        """select() then compact(); returns (idx, offsets) or (None, None)."""
+        idx, offsets = self.select()
+        if idx is not None:
+            self.compact(idx, offsets)
         return idx, offsets
 
 
