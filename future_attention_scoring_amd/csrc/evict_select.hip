@@ -47,14 +47,6 @@ constexpr int kMaxChunks = (kSelectMaxCandidates + 3) / kSelectChunk + 1;
 constexpr int kLdsList = 4096;  // (b1, b2) entries held in LDS
 constexpr int kRankMax = 128;   // up to this many, rank them by direct comparison
 
-typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  uint32_t u = __float_as_uint(f);
-  if (f != f) return 1u;
-  if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 __device__ __forceinline__ uint64_t composite(uint32_t key, uint32_t pos) {
   return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - pos);

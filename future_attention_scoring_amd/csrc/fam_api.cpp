@@ -502,4 +502,62 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
                     "kv_compact_inplace launch");
 }
 
+
+size_t fam_rank_order_workspace_size(int H, int n) {
+  if (H < 0 || n < 0) return 0;
+  return (size_t)2 * H * n * 8;
+}
+
+fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n, int32_t* order,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  if (H < 0 || n < 0) return fail(FAM_ERR_INVALID_ARG, "H and n must be >= 0");
+  if (n > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "n = %d exceeds %d", n, kMaxSeq);
+  if (H == 0 || n == 0) return ok();
+  if (!scores || !order) return fail(FAM_ERR_INVALID_ARG, "scores and order must be non-null");
+  if (row_stride < n) return fail(FAM_ERR_INVALID_ARG, "row stride must be >= n");
+  if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(order)) & 3u)
+    return fail(FAM_ERR_INVALID_ARG, "scores and order must be 4-byte aligned");
+  const size_t need = fam_rank_order_workspace_size(H, n);
+  if (!workspace || workspace_bytes < need)
+    return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  fam::RankArgs a{scores, row_stride, order, workspace, H, n};
+  return hip_status(fam::launch_rank(a, static_cast<hipStream_t>(stream)), "fam_rank_order launch");
+}
+
+fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const int32_t* order, int H,
+                             int n, double* cost, void* stream) {
+  if (H < 0 || n < 0) return fail(FAM_ERR_INVALID_ARG, "H and n must be >= 0");
+  if (n > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "n = %d exceeds %d", n, kMaxSeq);
+  if (H == 0) return ok();
+  if (!cost) return fail(FAM_ERR_INVALID_ARG, "cost must be non-null");
+  if (n > 0 && (!importance || !order))
+    return fail(FAM_ERR_INVALID_ARG, "importance and order must be non-null");
+  if (row_stride < n) return fail(FAM_ERR_INVALID_ARG, "row stride must be >= n");
+  if ((reinterpret_cast<uintptr_t>(importance) | reinterpret_cast<uintptr_t>(order)) & 3u ||
+      (reinterpret_cast<uintptr_t>(cost) & 7u))
+    return fail(FAM_ERR_INVALID_ARG, "importance and order must be 4-byte, cost 8-byte aligned");
+  fam::CostArgs a{importance, row_stride, order, cost, H, n};
+  return hip_status(fam::launch_cost(a, static_cast<hipStream_t>(stream)), "fam_eviction_cost launch");
+}
+
+fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a, const int32_t* idx_b,
+                                 const int64_t* offsets_b, int H, int S, int64_t* common,
+                                 void* stream) {
+  if (H < 0 || S < 1) return fail(FAM_ERR_INVALID_ARG, "need H >= 0 and S >= 1");
+  if (S > fam::kOverlapMaxS)
+    return fail(FAM_ERR_UNSUPPORTED, "S = %d exceeds %d positions", S, fam::kOverlapMaxS);
+  if (H == 0) return ok();
+  if (!idx_a || !offsets_a || !idx_b || !offsets_b || !common)
+    return fail(FAM_ERR_INVALID_ARG, "pointers must be non-null");
+  if ((reinterpret_cast<uintptr_t>(offsets_a) | reinterpret_cast<uintptr_t>(offsets_b) |
+       reinterpret_cast<uintptr_t>(common)) & 7u)
+    return fail(FAM_ERR_INVALID_ARG, "offsets and common must be 8-byte aligned");
+  fam::OverlapArgs a{idx_a, offsets_a, idx_b, offsets_b, common, H, S};
+  return hip_status(fam::launch_overlap(a, static_cast<hipStream_t>(stream)),
+                    "fam_retention_overlap launch");
+}
+
 }  // extern "C"

@@ -11,6 +11,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -75,6 +76,16 @@ template <> __device__ __forceinline__ float sumsq8<Fp16>(u32x4_t v) {
     s = fmaf(lo, lo, fmaf(hi, hi, s));
   }
   return s;
+}
+
+// Order-preserving u32 key of a score: larger scores give larger keys, -0.0
+// maps like +0.0, NaN maps to 1 (below every number; 0 stays free as a
+// "no entry" marker).
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (f != f) return 1u;
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
 // Pairwise sum of the 16 accumulator-shaped values.

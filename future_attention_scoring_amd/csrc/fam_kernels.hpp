@@ -128,4 +128,35 @@ struct InplaceArgs {
 };
 hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s);
 
+// Ranking measures: stable per-head order by score, the eviction cost of an
+// order summed over budgets, and the overlap of two kept sets.
+struct RankArgs {
+  const float* scores;
+  int64_t row_stride;
+  int32_t* order;  // [H, n]
+  void* ws;        // 2 * H * n (key, position) pairs of 8 bytes
+  int H, n;
+};
+hipError_t launch_rank(const RankArgs& a, hipStream_t s);
+
+struct CostArgs {
+  const float* importance;
+  int64_t row_stride;
+  const int32_t* order;  // [H, n]
+  double* cost;          // [H]
+  int H, n;
+};
+hipError_t launch_cost(const CostArgs& a, hipStream_t s);
+
+struct OverlapArgs {
+  const int32_t* idx_a;
+  const int64_t* off_a;
+  const int32_t* idx_b;
+  const int64_t* off_b;
+  int64_t* common;  // [H]
+  int H, S;
+};
+constexpr int kOverlapMaxS = 1 << 18;  // bitmap of the positions in 32 KiB of LDS
+hipError_t launch_overlap(const OverlapArgs& a, hipStream_t s);
+
 }  // namespace fam

@@ -49,6 +49,10 @@ _SIGNATURES = {
                        _i64, _i, _i, _p, _i64, _i, _p]),
     "kv_compact_inplace": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p,
                                 _i64, _p]),
+    "fam_rank_order": (_i, [_p, _i64, _i, _i, _p, _p, ctypes.c_size_t, _p]),
+    "fam_rank_order_workspace_size": (ctypes.c_size_t, [_i, _i]),
+    "fam_eviction_cost": (_i, [_p, _i64, _p, _i, _i, _p, _p]),
+    "fam_retention_overlap": (_i, [_p, _p, _p, _p, _i, _i, _p, _p]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -486,3 +490,62 @@ def prefill_compress(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: i
         cache.score(q[:, :, p0:p1], workspace=ws)
         cache.compress()
     return cache
+
+
+def _score_rows(x: torch.Tensor, what: str) -> Tuple[int, int]:
+    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+        raise FamError(1, f"{what} must be a device fp32 [H, n] tensor with contiguous rows")
+    return x.shape[0], x.shape[1]
+
+
+def fam_rank_order(scores: torch.Tensor, order: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Positions of each row's entries, best first (ties to the lower position)."""
+    H, n = _score_rows(scores, "scores")
+    if order is None:
+        order = torch.empty((H, n), dtype=torch.int32, device=scores.device)
+    if workspace is None:
+        nbytes = int(load().fam_rank_order_workspace_size(H, n))
+        workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=scores.device)
+    _check(load().fam_rank_order(scores.data_ptr(), scores.stride(0), H, n, order.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                 _stream(scores)))
+    return order
+
+
+def fam_eviction_cost(importance: torch.Tensor, order: torch.Tensor,
+                      cost: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Importance evicted by `order`, summed over all budgets: [H] fp64."""
+    H, n = _score_rows(importance, "importance")
+    if order.dtype != torch.int32 or tuple(order.shape) != (H, n) or not order.is_contiguous():
+        raise FamError(1, "order must be a contiguous int32 [H, n] tensor")
+    if cost is None:
+        cost = torch.empty(H, dtype=torch.float64, device=importance.device)
+    _check(load().fam_eviction_cost(importance.data_ptr(), importance.stride(0), order.data_ptr(), H,
+                                    n, cost.data_ptr(), _stream(importance)))
+    return cost
+
+
+def eviction_cost_ratio(scores: torch.Tensor, importance: torch.Tensor) -> torch.Tensor:
+    """KVP's normalised eviction cost of ranking by `scores`: cost over the cost
+    of ranking by `importance` itself (>= 1; 1 is optimal), per row."""
+    c = fam_eviction_cost(importance, fam_rank_order(scores))
+    c_opt = fam_eviction_cost(importance, fam_rank_order(importance))
+    return c / c_opt
+
+
+def fam_retention_overlap(idx_a: torch.Tensor, offsets_a: torch.Tensor, idx_b: torch.Tensor,
+                          offsets_b: torch.Tensor, S: int,
+                          common: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per head, the number of positions both kept lists hold: [H] int64."""
+    H = offsets_a.numel() - 1
+    if offsets_b.numel() != H + 1 or offsets_a.dtype != torch.int64 or offsets_b.dtype != torch.int64:
+        raise FamError(1, "offsets must be int64 [H + 1] tensors of one length")
+    if idx_a.dtype != torch.int32 or idx_b.dtype != torch.int32:
+        raise FamError(1, "idx lists must be int32")
+    if common is None:
+        common = torch.empty(H, dtype=torch.int64, device=idx_a.device)
+    _check(load().fam_retention_overlap(idx_a.data_ptr(), offsets_a.data_ptr(), idx_b.data_ptr(),
+                                        offsets_b.data_ptr(), H, int(S), common.data_ptr(),
+                                        _stream(idx_a)))
+    return common

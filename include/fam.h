@@ -407,6 +407,75 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
                               const int32_t* idx, const int64_t* offsets_dev,
                               int64_t total_rows, int32_t* pos, int64_t pos_sh, void* stream);
 
+/* ------------------------------------------------------------------------
+ * fam_rank_order -- each head's entries ordered best first.
+ *
+ * [KVP] section 3: a ranking's top-b entries form the cache for every budget
+ * b. The order is by score descending; ties go to the lower position, -0.0
+ * equals +0.0 and NaN ranks below every number (NaNs by position), as in
+ * evict_select.
+ *
+ *   order[h * n + r] = position (0 .. n-1) of the r-th best entry of row h
+ *
+ *   scores     device, [H] rows of n fp32 with row stride row_stride >= n
+ *   order      device out, [H, n] int32, fully overwritten
+ *   workspace  device scratch of fam_rank_order_workspace_size(H, n) bytes
+ *              (16 * H * n), 8-byte aligned, owned by the caller; contents
+ *              irrelevant on entry and unspecified on return
+ * One workgroup sorts one head (a stable radix sort, 4 passes), so a call
+ * costs about 1 ms per 131072 entries whatever H is, up to the CU count.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (n > 2^28),
+ * FAM_ERR_WORKSPACE, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n, int32_t* order,
+                          void* workspace, size_t workspace_bytes, void* stream);
+size_t fam_rank_order_workspace_size(int H, int n);
+
+/* ------------------------------------------------------------------------
+ * fam_eviction_cost -- the importance a ranking evicts, summed over budgets.
+ *
+ * [KVP] 3.1.1: a ranking is scored by the future-attention importance of the
+ * entries it evicts across cache budgets (a cost-versus-budget area under
+ * the curve), normalised by the same area of the optimal ranking (the order
+ * of the importance itself). With order from fam_rank_order:
+ *
+ *   cost[h] = sum_{b=0}^{n} sum_{r >= b} importance[h, order[h, r]]
+ *           = sum_r (r + 1) * importance[h, order[h, r]]
+ *
+ * and the normalised cost is cost / cost_optimal, where cost_optimal uses
+ * the order of importance (it is >= 1 for non-negative importance and
+ * equals 1 exactly for an optimal order).
+ *
+ *   importance  device, [H] rows of n fp32, row stride row_stride >= n
+ *   order       device, [H, n] int32 (entries outside [0, n) are skipped)
+ *   cost        device out, [H] fp64 (sums in fp64, fixed order)
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const int32_t* order,
+                             int H, int n, double* cost, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fam_retention_overlap -- entries two kept sets share, per head.
+ *
+ * [KVpop] Figure 7: top-k retention recall is the fraction of the teacher's
+ * kept set (the top of the future-attention mass) that another scorer also
+ * keeps under the same budget. With kept lists a (the teacher's) and b:
+ *
+ *   common[h] = | {idx_a[offsets_a[h] ..]} & {idx_b[offsets_b[h] ..]} |
+ *
+ * and the recall of head h is common[h] / |set of a_h|. Duplicates count
+ * once; indices outside [0, S) are ignored.
+ *
+ *   idx_a, idx_b          device int32 kept positions (e.g. evict_select's)
+ *   offsets_a, offsets_b  device [H + 1] int64, non-decreasing
+ *   common                device out, [H] int64
+ * Requirements: S <= 262144 (a bitmap of the positions in LDS).
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
+                                 const int32_t* idx_b, const int64_t* offsets_b, int H, int S,
+                                 int64_t* common, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -244,3 +244,18 @@ def test_kv_append_and_inplace_validation():
     assert lib.kv_compact_inplace(*bad) == 0                       # no heads
     bad = list(ip); bad[12] = 0
     assert lib.kv_compact_inplace(*bad) == 0                       # nothing kept
+
+
+def test_ranking_validation():
+    lib = fam.load()
+    assert lib.fam_rank_order_workspace_size(8, 131072) == 16 * 8 * 131072
+    ws = lib.fam_rank_order_workspace_size(2, 100)
+    assert lib.fam_rank_order(FAKE, 100, 2, 100, FAKE, FAKE, ws - 1, None) == WORKSPACE
+    assert lib.fam_rank_order(FAKE, 99, 2, 100, FAKE, FAKE, ws, None) == INVALID       # stride < n
+    assert lib.fam_rank_order(FAKE, 100, 2, 100, FAKE, FAKE + 4, ws, None) == INVALID  # workspace alignment
+    assert lib.fam_rank_order(None, 100, 0, 100, None, None, 0, None) == 0             # H == 0
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, None, None) == INVALID
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE + 4, None) == INVALID   # cost alignment
+    assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 2, 300000, FAKE, None) == UNSUPPORTED
+    assert lib.fam_retention_overlap(FAKE, FAKE, None, FAKE, 2, 100, FAKE, None) == INVALID
+    assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 0, 100, None, None) == 0
