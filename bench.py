@@ -13,12 +13,14 @@ launch over its mean HIP-event duration); `cpu_baseline` times the fp64
 oracle on a bounded sample of the same workload.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                       [--no-cpu-baseline] [--target-steps N] [--chunked-runs N]
+                       [--no-cpu-baseline] [--target-steps N] [--ranking-runs N]
+                       [--chunked-runs N]
 
-Two widened rows are timed apart from the step and reported beside it: the
-KVpop target (per-query-head mass and its epilogue) and the chunked
-prefill-compress loop (chunks of 4096, a uniform budget of 16384 rows per
-head, compaction in place).
+Three widened rows are timed apart from the step and reported beside it:
+the KVpop target (per-query-head mass and its epilogue), the ranking-quality
+measures (order, eviction cost over budgets, retention overlap) on the
+step's masses, and the chunked prefill-compress loop (chunks of 4096, a
+uniform budget of 16384 rows per head, compaction in place).
 """
 from __future__ import annotations
 
@@ -238,6 +240,58 @@ def chunked_row(runs, q, k, v, wl, stream, chunk=4096, budget=16384):
     }
 
 
+def ranking_row(runs, mass, wl, stream):
+    """Time the ranking-quality row on the step's masses: fam_rank_order of the
+    masses (the teacher's order) and of a recency score (newest first),
+    fam_eviction_cost of both against the masses (KVP's cost over budgets and
+    its normalised form), and fam_retention_overlap of the two kept sets at a
+    budget of S/8 (KVpop's top-k retention recall)."""
+    m = mass[0]
+    H, S = m.shape
+    recency = torch.arange(S, dtype=torch.float32, device=m.device).expand(H, S).contiguous()
+    order = torch.empty((H, S), dtype=torch.int32, device=m.device)
+    ws = torch.empty(max(8, fam.fam_rank_order_workspace_size(H, S)), dtype=torch.uint8, device=m.device)
+    cost = torch.empty(H, dtype=torch.float64, device=m.device)
+    budgets = [S // 8] * H
+    ia, oa = fam.evict_select(m, budgets, wl.sinks, wl.recent)
+    ib, ob = fam.evict_select(recency, budgets, wl.sinks, wl.recent)
+
+    def one(e=None):
+        if e:
+            e[0].record(stream)
+        fam.fam_rank_order(m, order=order, workspace=ws)
+        if e:
+            e[1].record(stream)
+        fam.fam_eviction_cost(m, order, cost=cost)
+        if e:
+            e[2].record(stream)
+        common = fam.fam_retention_overlap(ia, oa, ib, ob, S)
+        if e:
+            e[3].record(stream)
+        return common
+
+    one()
+    torch.cuda.synchronize()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(runs)]
+    for e in ev:
+        common = one(e)
+    torch.cuda.synchronize()
+    ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(3)]
+    ratio = fam.eviction_cost_ratio(recency, m).cpu().numpy()
+    recall = (common.double() / (oa[1:] - oa[:-1]).double()).cpu().numpy()
+    rank_bytes = 2 * 4 * H * S   # scores in, order out
+    return {
+        "heads": H, "entries_per_head": S, "runs": runs,
+        "ms": {"fam_rank_order": round(ms[0], 4), "fam_eviction_cost": round(ms[1], 4),
+               "fam_retention_overlap": round(ms[2], 4)},
+        "fam_rank_order": {"bound": "latency", "bytes": rank_bytes,
+                           "achieved": round(rank_bytes / (ms[0] * 1e-3) / 1e9, 3), "unit": "GB/s",
+                           "note": "one workgroup per head, four dependent radix passes"},
+        "recency_vs_mass": {"normalised_cost_mean": round(float(ratio.mean()), 6),
+                            "retention_recall_mean_at_S_over_8": round(float(recall.mean()), 6)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -249,6 +303,8 @@ def main():
                     help="timed runs of the KVpop target row (per-head mass + epilogue); 0 skips it")
     ap.add_argument("--chunked-runs", type=int, default=1,
                     help="timed runs of the chunked prefill-compress loop; 0 skips it")
+    ap.add_argument("--ranking-runs", type=int, default=3,
+                    help="timed runs of the ranking-quality row; 0 skips it")
     ap.add_argument("--chunked-only", action="store_true",
                     help="run only the chunked prefill-compress row (for a kernel trace of it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -373,6 +429,8 @@ def main():
         out["kvpop_target"] = kvpop_target_row(args.target_steps, q, k, lse, wl, work, stream)
         for n in ("fam_mass_per_head", "fam_kvpop_target"):
             out["kvpop_target"][n]["traffic"] = traffic.get(n)
+    if args.ranking_runs > 0:
+        out["ranking"] = ranking_row(args.ranking_runs, mass, wl, stream)
     if args.chunked_runs > 0:
         out["chunked_prefill"] = chunked_row(args.chunked_runs, q, k, v, wl, stream)
     if not args.no_cpu_baseline:

@@ -14,11 +14,12 @@
 // the complemented order key, 8 bits per pass, between two buffers of (key,
 // position) pairs in the workspace; the first pass reads the scores and the
 // last writes only positions. A pass counts its digits over the whole head
-// (LDS atomics) and scans the 256 counts into bases, then walks the head in
-// tiles of 1024 entries in order. Inside a tile an entry's rank among the
+// (LDS atomics), scans the 256 counts into bases, then walks the head in
+// tiles of 4096 entries in order. Inside a tile an entry's rank among the
 // entries with its digit comes from eight wave ballots (the lanes that share
-// its digit) and a per-digit prefix over the 16 waves, so the scatter keeps
-// the order of equal digits and the sort is stable.
+// its digit), the wave's running count of that digit, and a per-digit prefix
+// over the 16 waves, so the scatter keeps the order of equal digits and the
+// sort is stable.
 //
 // cost_kernel: cost[h] = sum_r (r + 1) * importance[h, order[h, r]], which
 // equals the sum over budgets b = 0 .. n of the importance evicted at b
@@ -36,9 +37,24 @@ namespace {
 constexpr int kRankThreads = 1024;
 constexpr int kRankWaves = kRankThreads / 64;
 constexpr int kDigits = 256;
+constexpr int kRankSteps = 4;                           // 64-lane steps per wave and tile
+constexpr int kRankTile = kRankThreads * kRankSteps;
+
+// Lanes of the wave whose digit equals this lane's (among the lanes in `live`).
+__device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool live) {
+  uint64_t peers = __ballot(live);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t bal = __ballot(bit);
+    peers &= bit ? bal : ~bal;
+  }
+  return peers;
+}
 
 __global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
-  __shared__ int base[kDigits];                // digit base, then running offset
+  __shared__ int base[kDigits];                // digit counts, then running offsets
+  __shared__ int next[kDigits];                // counts of the pass's digit
   __shared__ int wcnt[kRankWaves][kDigits];    // per wave: count, then exclusive prefix
   const int h = blockIdx.x;
   const int n = p.n;
@@ -49,19 +65,19 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
   int32_t* out = p.order + (int64_t)h * n;
   const uint64_t below = (1ull << lane) - 1ull;
 
+  if (tid < kDigits) {
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) wcnt[w][tid] = 0;
+  }
   for (int pass = 0; pass < 4; ++pass) {
     const int shift = 8 * pass;
     const u32x2_t* src = pass == 1 || pass == 3 ? buf0 : buf1;   // pass 0 reads the scores
     u32x2_t* dst = pass == 0 || pass == 2 ? buf0 : buf1;         // pass 3 writes positions
-    if (tid < kDigits) {
-      base[tid] = 0;
-#pragma unroll
-      for (int w = 0; w < kRankWaves; ++w) wcnt[w][tid] = 0;
-    }
+    if (tid < kDigits) next[tid] = 0;
     __syncthreads();
     for (int e = tid; e < n; e += kRankThreads) {
       const uint32_t key = pass == 0 ? ~order_key(srow[e]) : src[e].x;
-      atomicAdd(&base[(key >> shift) & 255u], 1);
+      atomicAdd(&next[(key >> shift) & 255u], 1);
     }
     __syncthreads();
     // exclusive scan of the 256 digit counts (wave 0, four digits per lane)
@@ -69,7 +85,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
       int c[4], sum = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        c[i] = base[4 * lane + i];
+        c[i] = next[4 * lane + i];
         sum += c[i];
       }
       int incl = sum;
@@ -87,30 +103,45 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
     }
     __syncthreads();
 
-    for (int t0 = 0; t0 < n; t0 += kRankThreads) {   // uniform across the workgroup
-      const int e = t0 + tid;
-      const bool valid = e < n;
-      uint32_t key = 0, pos = 0;
-      if (valid) {
-        if (pass == 0) {
-          key = ~order_key(srow[e]);
-          pos = (uint32_t)e;
-        } else {
-          const u32x2_t kv = src[e];
-          key = kv.x;
-          pos = kv.y;
+    // Tiles of kRankTile entries; wave w takes the contiguous 256 entries
+    // t0 + 256 w .. in four 64-lane steps, so (wave, step, lane) order is
+    // entry order. A step ranks its lanes among the wave's earlier entries of
+    // the same digit (the wave's running count in LDS plus the lanes below
+    // with that digit); after the tile a per-digit prefix over the waves
+    // gives every entry its place.
+    for (int t0 = 0; t0 < n; t0 += kRankTile) {   // uniform across the workgroup
+      uint32_t key[kRankSteps], pos[kRankSteps], dg[kRankSteps];
+      int rank[kRankSteps];
+#pragma unroll
+      for (int st = 0; st < kRankSteps; ++st) {
+        const int e = t0 + wave * 64 * kRankSteps + st * 64 + lane;
+        key[st] = 0;
+        pos[st] = 0;
+        if (e < n) {
+          if (pass == 0) {
+            key[st] = ~order_key(srow[e]);
+            pos[st] = (uint32_t)e;
+          } else {
+            const u32x2_t kv = src[e];
+            key[st] = kv.x;
+            pos[st] = kv.y;
+          }
         }
       }
-      const uint32_t d = (key >> shift) & 255u;
-      uint64_t peers = __ballot(valid);
 #pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t bal = __ballot(bit);
-        peers &= bit ? bal : ~bal;
+      for (int st = 0; st < kRankSteps; ++st) {
+        const int e = t0 + wave * 64 * kRankSteps + st * 64 + lane;
+        const bool valid = e < n;
+        const uint32_t d = (key[st] >> shift) & 255u;
+        const uint64_t peers = digit_peers(d, valid);
+        const uint64_t before = peers & below;
+        // all lanes of a digit read the wave's count before its first lane
+        // adds the step's lanes (LDS operations of a wave run in order)
+        const int seen = valid ? wcnt[wave][d] : 0;
+        rank[st] = valid ? seen + (int)__popcll(before) : -1;
+        dg[st] = d;
+        if (valid && before == 0ull) wcnt[wave][d] = seen + (int)__popcll(peers);
       }
-      const uint64_t before = peers & below;
-      if (valid && before == 0ull) wcnt[wave][d] = __popcll(peers);
       __syncthreads();
       int total = 0;
       if (tid < kDigits) {
@@ -122,10 +153,12 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
         }
       }
       __syncthreads();
-      if (valid) {
-        const int at = base[d] + wcnt[wave][d] + __popcll(before);
-        if (pass == 3) out[at] = (int32_t)pos;
-        else dst[at] = u32x2_t{key, pos};
+#pragma unroll
+      for (int st = 0; st < kRankSteps; ++st) {
+        if (rank[st] < 0) continue;
+        const int at = base[dg[st]] + wcnt[wave][dg[st]] + rank[st];
+        if (pass == 3) out[at] = (int32_t)pos[st];
+        else dst[at] = u32x2_t{key[st], pos[st]};
       }
       __syncthreads();
       if (tid < kDigits) {
@@ -138,7 +171,8 @@ __global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
   }
 }
 
-constexpr int kCostThreads = 256;
+constexpr int kCostThreads = 1024;
+constexpr int kCostUnroll = 4;   // gathers in flight per thread
 
 __global__ __launch_bounds__(kCostThreads) void cost_kernel(CostArgs p) {
   __shared__ double part[kCostThreads];
@@ -146,9 +180,19 @@ __global__ __launch_bounds__(kCostThreads) void cost_kernel(CostArgs p) {
   const float* imp = p.importance + h * p.row_stride;
   const int32_t* ord = p.order + (int64_t)h * p.n;
   double acc = 0.0;
-  for (int r = threadIdx.x; r < p.n; r += kCostThreads) {
-    const int j = ord[r];
-    if (j >= 0 && j < p.n) acc = fma((double)(r + 1), (double)imp[j], acc);
+  for (int r0 = threadIdx.x; r0 < p.n; r0 += kCostThreads * kCostUnroll) {
+    int j[kCostUnroll];
+    float x[kCostUnroll];
+#pragma unroll
+    for (int u = 0; u < kCostUnroll; ++u) {
+      const int r = r0 + u * kCostThreads;
+      j[u] = r < p.n ? ord[r] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kCostUnroll; ++u) x[u] = (j[u] >= 0 && j[u] < p.n) ? imp[j[u]] : 0.f;
+#pragma unroll
+    for (int u = 0; u < kCostUnroll; ++u)
+      acc = fma((double)(r0 + u * kCostThreads + 1), (double)x[u], acc);
   }
   part[threadIdx.x] = acc;
   __syncthreads();

@@ -498,6 +498,10 @@ def _score_rows(x: torch.Tensor, what: str) -> Tuple[int, int]:
     return x.shape[0], x.shape[1]
 
 
+def fam_rank_order_workspace_size(H: int, n: int) -> int:
+    return int(load().fam_rank_order_workspace_size(int(H), int(n)))
+
+
 def fam_rank_order(scores: torch.Tensor, order: Optional[torch.Tensor] = None,
                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Positions of each row's entries, best first (ties to the lower position)."""
@@ -505,8 +509,8 @@ def fam_rank_order(scores: torch.Tensor, order: Optional[torch.Tensor] = None,
     if order is None:
         order = torch.empty((H, n), dtype=torch.int32, device=scores.device)
     if workspace is None:
-        nbytes = int(load().fam_rank_order_workspace_size(H, n))
-        workspace = torch.empty(max(nbytes, 8), dtype=torch.uint8, device=scores.device)
+        workspace = torch.empty(max(fam_rank_order_workspace_size(H, n), 8), dtype=torch.uint8,
+                                device=scores.device)
     _check(load().fam_rank_order(scores.data_ptr(), scores.stride(0), H, n, order.data_ptr(),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                  _stream(scores)))

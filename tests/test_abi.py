@@ -259,3 +259,9 @@ def test_ranking_validation():
     assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 2, 300000, FAKE, None) == UNSUPPORTED
     assert lib.fam_retention_overlap(FAKE, FAKE, None, FAKE, 2, 100, FAKE, None) == INVALID
     assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 0, 100, None, None) == 0
+
+
+def test_every_entry_point_has_a_python_wrapper_of_the_same_name():
+    plain = {"fam_status_string", "fam_last_error"}
+    missing = [n for n in fam.EXPORTED if n not in plain and not callable(getattr(fam, n, None))]
+    assert missing == []
