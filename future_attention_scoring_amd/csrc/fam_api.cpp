@@ -358,7 +358,7 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   if (H == 0) return ok();
   if (!scores || !idx || !offsets_dev || !budgets)
     return fail(FAM_ERR_INVALID_ARG, "scores, budgets, idx and offsets_dev must be non-null");
-  if (score_row_stride < S) return fail(FAM_ERR_INVALID_ARG, "score row stride must be >= S");
+  if (H > 1 && score_row_stride < S) return fail(FAM_ERR_INVALID_ARG, "score row stride must be >= S");
   for (int h = 0; h < H; ++h)
     if (budgets[h] < 0) return fail(FAM_ERR_INVALID_ARG, "budget of head %d is negative", h);
   const Plan p = plan_of(S, sinks, recent);
@@ -514,7 +514,7 @@ fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n,
   if (n > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "n = %d exceeds %d", n, kMaxSeq);
   if (H == 0 || n == 0) return ok();
   if (!scores || !order) return fail(FAM_ERR_INVALID_ARG, "scores and order must be non-null");
-  if (row_stride < n) return fail(FAM_ERR_INVALID_ARG, "row stride must be >= n");
+  if (H > 1 && row_stride < n) return fail(FAM_ERR_INVALID_ARG, "row stride must be >= n");
   if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(order)) & 3u)
     return fail(FAM_ERR_INVALID_ARG, "scores and order must be 4-byte aligned");
   const size_t need = fam_rank_order_workspace_size(H, n);
@@ -535,7 +535,7 @@ fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const 
   if (!cost) return fail(FAM_ERR_INVALID_ARG, "cost must be non-null");
   if (n > 0 && (!importance || !order))
     return fail(FAM_ERR_INVALID_ARG, "importance and order must be non-null");
-  if (row_stride < n) return fail(FAM_ERR_INVALID_ARG, "row stride must be >= n");
+  if (H > 1 && row_stride < n) return fail(FAM_ERR_INVALID_ARG, "row stride must be >= n");
   if ((reinterpret_cast<uintptr_t>(importance) | reinterpret_cast<uintptr_t>(order)) & 3u ||
       (reinterpret_cast<uintptr_t>(cost) & 7u))
     return fail(FAM_ERR_INVALID_ARG, "importance and order must be 4-byte, cost 8-byte aligned");
@@ -558,6 +558,32 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
   fam::OverlapArgs a{idx_a, offsets_a, idx_b, offsets_b, common, H, S};
   return hip_status(fam::launch_overlap(a, static_cast<hipStream_t>(stream)),
                     "fam_retention_overlap launch");
+}
+
+
+size_t fam_topk_cutoff_workspace_size(int H, int S) {
+  if (H < 0 || S < 0) return 0;
+  return (size_t)H * S * sizeof(int32_t);
+}
+
+fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int32_t* tau,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  if (H < 0 || S < 1 || w < 0 || k < 0)
+    return fail(FAM_ERR_INVALID_ARG, "need H >= 0, S >= 1, w >= 0 and k >= 0");
+  if (S > fam::kCutoffMaxS)
+    return fail(FAM_ERR_UNSUPPORTED, "S = %d exceeds %d positions", S, fam::kCutoffMaxS);
+  if (H == 0) return ok();
+  if (!order || !tau) return fail(FAM_ERR_INVALID_ARG, "order and tau must be non-null");
+  if ((reinterpret_cast<uintptr_t>(order) | reinterpret_cast<uintptr_t>(tau)) & 3u)
+    return fail(FAM_ERR_INVALID_ARG, "order and tau must be 4-byte aligned");
+  const size_t need = fam_topk_cutoff_workspace_size(H, S);
+  if (!workspace || workspace_bytes < need)
+    return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+  fam::CutoffArgs a{order, static_cast<int32_t*>(workspace), tau, H, S, w, k};
+  return hip_status(fam::launch_cutoff(a, static_cast<hipStream_t>(stream)), "fam_topk_cutoff launch");
 }
 
 }  // extern "C"

@@ -159,4 +159,14 @@ struct OverlapArgs {
 constexpr int kOverlapMaxS = 1 << 18;  // bitmap of the positions in 32 KiB of LDS
 hipError_t launch_overlap(const OverlapArgs& a, hipStream_t s);
 
+// Running top-k cut-off over static ranks.
+struct CutoffArgs {
+  const int32_t* order;  // [H, S] positions best first (fam_rank_order)
+  int32_t* rank;         // [H, S] workspace: rank of every position
+  int32_t* tau;          // [H, S] out
+  int H, S, w, k;
+};
+constexpr int kCutoffMaxS = 1 << 18;  // bitset of the ranks in 32 KiB of LDS
+hipError_t launch_cutoff(const CutoffArgs& a, hipStream_t s);
+
 }  // namespace fam

@@ -53,6 +53,8 @@ _SIGNATURES = {
     "fam_rank_order_workspace_size": (ctypes.c_size_t, [_i, _i]),
     "fam_eviction_cost": (_i, [_p, _i64, _p, _i, _i, _p, _p]),
     "fam_retention_overlap": (_i, [_p, _p, _p, _p, _i, _i, _p, _p]),
+    "fam_topk_cutoff": (_i, [_p, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]),
+    "fam_topk_cutoff_workspace_size": (ctypes.c_size_t, [_i, _i]),
 }
 EXPORTED = tuple(_SIGNATURES)
 
@@ -279,7 +281,7 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
                  workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
     if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
         raise FamError(1, "scores must be a device fp32 [H, S] tensor")
-    if scores.stride(1) != 1:
+    if scores.shape[1] > 1 and scores.stride(1) != 1:
         raise FamError(1, "scores rows must be contiguous")
     H, S = scores.shape
     b = _i64_array(budgets)
@@ -294,7 +296,7 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
     if workspace is None:
         nbytes = evict_select_workspace_size(H, S, sinks, recent)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=scores.device)
-    _check(load().evict_select(scores.data_ptr(), scores.stride(0), H, S, b.ctypes.data,
+    _check(load().evict_select(scores.data_ptr(), _row_stride(scores), H, S, b.ctypes.data,
                                int(sinks), int(recent), idx.data_ptr(), offsets.data_ptr(),
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(scores)))
@@ -493,9 +495,15 @@ def prefill_compress(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: i
 
 
 def _score_rows(x: torch.Tensor, what: str) -> Tuple[int, int]:
-    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda or x.stride(1) != 1:
+    if x.dim() != 2 or x.dtype != torch.float32 or not x.is_cuda or (x.shape[1] > 1 and x.stride(1) != 1):
         raise FamError(1, f"{what} must be a device fp32 [H, n] tensor with contiguous rows")
     return x.shape[0], x.shape[1]
+
+
+def _row_stride(x: torch.Tensor) -> int:
+    """Row stride of a 2-D tensor; a single row's stride is irrelevant (torch
+    may report any value for a dimension of size 1)."""
+    return x.stride(0) if x.shape[0] > 1 else x.shape[1]
 
 
 def fam_rank_order_workspace_size(H: int, n: int) -> int:
@@ -511,7 +519,7 @@ def fam_rank_order(scores: torch.Tensor, order: Optional[torch.Tensor] = None,
     if workspace is None:
         workspace = torch.empty(max(fam_rank_order_workspace_size(H, n), 8), dtype=torch.uint8,
                                 device=scores.device)
-    _check(load().fam_rank_order(scores.data_ptr(), scores.stride(0), H, n, order.data_ptr(),
+    _check(load().fam_rank_order(scores.data_ptr(), _row_stride(scores), H, n, order.data_ptr(),
                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                  _stream(scores)))
     return order
@@ -525,7 +533,7 @@ def fam_eviction_cost(importance: torch.Tensor, order: torch.Tensor,
         raise FamError(1, "order must be a contiguous int32 [H, n] tensor")
     if cost is None:
         cost = torch.empty(H, dtype=torch.float64, device=importance.device)
-    _check(load().fam_eviction_cost(importance.data_ptr(), importance.stride(0), order.data_ptr(), H,
+    _check(load().fam_eviction_cost(importance.data_ptr(), _row_stride(importance), order.data_ptr(), H,
                                     n, cost.data_ptr(), _stream(importance)))
     return cost
 
@@ -553,3 +561,24 @@ def fam_retention_overlap(idx_a: torch.Tensor, offsets_a: torch.Tensor, idx_b: t
                                         offsets_b.data_ptr(), H, int(S), common.data_ptr(),
                                         _stream(idx_a)))
     return common
+
+
+def fam_topk_cutoff_workspace_size(H: int, S: int) -> int:
+    return int(load().fam_topk_cutoff_workspace_size(int(H), int(S)))
+
+
+def fam_topk_cutoff(order: torch.Tensor, w: int, k: int, tau: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """KVpop's running cut-off tau [H, S] from fam_rank_order's order [H, S]."""
+    if order.dim() != 2 or order.dtype != torch.int32 or not order.is_cuda or not order.is_contiguous():
+        raise FamError(1, "order must be a contiguous device int32 [H, S] tensor")
+    H, S = order.shape
+    if tau is None:
+        tau = torch.empty((H, S), dtype=torch.int32, device=order.device)
+    if workspace is None:
+        workspace = torch.empty(max(fam_topk_cutoff_workspace_size(H, S), 4), dtype=torch.uint8,
+                                device=order.device)
+    _check(load().fam_topk_cutoff(order.data_ptr(), H, S, int(w), int(k), tau.data_ptr(),
+                                  workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                  _stream(order)))
+    return tau

@@ -294,7 +294,8 @@ fam_status fam_budgets_from_ratios(int H, const double* ratios, int64_t t, int64
  * best are chosen by score descending; equal scores go to the lower
  * position; -0.0 equals +0.0; NaN ranks below every number.
  *
- *   scores      device, [H, S] fp32, row stride `score_row_stride` (>= S)
+ *   scores      device, [H, S] fp32, row stride `score_row_stride` (>= S when
+ *               H > 1)
  *   budgets     host, [H] int64 (as for evict_plan)
  *   idx         device out, [offsets[H]] int32: for each head h, the kept
  *               positions in ascending order at idx[offsets[h] ...]
@@ -417,7 +418,8 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
  *
  *   order[h * n + r] = position (0 .. n-1) of the r-th best entry of row h
  *
- *   scores     device, [H] rows of n fp32 with row stride row_stride >= n
+ *   scores     device, [H] rows of n fp32 with row stride row_stride (>= n
+ *              when H > 1)
  *   order      device out, [H, n] int32, fully overwritten
  *   workspace  device scratch of fam_rank_order_workspace_size(H, n) bytes
  *              (16 * H * n), 8-byte aligned, owned by the caller; contents
@@ -446,7 +448,8 @@ size_t fam_rank_order_workspace_size(int H, int n);
  * the order of importance (it is >= 1 for non-negative importance and
  * equals 1 exactly for an optimal order).
  *
- *   importance  device, [H] rows of n fp32, row stride row_stride >= n
+ *   importance  device, [H] rows of n fp32, row stride row_stride (>= n when
+ *               H > 1)
  *   order       device, [H, n] int32 (entries outside [0, n) are skipped)
  *   cost        device out, [H] fp64 (sums in fp64, fixed order)
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
@@ -475,6 +478,36 @@ fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const 
 fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
                                  const int32_t* idx_b, const int64_t* offsets_b, int H, int S,
                                  int64_t* common, void* stream);
+
+/* ------------------------------------------------------------------------
+ * fam_topk_cutoff -- the running top-k cut-off of a sparse prefill mask.
+ *
+ * [KVpop] "Delayed Memory Scoring" and "Efficient Online Pruning": tokens
+ * are pre-sorted by a static priority score (rank 1 = best); at query q the
+ * token t = q - w leaves the protected window and becomes eligible; tau_q is
+ * the rank of the k-th best eligible token, and the attention keeps the
+ * sinks, the window and the eligible tokens with rank <= tau_q. The page
+ * finds tau_q with a Fenwick tree; this computes the same values with a
+ * sweep over a bitset of the eligible ranks (amortised O(1) per query).
+ *
+ *   tau[h, q] = k-th smallest rank among the positions t <= q - w of head h,
+ *               S if fewer than k are eligible, 0 if k == 0
+ *
+ *   order      device, [H, S] int32 positions best first (fam_rank_order's
+ *              output: every position exactly once; any other content gives
+ *              unspecified cut-offs, never an access out of bounds)
+ *   tau        device out, [H, S] int32, fully overwritten
+ *   workspace  device scratch of fam_topk_cutoff_workspace_size(H, S) bytes
+ *              (4 * H * S: the rank of every position), 4-byte aligned
+ * Requirements: S <= 262144 (the bitset lives in LDS); w >= 0, k >= 0.
+ * One workgroup sweeps one head sequentially, so a call is bound by latency
+ * (about 1 ms per 131072 queries, heads in parallel).
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
+ * FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int32_t* tau,
+                           void* workspace, size_t workspace_bytes, void* stream);
+size_t fam_topk_cutoff_workspace_size(int H, int S);
 
 #ifdef __cplusplus
 }

@@ -12,8 +12,9 @@ Modules
   kvpop_target    count-normalised log target and group aggregation (KVpop)
   chunked         chunked prefill with compression after every chunk (KVP)
   ranking         eviction cost over budgets and retention recall (KVP, KVpop)
+  topk_cutoff     running top-k cut-off over static ranks (KVpop)
 
 Every function is pinned by the CPU tests in ``tests/test_oracle_*.py``
 against brute force, closed forms, invariants or the pages' worked example.
 """
-from . import chunked, fam_oracle, kvpop_target, ranking, select_oracle, soft_topk  # noqa: F401
+from . import chunked, fam_oracle, kvpop_target, ranking, select_oracle, soft_topk, topk_cutoff  # noqa: F401

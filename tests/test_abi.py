@@ -265,3 +265,15 @@ def test_every_entry_point_has_a_python_wrapper_of_the_same_name():
     plain = {"fam_status_string", "fam_last_error"}
     missing = [n for n in fam.EXPORTED if n not in plain and not callable(getattr(fam, n, None))]
     assert missing == []
+
+
+def test_topk_cutoff_validation():
+    lib = fam.load()
+    assert lib.fam_topk_cutoff_workspace_size(8, 131072) == 4 * 8 * 131072
+    ws = lib.fam_topk_cutoff_workspace_size(2, 100)
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, 10, FAKE, FAKE, ws - 1, None) == WORKSPACE
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, -1, 10, FAKE, FAKE, ws, None) == INVALID
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, -1, FAKE, FAKE, ws, None) == INVALID
+    assert lib.fam_topk_cutoff(FAKE, 2, 300000, 8, 10, FAKE, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.fam_topk_cutoff(None, 2, 100, 8, 10, FAKE, FAKE, ws, None) == INVALID
+    assert lib.fam_topk_cutoff(None, 0, 100, 8, 10, None, None, 0, None) == 0
