@@ -244,8 +244,9 @@ def ranking_row(runs, mass, wl, stream):
     """Time the ranking-quality row on the step's masses: fam_rank_order of the
     masses (the teacher's order) and of a recency score (newest first),
     fam_eviction_cost of both against the masses (KVP's cost over budgets and
-    its normalised form), and fam_retention_overlap of the two kept sets at a
-    budget of S/8 (KVpop's top-k retention recall)."""
+    its normalised form), fam_retention_overlap of the two kept sets at a
+    budget of S/8 (KVpop's top-k retention recall), and fam_topk_cutoff of the
+    mass order (KVpop's running cut-off, window W, k = S/8)."""
     m = mass[0]
     H, S = m.shape
     recency = torch.arange(S, dtype=torch.float32, device=m.device).expand(H, S).contiguous()
@@ -255,6 +256,9 @@ def ranking_row(runs, mass, wl, stream):
     budgets = [S // 8] * H
     ia, oa = fam.evict_select(m, budgets, wl.sinks, wl.recent)
     ib, ob = fam.evict_select(recency, budgets, wl.sinks, wl.recent)
+
+    tau = torch.empty((H, S), dtype=torch.int32, device=m.device)
+    cut_ws = torch.empty(max(4, fam.fam_topk_cutoff_workspace_size(H, S)), dtype=torch.uint8, device=m.device)
 
     def one(e=None):
         if e:
@@ -268,22 +272,27 @@ def ranking_row(runs, mass, wl, stream):
         common = fam.fam_retention_overlap(ia, oa, ib, ob, S)
         if e:
             e[3].record(stream)
+        fam.fam_topk_cutoff(order, wl.W, S // 8, tau=tau, workspace=cut_ws)
+        if e:
+            e[4].record(stream)
         return common
 
     one()
     torch.cuda.synchronize()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(runs)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(runs)]
     for e in ev:
         common = one(e)
     torch.cuda.synchronize()
-    ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(3)]
+    ms = [float(np.mean([e[i].elapsed_time(e[i + 1]) for e in ev])) for i in range(4)]
     ratio = fam.eviction_cost_ratio(recency, m).cpu().numpy()
     recall = (common.double() / (oa[1:] - oa[:-1]).double()).cpu().numpy()
     rank_bytes = 2 * 4 * H * S   # scores in, order out
     return {
         "heads": H, "entries_per_head": S, "runs": runs,
         "ms": {"fam_rank_order": round(ms[0], 4), "fam_eviction_cost": round(ms[1], 4),
-               "fam_retention_overlap": round(ms[2], 4)},
+               "fam_retention_overlap": round(ms[2], 4), "fam_topk_cutoff": round(ms[3], 4)},
+        "fam_topk_cutoff": {"window": wl.W, "k": S // 8, "queries_per_head": S,
+                            "queries_per_s": round(H * S / (ms[3] * 1e-3), 1)},
         "fam_rank_order": {"bound": "latency", "bytes": rank_bytes,
                            "achieved": round(rank_bytes / (ms[0] * 1e-3) / 1e9, 3), "unit": "GB/s",
                            "note": "one workgroup per head, four dependent radix passes"},

@@ -20,7 +20,8 @@
 // ranks_kernel: rank[h, order[h, r]] = r + 1 (the inverse of the order that
 // fam_rank_order writes). cutoff_kernel: one workgroup per head; all threads
 // stage the ranks of the next chunk of 2048 newly eligible tokens in LDS and
-// store the previous chunk's cut-offs, while one lane runs the sweep.
+// store the previous chunk's cut-offs, while wave 0 runs the sweep on
+// wave-uniform values (scalar registers and branches).
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -44,8 +45,8 @@ __global__ __launch_bounds__(256) void ranks_kernel(const int32_t* order, int32_
 
 __global__ __launch_bounds__(kCutThreads) void cutoff_kernel(CutoffArgs p) {
   __shared__ uint32_t bits[kCutWords];          // bit r-1 set: rank r is eligible
-  __shared__ int32_t rk[2][kCutChunk];          // ranks of the tokens that become eligible
-  __shared__ int32_t tau[kCutChunk];            // cut-offs of the chunk's queries
+  __shared__ __attribute__((aligned(16))) int32_t rk[2][kCutChunk];   // ranks of the tokens that become eligible
+  __shared__ __attribute__((aligned(16))) int32_t tau[kCutChunk];     // cut-offs of the chunk's queries
   const int h = blockIdx.x;
   const int S = p.S, w = p.w, k = p.k;
   const int tid = threadIdx.x;
@@ -63,7 +64,7 @@ __global__ __launch_bounds__(kCutThreads) void cutoff_kernel(CutoffArgs p) {
   stage(0, 0);
   __syncthreads();
 
-  // sweep state (lane 0 of wave 0 only)
+  // sweep state (wave 0, uniform across its lanes)
   int count = 0;       // eligible tokens so far
   int cut = S;         // current cut-off once count >= k
   int maxr = 0;        // largest eligible rank while count < k
@@ -71,30 +72,40 @@ __global__ __launch_bounds__(kCutThreads) void cutoff_kernel(CutoffArgs p) {
   for (int c = 0; c < nchunks; ++c) {   // uniform across the workgroup
     const int q0 = c * kCutChunk;
     if (c + 1 < nchunks) stage(q0 + kCutChunk, (c + 1) & 1);
-    if (tid == 0 && k == 0) {
-      for (int i = 0; i < min(kCutChunk, S - q0); ++i) tau[i] = 0;
-    } else if (tid == 0) {
-      const int nq = min(kCutChunk, S - q0);
-      for (int i = 0; i < nq; ++i) {
-        const int r = rk[c & 1][i];
-        if (r >= 1 && r <= S) {
-          bits[(r - 1) >> 5] |= 1u << ((r - 1) & 31);
-          ++count;
-          if (count <= k) {
-            maxr = max(maxr, r);
-            if (count == k) cut = maxr;
-          } else if (r < cut) {
-            // the old k-th best drops out: the largest present rank below it
-            int b = cut - 2;   // bit index of rank cut - 1
-            uint32_t word = bits[b >> 5] & (0xffffffffu >> (31 - (b & 31)));
-            while (word == 0u) {
-              b = (b & ~31) - 1;
-              word = bits[b >> 5];
+    if (tid < 64) {
+      // wave 0 runs the sweep on wave-uniform values (scalar registers and
+      // branches); lane 0 writes
+      const int nq4 = (min(kCutChunk, S - q0) + 3) & ~3;
+      const int4* rk4 = reinterpret_cast<const int4*>(rk[c & 1]);
+      for (int i = 0; i < nq4; i += 4) {
+        const int4 cur = rk4[i >> 2];
+        const int rr[4] = {__builtin_amdgcn_readfirstlane(cur.x), __builtin_amdgcn_readfirstlane(cur.y),
+                           __builtin_amdgcn_readfirstlane(cur.z), __builtin_amdgcn_readfirstlane(cur.w)};
+        int out4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int r = rr[j];
+          if (k > 0 && r >= 1 && r <= S) {
+            const int bi = r - 1;
+            if (tid == 0) atomicOr(&bits[bi >> 5], 1u << (bi & 31));
+            ++count;
+            if (count <= k) {
+              maxr = max(maxr, r);
+              if (count == k) cut = maxr;
+            } else if (r < cut) {
+              // the old k-th best drops out: the largest present rank below it
+              int b = cut - 2;   // bit index of rank cut - 1
+              uint32_t word = __builtin_amdgcn_readfirstlane(bits[b >> 5]) & (0xffffffffu >> (31 - (b & 31)));
+              while (word == 0u) {
+                b = (b & ~31) - 1;
+                word = __builtin_amdgcn_readfirstlane(bits[b >> 5]);
+              }
+              cut = ((b & ~31) | (31 - __builtin_clz(word))) + 1;
             }
-            cut = ((b & ~31) | (31 - __builtin_clz(word))) + 1;
           }
+          out4[j] = k == 0 ? 0 : (count >= k ? cut : S);
         }
-        tau[i] = count >= k ? cut : S;
+        if (tid == 0) *reinterpret_cast<int4*>(&tau[i]) = int4{out4[0], out4[1], out4[2], out4[3]};
       }
     }
     __syncthreads();
