@@ -562,8 +562,8 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
 
 
 size_t fam_topk_cutoff_workspace_size(int H, int S) {
-  if (H < 0 || S < 0) return 0;
-  return (size_t)H * S * sizeof(int32_t);
+  if (H < 0 || S < 1 || S > fam::kCutoffMaxS) return 0;
+  return (size_t)H * S * sizeof(int32_t) + fam::cutoff_workspace_bytes(H, S);
 }
 
 fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int32_t* tau,
@@ -572,6 +572,7 @@ fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int
     return fail(FAM_ERR_INVALID_ARG, "need H >= 0, S >= 1, w >= 0 and k >= 0");
   if (S > fam::kCutoffMaxS)
     return fail(FAM_ERR_UNSUPPORTED, "S = %d exceeds %d positions", S, fam::kCutoffMaxS);
+  if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
   if (H == 0) return ok();
   if (!order || !tau) return fail(FAM_ERR_INVALID_ARG, "order and tau must be non-null");
   if ((reinterpret_cast<uintptr_t>(order) | reinterpret_cast<uintptr_t>(tau)) & 3u)
@@ -582,7 +583,13 @@ fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int
                 workspace ? workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(workspace) & 3u)
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
-  fam::CutoffArgs a{order, static_cast<int32_t*>(workspace), tau, H, S, w, k};
+  fam::CutoffArgs a{};
+  a.order = order;
+  a.rank = static_cast<int32_t*>(workspace);
+  a.tau = tau;
+  a.ws = static_cast<int32_t*>(workspace) + (size_t)H * S;
+  a.H = H, a.S = S, a.w = w, a.k = k;
+  fam::cutoff_shape(S, a.L, a.nw, a.ntiles);
   return hip_status(fam::launch_cutoff(a, static_cast<hipStream_t>(stream)), "fam_topk_cutoff launch");
 }
 

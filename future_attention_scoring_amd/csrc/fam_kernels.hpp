@@ -164,9 +164,24 @@ struct CutoffArgs {
   const int32_t* order;  // [H, S] positions best first (fam_rank_order)
   int32_t* rank;         // [H, S] workspace: rank of every position
   int32_t* tau;          // [H, S] out
+  void* ws;              // wavelet matrix (cutoff_workspace_bytes after rank)
   int H, S, w, k;
+  int L, nw, ntiles;     // levels, words per level (with a terminal word), 4096-position tiles
 };
-constexpr int kCutoffMaxS = 1 << 18;  // bitset of the ranks in 32 KiB of LDS
+constexpr int kCutoffMaxS = 1 << 18;  // at most 64 tiles of 4096 positions
+// Levels (bits of a rank - 1), words per level and tiles for S positions, and
+// the workspace bytes after the ranks.
+inline void cutoff_shape(int S, int& L, int& nw, int& ntiles) {
+  L = 1;
+  while ((1 << L) < S) ++L;
+  ntiles = (S + 4095) / 4096;
+  nw = ntiles * 128 + 1;
+}
+inline size_t cutoff_workspace_bytes(int H, int S) {
+  int L, nw, ntiles;
+  cutoff_shape(S, L, nw, ntiles);
+  return 4 * ((size_t)2 * H * S + (size_t)2 * H * L * nw + (size_t)H * ntiles);
+}
 hipError_t launch_cutoff(const CutoffArgs& a, hipStream_t s);
 
 }  // namespace fam

@@ -487,8 +487,9 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
  * token t = q - w leaves the protected window and becomes eligible; tau_q is
  * the rank of the k-th best eligible token, and the attention keeps the
  * sinks, the window and the eligible tokens with rank <= tau_q. The page
- * finds tau_q with a Fenwick tree; this computes the same values with a
- * sweep over a bitset of the eligible ranks (amortised O(1) per query).
+ * finds tau_q with a Fenwick tree, one insertion per query; this answers
+ * every query independently from a wavelet matrix of the per-position ranks
+ * (tau_q is the k-th smallest value of a prefix of that sequence).
  *
  *   tau[h, q] = k-th smallest rank among the positions t <= q - w of head h,
  *               S if fewer than k are eligible, 0 if k == 0
@@ -498,10 +499,10 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
  *              unspecified cut-offs, never an access out of bounds)
  *   tau        device out, [H, S] int32, fully overwritten
  *   workspace  device scratch of fam_topk_cutoff_workspace_size(H, S) bytes
- *              (4 * H * S: the rank of every position), 4-byte aligned
- * Requirements: S <= 262144 (the bitset lives in LDS); w >= 0, k >= 0.
- * One workgroup sweeps one head sequentially, so a call is bound by latency
- * (about 1 ms per 131072 queries, heads in parallel).
+ *              (the ranks, two level sequences and the bit words and
+ *              counts of ceil(log2 S) levels: about 16 bytes per entry at
+ *              S = 131072), 4-byte aligned, owned by the caller
+ * Requirements: S <= 262144; H <= 65535; w >= 0, k >= 0.
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
  * FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */

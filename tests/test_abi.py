@@ -269,7 +269,8 @@ def test_every_entry_point_has_a_python_wrapper_of_the_same_name():
 
 def test_topk_cutoff_validation():
     lib = fam.load()
-    assert lib.fam_topk_cutoff_workspace_size(8, 131072) == 4 * 8 * 131072
+    assert lib.fam_topk_cutoff_workspace_size(8, 131072) >= 4 * 8 * 131072 * 3
+    assert lib.fam_topk_cutoff_workspace_size(8, 300000) == 0
     ws = lib.fam_topk_cutoff_workspace_size(2, 100)
     assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, 10, FAKE, FAKE, ws - 1, None) == WORKSPACE
     assert lib.fam_topk_cutoff(FAKE, 2, 100, -1, 10, FAKE, FAKE, ws, None) == INVALID
