@@ -4,10 +4,12 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
+#include <vector>
 
 #include "fam_kernels.hpp"
 
@@ -591,6 +593,63 @@ fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int
   a.H = H, a.S = S, a.w = w, a.k = k;
   fam::cutoff_shape(S, a.L, a.nw, a.ntiles);
   return hip_status(fam::launch_cutoff(a, static_cast<hipStream_t>(stream)), "fam_topk_cutoff launch");
+}
+
+
+fam_status fam_soft_topk(const double* x, int n, double k, double tau, double* out) {
+  if (n < 1 || !x || !out) return fail(FAM_ERR_INVALID_ARG, "need n >= 1 and non-null x and out");
+  if (!(k > 0.0) || !(k < (double)n)) return fail(FAM_ERR_INVALID_ARG, "need 0 < k < n (got k = %g, n = %d)", k, n);
+  if (!(tau > 0.0) || !std::isfinite(tau)) return fail(FAM_ERR_INVALID_ARG, "tau must be finite and > 0");
+  for (int i = 0; i < n; ++i)
+    if (!std::isfinite(x[i])) return fail(FAM_ERR_INVALID_ARG, "x[%d] is not finite", i);
+  // z = x / tau in decreasing order
+  std::vector<double> z(n);
+  for (int i = 0; i < n; ++i) z[i] = x[i] / tau;
+  std::sort(z.begin(), z.end(), [](double a, double b) { return a > b; });
+  // log S1(m) = log sum_{i<m} exp(-z_i) and log S2(m) = log sum_{i>=m} exp(z_i)
+  auto lae = [](double a, double b) {   // log(exp(a) + exp(b))
+    if (a == -HUGE_VAL) return b;
+    if (b == -HUGE_VAL) return a;
+    const double hi = a > b ? a : b, lo = a > b ? b : a;
+    return hi + std::log1p(std::exp(lo - hi));
+  };
+  std::vector<double> ls1(n + 1), ls2(n + 1);
+  ls1[0] = -HUGE_VAL;
+  for (int m = 1; m <= n; ++m) ls1[m] = lae(ls1[m - 1], -z[m - 1]);
+  ls2[n] = -HUGE_VAL;
+  for (int m = n - 1; m >= 0; --m) ls2[m] = lae(ls2[m + 1], z[m]);
+  // With m entries at or above lambda the masks sum to
+  // m - e^lambda S1 / 2 + e^-lambda S2 / 2; setting that to k gives a
+  // quadratic in e^lambda. Exactly one m is consistent with its own lambda.
+  double lam = 0.0;
+  bool found = false;
+  for (int m = 0; m <= n && !found; ++m) {
+    const double a = k - m;
+    double l;
+    if (m == 0) {
+      l = ls2[0] - std::log(2.0 * k);
+    } else if (m == n) {
+      l = std::log(2.0 * (n - k)) - ls1[n];
+    } else if (a > 0) {   // e^lambda = S2 / (sqrt(a^2 + S1 S2) + a)
+      const double root = 0.5 * lae(2.0 * std::log(a), ls1[m] + ls2[m]);
+      l = ls2[m] - lae(root, std::log(a));
+    } else if (a < 0) {   // e^lambda = (sqrt(a^2 + S1 S2) - a) / S1
+      const double root = 0.5 * lae(2.0 * std::log(-a), ls1[m] + ls2[m]);
+      l = lae(root, std::log(-a)) - ls1[m];
+    } else {
+      l = 0.5 * (ls1[m] + ls2[m]) - ls1[m];
+    }
+    if ((m == 0 || z[m - 1] >= l) && (m == n || l > z[m])) {
+      lam = l;
+      found = true;
+    }
+  }
+  if (!found) return fail(FAM_ERR_INVALID_ARG, "no consistent threshold (degenerate input)");
+  for (int i = 0; i < n; ++i) {
+    const double u = x[i] / tau - lam;
+    out[i] = u >= 0.0 ? 1.0 - 0.5 * std::exp(-u) : 0.5 * std::exp(u);
+  }
+  return ok();
 }
 
 }  // extern "C"

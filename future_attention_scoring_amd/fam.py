@@ -40,6 +40,7 @@ _SIGNATURES = {
                          _i, _f, _p, _p, _p, ctypes.c_size_t, _p]),
     "evict_plan": (_i, [_i, _i, _p, _i, _i, _p, _p]),
     "fam_budgets_from_ratios": (_i, [_i, _p, _i64, _p]),
+    "fam_soft_topk": (_i, [_p, _i, ctypes.c_double, ctypes.c_double, _p]),
     "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
     "evict_select_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
@@ -270,6 +271,14 @@ def fam_budgets_from_ratios(ratios: Sequence[float], t: int) -> np.ndarray:
     out = np.empty(r.size, dtype=np.int64)
     _check(load().fam_budgets_from_ratios(r.size, r.ctypes.data, int(t), out.ctypes.data))
     return out
+
+
+def fam_soft_topk(x: Sequence[float], k: float, tau: float = 1.0) -> np.ndarray:
+    """LKV's Soft-TopK masks of x (host, fp64): in (0, 1), summing to k."""
+    a = np.ascontiguousarray(np.asarray(x, dtype=np.float64).ravel())
+    out = np.empty_like(a)
+    _check(load().fam_soft_topk(a.ctypes.data, a.size, float(k), float(tau), out.ctypes.data))
+    return out.reshape(np.shape(x))
 
 
 def evict_select_workspace_size(H: int, S: int, sinks: int, recent: int) -> int:

@@ -273,6 +273,25 @@ fam_status evict_plan(int H, int S, const int64_t* budgets, int sinks, int recen
                       int64_t* kept, int64_t* offsets);
 
 /* ------------------------------------------------------------------------
+ * fam_soft_topk -- host-only, LKV's closed-form Soft-TopK (fp64).
+ *
+ * [LKV] "The Differentiable Soft-TopK Operator": ST_k(x; tau) has entries in
+ * (0, 1) that sum to k, keeps the order of x and ignores a constant shift;
+ * the page prints its threshold lambda in closed form. The mask is read as
+ * the Laplace CDF of x_i / tau - lambda (1 - e^-u / 2 for u >= 0, e^u / 2
+ * below), which makes the printed lambda exactly the root that sums to k.
+ * [LKV] "LKV-H: Learning Global Budget Allocation": a model's per-head
+ * retention ratios are ST of the flattened head scores with k = the mean
+ * ratio times the number of heads; fam_budgets_from_ratios then floors
+ * r * t.
+ *
+ *   x    host, [n] finite scores;  out  host out, [n] fp64 masks
+ *   k    0 < k < n;  tau > 0 (finite)
+ * Errors: FAM_ERR_INVALID_ARG.
+ * ---------------------------------------------------------------------- */
+fam_status fam_soft_topk(const double* x, int n, double k, double tau, double* out);
+
+/* ------------------------------------------------------------------------
  * fam_budgets_from_ratios -- host-only, b[h] = floor(ratios[h] * t).
  *
  * [LKV] "LKV-H: Learning Global Budget Allocation": a head's discrete budget
