@@ -507,7 +507,7 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
 
 size_t fam_rank_order_workspace_size(int H, int n) {
   if (H < 0 || n < 0) return 0;
-  return (size_t)2 * H * n * 8;
+  return fam::rank_workspace_bytes(H, n);
 }
 
 fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n, int32_t* order,
@@ -525,7 +525,8 @@ fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n,
                 workspace ? workspace_bytes : (size_t)0);
   if (reinterpret_cast<uintptr_t>(workspace) & 7u)
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
-  fam::RankArgs a{scores, row_stride, order, workspace, H, n};
+  if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
+  fam::RankArgs a{scores, row_stride, order, workspace, H, n, fam::rank_tiles(n)};
   return hip_status(fam::launch_rank(a, static_cast<hipStream_t>(stream)), "fam_rank_order launch");
 }
 

@@ -134,9 +134,14 @@ struct RankArgs {
   const float* scores;
   int64_t row_stride;
   int32_t* order;  // [H, n]
-  void* ws;        // 2 * H * n (key, position) pairs of 8 bytes
+  void* ws;        // rank_workspace_bytes(H, n): two (key, position) buffers, digit counts
   int H, n;
+  int ntiles;      // 4096-entry tiles per head
 };
+inline int rank_tiles(int n) { return (n + 4095) / 4096; }
+inline size_t rank_workspace_bytes(int H, int n) {
+  return (size_t)16 * H * n + (size_t)4 * H * 256 * rank_tiles(n);
+}
 hipError_t launch_rank(const RankArgs& a, hipStream_t s);
 
 struct CostArgs {

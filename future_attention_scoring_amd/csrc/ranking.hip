@@ -8,18 +8,18 @@
 // of the teacher's kept set that another scorer's kept set also holds under
 // the same budget).
 //
-// rank_kernel: order[h, r] is the position of the r-th best entry of head h
-// (score descending, ties to the lower position, -0 equal to +0, NaN last).
-// One workgroup per head runs a stable least-significant-digit radix sort on
-// the complemented order key, 8 bits per pass, between two buffers of (key,
+// rank_count / rank_place: order[h, r] is the position of the r-th best
+// entry of head h (score descending, ties to the lower position, -0 equal to
+// +0, NaN last). A stable least-significant-digit radix sort of the
+// complemented order key, 8 bits per pass, between two buffers of (key,
 // position) pairs in the workspace; the first pass reads the scores and the
-// last writes only positions. A pass counts its digits over the whole head
-// (LDS atomics), scans the 256 counts into bases, then walks the head in
-// tiles of 4096 entries in order. Inside a tile an entry's rank among the
-// entries with its digit comes from eight wave ballots (the lanes that share
-// its digit), the wave's running count of that digit, and a per-digit prefix
-// over the 16 waves, so the scatter keeps the order of equal digits and the
-// sort is stable.
+// last writes only positions. Each pass is three launches: rank_count writes
+// the digit counts of every (4096-entry tile, head), rank_scan turns them
+// into each tile's first slot per digit (one exclusive scan per head over
+// the digit-major counts), and rank_place ranks each entry among the tile's
+// entries with its digit (eight wave ballots, the wave's running count of
+// the digit, a per-digit prefix over the waves) and scatters it, keeping the
+// order of equal digits.
 //
 // cost_kernel: cost[h] = sum_r (r + 1) * importance[h, order[h, r]], which
 // equals the sum over budgets b = 0 .. n of the importance evicted at b
@@ -34,11 +34,11 @@
 namespace fam {
 namespace {
 
-constexpr int kRankThreads = 1024;
+constexpr int kRankThreads = 256;
 constexpr int kRankWaves = kRankThreads / 64;
 constexpr int kDigits = 256;
-constexpr int kRankSteps = 4;                           // 64-lane steps per wave and tile
-constexpr int kRankTile = kRankThreads * kRankSteps;
+constexpr int kRankSteps = 16;                          // 64-lane steps per wave and tile
+constexpr int kRankTile = kRankThreads * kRankSteps;    // 4096 entries
 
 // Lanes of the wave whose digit equals this lane's (among the lanes in `live`).
 __device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool live) {
@@ -52,122 +52,143 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool live) {
   return peers;
 }
 
-__global__ __launch_bounds__(kRankThreads) void rank_kernel(RankArgs p) {
-  __shared__ int base[kDigits];                // digit counts, then running offsets
-  __shared__ int next[kDigits];                // counts of the pass's digit
-  __shared__ int wcnt[kRankWaves][kDigits];    // per wave: count, then exclusive prefix
-  const int h = blockIdx.x;
-  const int n = p.n;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* srow = p.scores + h * p.row_stride;
-  u32x2_t* buf0 = static_cast<u32x2_t*>(p.ws) + (int64_t)h * n;
-  u32x2_t* buf1 = static_cast<u32x2_t*>(p.ws) + ((int64_t)p.H + h) * n;
-  int32_t* out = p.order + (int64_t)h * n;
-  const uint64_t below = (1ull << lane) - 1ull;
-
-  if (tid < kDigits) {
-#pragma unroll
-    for (int w = 0; w < kRankWaves; ++w) wcnt[w][tid] = 0;
+// Key and position of entry e at pass `pass` (pass 0 reads the scores).
+__device__ __forceinline__ void rank_entry(const RankArgs& p, int h, int pass, int e, uint32_t& key,
+                                           uint32_t& pos) {
+  if (pass == 0) {
+    key = ~order_key(p.scores[h * p.row_stride + e]);
+    pos = (uint32_t)e;
+  } else {
+    const u32x2_t* src = static_cast<const u32x2_t*>(p.ws) + ((int64_t)((pass & 1) ? 0 : p.H) + h) * p.n;
+    const u32x2_t kv = src[e];
+    key = kv.x;
+    pos = kv.y;
   }
-  for (int pass = 0; pass < 4; ++pass) {
-    const int shift = 8 * pass;
-    const u32x2_t* src = pass == 1 || pass == 3 ? buf0 : buf1;   // pass 0 reads the scores
-    u32x2_t* dst = pass == 0 || pass == 2 ? buf0 : buf1;         // pass 3 writes positions
-    if (tid < kDigits) next[tid] = 0;
-    __syncthreads();
-    for (int e = tid; e < n; e += kRankThreads) {
-      const uint32_t key = pass == 0 ? ~order_key(srow[e]) : src[e].x;
-      atomicAdd(&next[(key >> shift) & 255u], 1);
-    }
-    __syncthreads();
-    // exclusive scan of the 256 digit counts (wave 0, four digits per lane)
-    if (wave == 0) {
-      int c[4], sum = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        c[i] = next[4 * lane + i];
-        sum += c[i];
-      }
-      int incl = sum;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const int t = __shfl_up(incl, o);
-        if (lane >= o) incl += t;
-      }
-      int run = incl - sum;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        base[4 * lane + i] = run;
-        run += c[i];
-      }
-    }
-    __syncthreads();
+}
 
-    // Tiles of kRankTile entries; wave w takes the contiguous 256 entries
-    // t0 + 256 w .. in four 64-lane steps, so (wave, step, lane) order is
-    // entry order. A step ranks its lanes among the wave's earlier entries of
-    // the same digit (the wave's running count in LDS plus the lanes below
-    // with that digit); after the tile a per-digit prefix over the waves
-    // gives every entry its place.
-    for (int t0 = 0; t0 < n; t0 += kRankTile) {   // uniform across the workgroup
-      uint32_t key[kRankSteps], pos[kRankSteps], dg[kRankSteps];
-      int rank[kRankSteps];
-#pragma unroll
-      for (int st = 0; st < kRankSteps; ++st) {
-        const int e = t0 + wave * 64 * kRankSteps + st * 64 + lane;
-        key[st] = 0;
-        pos[st] = 0;
-        if (e < n) {
-          if (pass == 0) {
-            key[st] = ~order_key(srow[e]);
-            pos[st] = (uint32_t)e;
-          } else {
-            const u32x2_t kv = src[e];
-            key[st] = kv.x;
-            pos[st] = kv.y;
-          }
-        }
-      }
-#pragma unroll
-      for (int st = 0; st < kRankSteps; ++st) {
-        const int e = t0 + wave * 64 * kRankSteps + st * 64 + lane;
-        const bool valid = e < n;
-        const uint32_t d = (key[st] >> shift) & 255u;
-        const uint64_t peers = digit_peers(d, valid);
-        const uint64_t before = peers & below;
-        // all lanes of a digit read the wave's count before its first lane
-        // adds the step's lanes (LDS operations of a wave run in order)
-        const int seen = valid ? wcnt[wave][d] : 0;
-        rank[st] = valid ? seen + (int)__popcll(before) : -1;
-        dg[st] = d;
-        if (valid && before == 0ull) wcnt[wave][d] = seen + (int)__popcll(peers);
-      }
-      __syncthreads();
-      int total = 0;
-      if (tid < kDigits) {
-#pragma unroll
-        for (int w = 0; w < kRankWaves; ++w) {
-          const int c = wcnt[w][tid];
-          wcnt[w][tid] = total;
-          total += c;
-        }
-      }
-      __syncthreads();
-#pragma unroll
-      for (int st = 0; st < kRankSteps; ++st) {
-        if (rank[st] < 0) continue;
-        const int at = base[dg[st]] + wcnt[wave][dg[st]] + rank[st];
-        if (pass == 3) out[at] = (int32_t)pos[st];
-        else dst[at] = u32x2_t{key[st], pos[st]};
-      }
-      __syncthreads();
-      if (tid < kDigits) {
-        base[tid] += total;
-#pragma unroll
-        for (int w = 0; w < kRankWaves; ++w) wcnt[w][tid] = 0;
-      }
-      __syncthreads();
+__device__ __forceinline__ int* rank_hist(const RankArgs& p, int h) {
+  int* base = reinterpret_cast<int*>(static_cast<u32x2_t*>(p.ws) + (int64_t)2 * p.H * p.n);
+  return base + (int64_t)h * kDigits * p.ntiles;   // [H][256 digits][ntiles]
+}
+
+// Pass `pass`: digit counts of one tile of one head.
+__global__ __launch_bounds__(kRankThreads) void rank_count(RankArgs p, int pass) {
+  __shared__ int cnt[kDigits];
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int shift = 8 * pass;
+  if (threadIdx.x < kDigits) cnt[threadIdx.x] = 0;
+  __syncthreads();
+  const int e0 = tile * kRankTile;
+  for (int i = threadIdx.x; i < kRankTile; i += kRankThreads) {
+    const int e = e0 + i;
+    if (e < p.n) {
+      uint32_t key, pos;
+      rank_entry(p, h, pass, e, key, pos);
+      atomicAdd(&cnt[(key >> shift) & 255u], 1);
     }
+  }
+  __syncthreads();
+  if (threadIdx.x < kDigits) rank_hist(p, h)[(int64_t)threadIdx.x * p.ntiles + tile] = cnt[threadIdx.x];
+}
+
+// Pass `pass`: the counts of every (digit, tile) of a head, digit-major,
+// become exclusive offsets in place: the slots before a tile's entries of a
+// digit hold every smaller digit and that digit's entries of earlier tiles.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void rank_scan(RankArgs p) {
+  __shared__ int sh[kScanThreads / 64];
+  int* hist = rank_hist(p, blockIdx.x);
+  const int64_t n = (int64_t)kDigits * p.ntiles;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int carry = 0;   // entries of the chunks before
+  for (int64_t c0 = 0; c0 < n; c0 += kScanThreads * 16) {   // uniform across the workgroup
+    const int64_t i0 = c0 + (int64_t)threadIdx.x * 16;
+    int c[16], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      c[j] = i0 + j < n ? hist[i0 + j] : 0;
+      sum += c[j];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int t = __shfl_up(incl, o);
+      if (lane >= o) incl += t;
+    }
+    if (lane == 63) sh[wave] = incl;
+    __syncthreads();
+    int run = carry + incl - sum, all = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      run += w < wave ? sh[w] : 0;
+      all += sh[w];
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      if (i0 + j < n) hist[i0 + j] = run;
+      run += c[j];
+    }
+    carry += all;
+    __syncthreads();
+  }
+}
+
+// Pass `pass`: place one tile's entries after the slots rank_scan reserved;
+// inside the tile, (wave, step, lane) order is entry order, so equal digits
+// keep their order and the sort is stable.
+__global__ __launch_bounds__(kRankThreads) void rank_place(RankArgs p, int pass) {
+  __shared__ int base[kDigits];                // this tile's first slot per digit
+  __shared__ int wcnt[kRankWaves][kDigits];    // per wave: running count, then exclusive prefix
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int shift = 8 * pass;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t below = (1ull << lane) - 1ull;
+  base[tid] = rank_hist(p, h)[(int64_t)tid * p.ntiles + tile];
+#pragma unroll
+  for (int w = 0; w < kRankWaves; ++w) wcnt[w][tid] = 0;
+  __syncthreads();
+
+  uint32_t key[kRankSteps], pos[kRankSteps], dg[kRankSteps];
+  int rank[kRankSteps];
+  const int e0 = tile * kRankTile + wave * 64 * kRankSteps;
+#pragma unroll
+  for (int st = 0; st < kRankSteps; ++st) {
+    const int e = e0 + st * 64 + lane;
+    key[st] = 0;
+    pos[st] = 0;
+    if (e < p.n) rank_entry(p, h, pass, e, key[st], pos[st]);
+  }
+#pragma unroll
+  for (int st = 0; st < kRankSteps; ++st) {
+    const bool valid = e0 + st * 64 + lane < p.n;
+    const uint32_t d = (key[st] >> shift) & 255u;
+    const uint64_t peers = digit_peers(d, valid);
+    const uint64_t bef = peers & below;
+    // all lanes of a digit read the wave's count before its first lane adds
+    // the step's lanes (LDS operations of a wave run in order)
+    const int seen = valid ? wcnt[wave][d] : 0;
+    rank[st] = valid ? seen + (int)__popcll(bef) : -1;
+    dg[st] = d;
+    if (valid && bef == 0ull) wcnt[wave][d] = seen + (int)__popcll(peers);
+  }
+  __syncthreads();
+  if (tid < kDigits) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) {
+      const int c = wcnt[w][tid];
+      wcnt[w][tid] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  u32x2_t* dst = static_cast<u32x2_t*>(p.ws) + ((int64_t)((pass & 1) ? p.H : 0) + h) * p.n;
+  int32_t* out = p.order + (int64_t)h * p.n;
+#pragma unroll
+  for (int st = 0; st < kRankSteps; ++st) {
+    if (rank[st] < 0) continue;
+    const int at = base[dg[st]] + wcnt[wave][dg[st]] + rank[st];
+    if (pass == 3) out[at] = (int32_t)pos[st];
+    else dst[at] = u32x2_t{key[st], pos[st]};
   }
 }
 
@@ -241,7 +262,12 @@ __global__ __launch_bounds__(kOverlapThreads) void overlap_kernel(OverlapArgs p)
 
 hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
   if (a.H == 0 || a.n == 0) return hipSuccess;
-  hipLaunchKernelGGL(rank_kernel, dim3((unsigned)a.H), dim3(kRankThreads), 0, s, a);
+  const dim3 grid((unsigned)a.ntiles, (unsigned)a.H);
+  for (int pass = 0; pass < 4; ++pass) {
+    hipLaunchKernelGGL(rank_count, grid, dim3(kRankThreads), 0, s, a, pass);
+    hipLaunchKernelGGL(rank_scan, dim3((unsigned)a.H), dim3(kScanThreads), 0, s, a);
+    hipLaunchKernelGGL(rank_place, grid, dim3(kRankThreads), 0, s, a, pass);
+  }
   return hipGetLastError();
 }
 

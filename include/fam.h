@@ -441,10 +441,11 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
  *              when H > 1)
  *   order      device out, [H, n] int32, fully overwritten
  *   workspace  device scratch of fam_rank_order_workspace_size(H, n) bytes
- *              (16 * H * n), 8-byte aligned, owned by the caller; contents
+ *              (16 * H * n, plus 1 KiB per head and 4096 entries for digit
+ *              counts), 8-byte aligned, owned by the caller; contents
  *              irrelevant on entry and unspecified on return
- * One workgroup sorts one head (a stable radix sort, 4 passes), so a call
- * costs about 1 ms per 131072 entries whatever H is, up to the CU count.
+ * A stable radix sort, 4 passes of 3 launches over 4096-entry tiles.
+ * Requirements: H <= 65535.
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (n > 2^28),
  * FAM_ERR_WORKSPACE, FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */

@@ -248,7 +248,7 @@ def test_kv_append_and_inplace_validation():
 
 def test_ranking_validation():
     lib = fam.load()
-    assert lib.fam_rank_order_workspace_size(8, 131072) == 16 * 8 * 131072
+    assert lib.fam_rank_order_workspace_size(8, 131072) == 16 * 8 * 131072 + 4 * 8 * 256 * 32
     ws = lib.fam_rank_order_workspace_size(2, 100)
     assert lib.fam_rank_order(FAKE, 100, 2, 100, FAKE, FAKE, ws - 1, None) == WORKSPACE
     assert lib.fam_rank_order(FAKE, 99, 2, 100, FAKE, FAKE, ws, None) == INVALID       # stride < n
