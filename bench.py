@@ -172,7 +172,7 @@ def chunked_row(runs, q, k, v, wl, stream, chunk=4096, budget=16384):
     B, Hq, S, d = q.shape
     Hkv = k.shape[1]
     cap = max(budget, wl.sinks + wl.W) + chunk
-    ws_n = max([fam.fam_mass_workspace_size(B, Hq, Hkv, s) for s in range(chunk, cap + 1, chunk)] + [16])
+    ws_n = max([fam.fam_compute_workspace_size(B, Hq, Hkv, chunk, s) for s in range(chunk, cap + 1, chunk)] + [16])
     ws = torch.empty(ws_n, dtype=torch.uint8, device=q.device)
 
     def one(record):

@@ -97,6 +97,8 @@ fam::LseArgs lse_args(const void* q, const void* k, const ScoreShape& s, float s
   a.c = resolve_scale(scale, s.d);
   a.knorm = knorm;
   a.nkn = knorm ? fam_key_norm_parts(s.S) : 0;
+  a.part = nullptr;
+  a.nks = 1;
   return a;
 }
 
@@ -127,6 +129,24 @@ int mass_splits(int B, int Hkv, int S) {
   const int64_t wgs = (int64_t)((S + fam::kMassKeysPerWG - 1) / fam::kMassKeysPerWG) * B * Hkv;
   const int64_t n = (3072 + wgs - 1) / wgs;
   return (int)(n < 1 ? 1 : (n > 16 ? 16 : n));
+}
+
+// Key-range splits of the bounded first pass: aim at >= 3072 workgroups (as
+// for the mass pass), at most kLseMaxSplits, and at least 16 key tiles of 64
+// per split for the longest rows.
+int lse_splits(const ScoreShape& s) {
+  const int64_t npb = ((int64_t)s.rows() + 63) / 64;
+  const int64_t wgs = (npb * (s.Hq / s.Hkv) + 3) / 4 * s.B * s.Hkv;
+  int64_t n = (3072 + wgs - 1) / wgs;
+  const int64_t by_tiles = ((int64_t)s.S + 63) / 64 / 16;
+  if (n > by_tiles) n = by_tiles;
+  if (n > fam::kLseMaxSplits) n = fam::kLseMaxSplits;
+  return (int)(n < 1 ? 1 : n);
+}
+
+// Bytes of the first pass's split partial sums: nks + 1 floats per row.
+size_t lse_split_bytes(const ScoreShape& s, int nks) {
+  return nks > 1 ? (size_t)(nks + 1) * s.B * s.Hq * s.rows() * sizeof(float) : 0;
 }
 
 fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
@@ -162,7 +182,15 @@ fam_status compute_all(const void* q, const void* k, fam_dtype dtype, const Scor
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
   if (workspace && !aligned16(workspace))
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
-  const fam::LseArgs a = lse_args(q, k, s, scale, lse, mass);
+  fam::LseArgs a = lse_args(q, k, s, scale, lse, mass);
+  // the first pass's partial sums are consumed before the mass pass reuses
+  // the workspace (stream order)
+  int nks = workspace ? lse_splits(s) : 1;
+  while (nks > 1 && lse_split_bytes(s, nks) > workspace_bytes) --nks;
+  if (nks > 1) {
+    a.nks = nks;
+    a.part = static_cast<float*>(workspace);
+  }
   std::string what = std::string(who) + " key-norm launch";
   hipError_t e = fam::launch_knorm(a, elem_of(dtype), hs);
   if (e != hipSuccess) return hip_status(e, what.c_str());
@@ -232,6 +260,14 @@ size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S) {
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0) return 0;
   const int n = mass_splits(B, Hkv, S);
   return n > 1 ? (size_t)n * B * Hkv * S * sizeof(float) : 0;
+}
+
+size_t fam_compute_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Sq < 1 || Sq > Sk || Hq % Hkv != 0) return 0;
+  const ScoreShape s{B, Hq, Hkv, Sk, 64, 0, 0, 0, 0, 0, 0, Sq};
+  const size_t lse_bytes = lse_split_bytes(s, lse_splits(s));
+  const size_t mass_bytes = fam_mass_workspace_size(B, Hq, Hkv, Sk);
+  return lse_bytes > mass_bytes ? lse_bytes : mass_bytes;
 }
 
 fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype, int B, int Hq,

@@ -27,8 +27,17 @@ struct LseArgs {
   // the running-maximum form of the first pass.
   float* knorm;
   int nkn;
+  // Key-range split of the bounded form (nks > 1, knorm set): workgroup
+  // split s sums its share of the key tiles and writes the row's partial sum
+  // to part[s * R + row] (R = B * Hq * Sq rows); split 0 also writes the
+  // row's shift M to part[nks * R + row]. A second launch adds the partial
+  // sums and repeats the sweep with the running maximum where the bound
+  // turned out loose. part holds (nks + 1) * R floats.
+  float* part;
+  int nks;
 };
-constexpr int kNormParts = 64;  // partial key-norm maxima per (batch, KV head)
+constexpr int kNormParts = 64;   // partial key-norm maxima per (batch, KV head)
+constexpr int kLseMaxSplits = 8; // key-range splits of the bounded first pass
 hipError_t launch_knorm(const LseArgs& a, Elem e, hipStream_t s);
 hipError_t launch_lse(const LseArgs& a, Elem e, hipStream_t s);
 

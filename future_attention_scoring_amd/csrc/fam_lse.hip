@@ -34,6 +34,15 @@
 //     underflow could matter), the workgroup repeats its sweep with the
 //     running maximum. A sum of at least 2^-80 over at most 2^28 terms leaves
 //     the underflowed part below 2^-98 of it.
+//
+// Key-range split. A chunk's few thousand queries (or a short sequence) give
+// fewer workgroups than the chip holds at once. Since the bounded form's
+// shift does not depend on the keys seen, the partial sums of disjoint key
+// ranges simply add: the host may split every workgroup's key tiles over
+// nks workgroups, each writing its rows' partial sums (and split 0 the
+// shift) to a workspace. A second launch of the running-maximum kernel adds
+// them in split order and writes the normalisers; a workgroup with a loose
+// row repeats the whole sweep with the running maximum, exactly as above.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -117,8 +126,9 @@ __global__ __launch_bounds__(kThreads) void knorm_kernel(LseArgs p, int chunk) {
   if (tid == 0) p.knorm[(int64_t)bh * p.nkn + part] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-template <int D, typename T, bool BOUND>
+template <int D, typename T, bool BOUND, bool SPLIT>
 __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
+  static_assert(BOUND || !SPLIT, "only the bounded form splits the key range");
   constexpr int PITCH = D + 8;                 // LDS row pitch in elements
   constexpr int KS = D / 16;                   // MFMA k-steps per 32x32 block
   constexpr int CPR = D / 8;                   // 16-byte chunks per row
@@ -126,8 +136,10 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKeyTile * PITCH];
 
   const int nbh = p.B * p.Hkv;
+  const int nks = SPLIT ? p.nks : 1;   // key-range splits of this launch
   const int bh = blockIdx.x % nbh;
-  const int slot = blockIdx.x / nbh;
+  const int split = (blockIdx.x / nbh) % nks;
+  const int slot = (blockIdx.x / nbh) / nks;
   const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -147,6 +159,26 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
 
   const uint16_t* qbase = p.q + b * p.q_sb + qh * p.q_sh;
   const uint16_t* kbase = p.k + b * p.k_sb + h * p.k_sh;
+  const int64_t rows = (int64_t)p.B * p.Hq * p.Sq;
+  const int64_t row0 = ((int64_t)b * p.Hq + qh) * p.Sq + q0;   // this wave's first row
+
+  if constexpr (!BOUND) {
+    if (p.part) {
+      // second launch of a split bounded sweep: add the partial sums (split
+      // order), and sweep again with the running maximum only if some row
+      // of the workgroup came out loose
+      const int row = q0 + lane;
+      int loose = 0;
+      if (active && row < p.Sq) {
+        float L = 0.f;
+        for (int sp = 0; sp < p.nks; ++sp) L += p.part[sp * rows + row0 + lane];
+        const float M = p.part[p.nks * rows + row0 + lane];
+        if (L < kMinBoundSum) loose = 1;
+        else p.lse[row0 + lane] = (M + fast_log2(L)) * kLn2;
+      }
+      if (!__syncthreads_or(loose)) return;
+    }
+  }
 
   u32x4_t qf[2][KS];
 #pragma unroll
@@ -184,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
     for (int c = 0; c < CHUNKS; ++c) store16(&sk[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
   };
 
-  float* lse_row = p.lse + ((int64_t)b * p.Hq + qh) * p.Sq + q0;
+  float* lse_row = p.lse + row0;
   bool done = false;
 
   if constexpr (BOUND) {
@@ -201,13 +233,17 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
       qq += __shfl_xor(qq, 32);
       M[blk] = p.c * sqrtf(qq * kk);
     }
-    load_tile(0);
-    store_tile(0);
+    // this workgroup's share of the key tiles
+    const int t0 = (int)((int64_t)ntiles * split / nks), t1 = (int)((int64_t)ntiles * (split + 1) / nks);
+    if (t0 < t1) {
+      load_tile(t0);
+      store_tile(0);
+    }
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-      const bool more = t + 1 < ntiles;
+    for (int t = t0; t < t1; ++t) {
+      const bool more = t + 1 < t1;
       if (more) load_tile(t + 1);
-      const uint16_t* buf = sk[t & 1];
+      const uint16_t* buf = sk[(t - t0) & 1];
 #pragma unroll
       for (int kk2 = 0; kk2 < kKeyTile / 32; ++kk2) {
         const int kb = t * kKeyTile + 32 * kk2;
@@ -224,8 +260,20 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
           bound_update(acc1, kb, qp0 + 32, p.S, lane, p.c, M[1], l[1]);
         }
       }
-      if (more) store_tile((t + 1) & 1);
+      if (more) store_tile((t + 1 - t0) & 1);
       __syncthreads();
+    }
+    if constexpr (SPLIT) {   // partial sums and the shift; the second launch finishes
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const float Lp = l[blk] + __shfl_xor(l[blk], 32);
+        const int row = q0 + 32 * blk + col;
+        if (active && half == 0 && row < p.Sq) {
+          p.part[split * rows + row0 + 32 * blk + col] = Lp;
+          if (split == 0) p.part[nks * rows + row0 + 32 * blk + col] = M[blk];
+        }
+      }
+      return;
     }
     float L[2];
     int loose = 0;
@@ -294,10 +342,17 @@ hipError_t launch_lse_t(const LseArgs& a, hipStream_t s) {
   const int slots = (npb * a.g + kWaves - 1) / kWaves;
   const int64_t grid = (int64_t)slots * a.B * a.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.knorm)
-    hipLaunchKernelGGL((lse_kernel<D, T, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
-  else
-    hipLaunchKernelGGL((lse_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  if (a.knorm && a.nks > 1 && a.part) {
+    if (grid * a.nks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL((lse_kernel<D, T, true, true>), dim3((unsigned)(grid * a.nks)), dim3(kThreads), 0, s, a, npb);
+    hipLaunchKernelGGL((lse_kernel<D, T, false, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  } else if (a.knorm) {
+    hipLaunchKernelGGL((lse_kernel<D, T, true, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a, npb);
+  } else {
+    LseArgs b = a;
+    b.part = nullptr;
+    hipLaunchKernelGGL((lse_kernel<D, T, false, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, b, npb);
+  }
   return hipGetLastError();
 }
 

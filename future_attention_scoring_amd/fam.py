@@ -33,6 +33,7 @@ _SIGNATURES = {
     "fam_mass": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
                       _i, _f, _p, _p, ctypes.c_size_t, _p]),
     "fam_mass_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "fam_compute_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "fam_mass_per_head": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
                                _i64, _i, _f, _p, _p]),
     "fam_kvpop_target": (_i, [_p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
@@ -180,6 +181,22 @@ def _mass_workspace(workspace, B, Hq, Hkv, S, device):
     return ws.data_ptr(), n
 
 
+def fam_compute_workspace_size(B: int, Hq: int, Hkv: int, Sq: int, Sk: int) -> int:
+    return int(load().fam_compute_workspace_size(int(B), int(Hq), int(Hkv), int(Sq), int(Sk)))
+
+
+def _compute_workspace(workspace, B, Hq, Hkv, Sq, Sk, device):
+    """The caller's workspace, or one of the recommended size for both
+    passes of fam_compute / fam_compute_chunk (None if 0)."""
+    if workspace is not None:
+        return workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    n = fam_compute_workspace_size(B, Hq, Hkv, Sq, Sk)
+    if n == 0:
+        return None, 0
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    return ws.data_ptr(), n
+
+
 def fam_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
              scale: Optional[float] = None, mass: Optional[torch.Tensor] = None,
              workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
@@ -241,7 +258,7 @@ def fam_compute(q: torch.Tensor, k: torch.Tensor, W: int, scale: Optional[float]
         lse = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
     if mass is None:
         mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
-    ws, nbytes = _mass_workspace(workspace, B, Hq, Hkv, S, q4.device)
+    ws, nbytes = _compute_workspace(workspace, B, Hq, Hkv, S, S, q4.device)
     _check(load().fam_compute(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv, S, d,
                               *q4.stride()[:3], *k4.stride()[:3], int(W),
                               0.0 if scale is None else scale, lse.data_ptr(), mass.data_ptr(),
@@ -350,7 +367,7 @@ def fam_compute_chunk(q: torch.Tensor, k: torch.Tensor, W: int, scale: Optional[
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q4.device)
     if mass is None:
         mass = torch.empty((B, Hkv, Sk), dtype=torch.float32, device=q4.device)
-    ws, nbytes = _mass_workspace(workspace, B, Hq, Hkv, Sk, q4.device)
+    ws, nbytes = _compute_workspace(workspace, B, Hq, Hkv, Sq, Sk, q4.device)
     _check(load().fam_compute_chunk(q4.data_ptr(), k4.data_ptr(), _dtype_code(q4), B, Hq, Hkv,
                                     Sq, Sk, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
                                     0.0 if scale is None else scale, lse.data_ptr(),
@@ -495,8 +512,9 @@ def prefill_compress(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, chunk: i
     for p0 in range(0, S, chunk):
         p1 = min(S, p0 + chunk)
         cache.append(k[:, :, p0:p1], v[:, :, p0:p1])
-        if ws is None or ws.numel() < fam_mass_workspace_size(B, Hq, Hkv, cache.n):
-            n = fam_mass_workspace_size(B, Hq, Hkv, cache.capacity)
+        need = fam_compute_workspace_size(B, Hq, Hkv, p1 - p0, cache.n)
+        if ws is None or ws.numel() < need:
+            n = max(need, fam_compute_workspace_size(B, Hq, Hkv, p1 - p0, cache.capacity))
             ws = torch.empty(max(n, 16), dtype=torch.uint8, device=q.device)
         cache.score(q[:, :, p0:p1], workspace=ws)
         cache.compress()

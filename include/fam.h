@@ -198,7 +198,15 @@ fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, 
 
 /* fam_compute -- fam_key_norms, fam_lse (bounded form) and fam_mass on the
  * same stream. The key-norm partial maxima are kept in the first entries of
- * `mass` until the mass pass overwrites it; the workspace is fam_mass's. */
+ * `mass` until the mass pass overwrites it. The optional workspace (16-byte
+ * aligned, caller-owned, contents irrelevant on entry and unspecified on
+ * return) serves both passes in turn: when the query rows are too few to fill
+ * the chip, the first pass splits every row's key range over several
+ * workgroups, adds their partial sums in a fixed order and repeats the sweep
+ * with the running maximum for any workgroup whose bound came out loose; the
+ * mass pass then splits as in fam_mass. fam_compute_workspace_size gives the
+ * bytes for all splits; fewer bytes (or NULL) mean fewer (or no) splits, with
+ * the same results up to fp32 rounding. */
 fam_status fam_compute(const void* q, const void* k, fam_dtype dtype,
                        int B, int Hq, int Hkv, int S, int d,
                        int64_t q_sb, int64_t q_sh, int64_t q_ss,
@@ -239,7 +247,7 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype,
  *   lse   device out, [B, Hq, Sq] fp32, contiguous, fully overwritten
  *   mass  device out, [B, Hkv, Sk] fp32, contiguous, fully overwritten
  *         (rows j > Sk - 1 - W get exactly 0)
- *   workspace  as for fam_mass, sized fam_mass_workspace_size(B, Hq, Hkv, Sk)
+ *   workspace  as for fam_compute, sized fam_compute_workspace_size(B, Hq, Hkv, Sq, Sk)
  * Requirements: 1 <= Sq <= Sk; otherwise as for fam_compute.
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
@@ -249,6 +257,12 @@ fam_status fam_compute_chunk(const void* q, const void* k, fam_dtype dtype,
                              int64_t k_sb, int64_t k_sh, int64_t k_ss,
                              int W, float scale, float* lse, float* mass,
                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fam_compute (Sq == Sk == S) and fam_compute_chunk use
+ * for these sizes: the larger of the first pass's split partial sums
+ * ((splits + 1) floats per query row) and fam_mass_workspace_size(B, Hq,
+ * Hkv, Sk). 0 when neither pass splits, or for invalid sizes. */
+size_t fam_compute_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk);
 
 /* ------------------------------------------------------------------------
  * evict_plan -- host-only budget plan (no device work).

@@ -148,6 +148,23 @@ def test_mass_workspace_size():
     assert lib.fam_mass_workspace_size(0, 4, 2, 100) == 0
 
 
+def test_compute_workspace_size():
+    """The larger of the first pass's split partial sums ((splits + 1) floats
+    per query row) and the mass pass's split parts."""
+    lib = fam.load()
+    # a 4096-query chunk over 20480 rows, 32 query and 8 KV heads: 512
+    # workgroups unsplit, so 6 key-range splits (3072 workgroups); the mass
+    # pass's 5 splits of 8 x 20480 keys need less
+    assert lib.fam_compute_workspace_size(1, 32, 8, 4096, 20480) == 7 * 32 * 4096 * 4
+    assert lib.fam_mass_workspace_size(1, 32, 8, 20480) == 5 * 8 * 20480 * 4
+    # the full 128k square fills the chip with neither pass split
+    assert lib.fam_compute_workspace_size(1, 32, 8, 131072, 131072) == 0
+    # fewer than 32 key tiles: no key-range split, the mass pass's need remains
+    assert lib.fam_compute_workspace_size(1, 8, 2, 100, 1000) == lib.fam_mass_workspace_size(1, 8, 2, 1000)
+    for bad in ((1, 8, 2, 0, 100), (1, 8, 2, 101, 100), (1, 3, 2, 10, 10), (0, 4, 2, 10, 10)):
+        assert lib.fam_compute_workspace_size(*bad) == 0
+
+
 WORKSPACE = 3
 
 

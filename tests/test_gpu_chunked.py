@@ -80,6 +80,9 @@ CASES = [
     (6, 1, 4, 4, 130, 700, 64, 0, torch.bfloat16, True),
     (7, 1, 16, 2, 96, 1200, 128, 40, torch.float16, True),
     (8, 1, 4, 1, 500, 501, 128, 499, torch.bfloat16, False),
+    # enough key tiles for the first pass to split every row's key range
+    (9, 1, 8, 2, 512, 4096, 128, 64, torch.bfloat16, True),
+    (10, 1, 4, 1, 200, 2500, 64, 30, torch.float16, True),
 ]
 
 
@@ -115,6 +118,48 @@ def test_compute_chunk_full_square_equals_fam_compute(S, W):
     l2, m2 = fam.fam_compute_chunk(q, k, W)
     torch.cuda.synchronize()
     assert torch.equal(l1, l2) and torch.equal(m1, m2)
+
+
+@pytest.mark.parametrize("Sq,Sk,loose", [(512, 4096, False), (700, 3000, True), (4096, 20480, False)])
+def test_compute_chunk_split_matches_unsplit(Sq, Sk, loose):
+    """With a workspace of fam_compute_workspace_size bytes the first pass
+    splits every row's key range over several workgroups (and the mass pass
+    its queries); with an empty one neither pass splits. Both agree to fp32
+    rounding and meet the oracle. With `loose`, the query rows of the second
+    half are long and orthogonal to one very long key, so their Cauchy-Schwarz
+    bound is far too high: their workgroups repeat the sweep with the running
+    maximum while the others keep the added partial sums."""
+    say(f"fam_compute_chunk split vs unsplit Sq={Sq} Sk={Sk} loose={loose}")
+    Hq, Hkv, W, d = (32, 8, 512, 128) if Sk > 10000 else (8, 2, 40, 128)
+    g = torch.Generator().manual_seed(Sq + Sk)
+    q = torch.randn(1, Hq, Sq, d, generator=g)
+    k = torch.randn(1, Hkv, Sk, d, generator=g)
+    if loose:
+        q[0, :, Sq // 2:, 0], q[0, :, Sq // 2:, 1] = 40.0, 0.0
+        k[0, :, :, 0], k[0, :, :, 1] = 0.0, 0.0
+        k[0, :, 3, 1] = 40.0
+    q, k = q.to(torch.bfloat16), k.to(torch.bfloat16)
+    qd, kd = q.to(DEV), k.to(DEV)
+    assert fam.fam_compute_workspace_size(1, Hq, Hkv, Sq, Sk) > 0
+    l1, m1 = fam.fam_compute_chunk(qd, kd, W)
+    l0, m0 = fam.fam_compute_chunk(qd, kd, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    torch.cuda.synchronize()
+    assert (l1 - l0).abs().max().item() <= 1e-5
+    pos = m0 > 0
+    assert torch.equal(m1[~pos], m0[~pos])
+    assert ((m1 - m0).abs()[pos] / m0[pos]).max().item() <= 1e-5
+    P = np.tile(np.arange(Sk, dtype=np.int64), (Hkv, 1))
+    if Sk <= 5000:
+        lse_ref = ch.chunk_lse(to64(q[0]), to64(k[0]), P, Sk - Sq)
+        check_lse(to64(l1[0]), lse_ref)
+        check_mass(to64(m1[0]), ch.chunk_mass(to64(q[0]), to64(k[0]), P, lse_ref, Sk - Sq, W))
+    else:   # sampled rows of two query heads against the oracle
+        kk = to64(k[0])
+        for qh in (0, Hq - 1):
+            h = qh // (Hq // Hkv)
+            for r in (0, 1, 63, 64, 1000, 2047, 2048, 4000, Sq - 1):
+                ref = ch.chunk_lse(to64(q[0, qh:qh + 1, r:r + 1]), kk[h:h + 1], P[:1], Sk - Sq + r)
+                check_lse(to64(l1[0, qh, r:r + 1]), ref[0])
 
 
 def sorted_subset(rng, S, n, keep_prefix=0):
