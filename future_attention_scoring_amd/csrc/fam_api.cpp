@@ -510,7 +510,8 @@ fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H
 fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, int d, int64_t k_sh,
                               int64_t k_ss, int64_t v_sh, int64_t v_ss, const int32_t* idx,
                               const int64_t* offsets_dev, int64_t total_rows, int32_t* pos,
-                              int64_t pos_sh, void* stream) {
+                              int64_t pos_sh, void* workspace, size_t workspace_bytes,
+                              void* stream) {
   if (elem_bytes != 2) return fail(FAM_ERR_UNSUPPORTED, "elem_bytes %d (need 2)", elem_bytes);
   if (d != 64 && d != 128 && d != 256) return fail(FAM_ERR_UNSUPPORTED, "head dim %d (need 64, 128 or 256)", d);
   if (H < 0 || S < 1 || total_rows < 0)
@@ -526,6 +527,12 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
   if (!aligned16(k) || !aligned16(v)) return fail(FAM_ERR_INVALID_ARG, "k and v must be 16-byte aligned");
   if (pos && (pos_sh < S || (reinterpret_cast<uintptr_t>(pos) & 3u)))
     return fail(FAM_ERR_INVALID_ARG, "pos needs a head stride >= S and 4-byte alignment");
+  const size_t need = fam::inplace_workspace_bytes(total_rows);
+  if (!workspace || workspace_bytes < need)
+    return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
   fam::InplaceArgs a{};
   a.k = static_cast<uint16_t*>(k);
   a.v = static_cast<uint16_t*>(v);
@@ -536,10 +543,15 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
   a.pos_sh = pos_sh;
   a.total = total_rows;
   a.H = H, a.S = S, a.d = d;
+  a.ws = static_cast<uint32_t*>(workspace);
   return hip_status(fam::launch_compact_inplace(a, static_cast<hipStream_t>(stream)),
                     "kv_compact_inplace launch");
 }
 
+
+size_t kv_compact_inplace_workspace_size(int64_t total_rows) {
+  return total_rows < 0 ? 0 : fam::inplace_workspace_bytes(total_rows);
+}
 
 size_t fam_rank_order_workspace_size(int H, int n) {
   if (H < 0 || n < 0) return 0;

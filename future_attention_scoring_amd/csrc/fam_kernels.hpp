@@ -134,7 +134,13 @@ struct InplaceArgs {
   int64_t pos_sh;
   int64_t total; // offsets[H]: kept rows over all heads
   int H, S, d;   // S: rows per head region
+  uint32_t* ws;  // ticket counter, then one flag per chunk from word kInplaceFlags0
 };
+constexpr int kInplaceFlags0 = 32;          // words before the first chunk flag
+constexpr int kInplaceMinChunkRows = 128;   // rows per chunk at d = 256 (more for smaller d)
+inline size_t inplace_workspace_bytes(int64_t total) {
+  return 4 * (size_t)(kInplaceFlags0 + (total + kInplaceMinChunkRows - 1) / kInplaceMinChunkRows);
+}
 hipError_t launch_compact_inplace(const InplaceArgs& a, hipStream_t s);
 
 // Ranking measures: stable per-head order by score, the eviction cost of an

@@ -50,7 +50,8 @@ _SIGNATURES = {
     "kv_append": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _i64, _i64,
                        _i64, _i, _i, _p, _i64, _i, _p]),
     "kv_compact_inplace": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p,
-                                _i64, _p]),
+                                _i64, _p, ctypes.c_size_t, _p]),
+    "kv_compact_inplace_workspace_size": (ctypes.c_size_t, [_i64]),
     "fam_rank_order": (_i, [_p, _i64, _i, _i, _p, _p, ctypes.c_size_t, _p]),
     "fam_rank_order_workspace_size": (ctypes.c_size_t, [_i, _i]),
     "fam_eviction_cost": (_i, [_p, _i64, _p, _i, _i, _p, _p]),
@@ -406,12 +407,21 @@ def kv_append(k_src: torch.Tensor, v_src: torch.Tensor, k_cache: torch.Tensor,
                             int(pos0), _stream(k_cache)))
 
 
+def kv_compact_inplace_workspace_size(total_rows: int) -> int:
+    return int(load().kv_compact_inplace_workspace_size(int(total_rows)))
+
+
 def kv_compact_inplace(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
                        offsets: torch.Tensor, pos: Optional[torch.Tensor] = None,
-                       total_rows: Optional[int] = None) -> None:
+                       total_rows: Optional[int] = None,
+                       workspace: Optional[torch.Tensor] = None) -> None:
     """Move each head's rows idx[offsets[h]:offsets[h+1]] to its first rows
     (total_rows = offsets[H], idx.numel() by default)."""
     H, S, d = _cache_args(k_cache, v_cache, "kv_compact_inplace")
+    total = int(idx.numel()) if total_rows is None else int(total_rows)
+    if workspace is None:
+        workspace = torch.empty(max(kv_compact_inplace_workspace_size(total), 4), dtype=torch.uint8,
+                                device=k_cache.device)
     if idx.dtype != torch.int32 or offsets.dtype != torch.int64 or offsets.numel() != H + 1:
         raise FamError(1, "idx must be int32 and offsets int64 [H + 1]")
     pp, psh = 0, 0
@@ -423,8 +433,9 @@ def kv_compact_inplace(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.
     _check(load().kv_compact_inplace(k_cache.data_ptr(), v_cache.data_ptr(), 2, H, S, d,
                                      k_cache.stride(0), k_cache.stride(1), v_cache.stride(0),
                                      v_cache.stride(1), idx.data_ptr(), offsets.data_ptr(),
-                                     int(idx.numel()) if total_rows is None else int(total_rows),
-                                     pp, psh, _stream(k_cache)))
+                                     total, pp, psh, workspace.data_ptr(),
+                                     workspace.numel() * workspace.element_size(),
+                                     _stream(k_cache)))
 
 
 class ChunkedCache:
@@ -455,6 +466,8 @@ class ChunkedCache:
         self.k = torch.empty((H, self.capacity, d), dtype=dtype, device=device)
         self.v = torch.empty_like(self.k)
         self.pos = torch.full((H, self.capacity), -1, dtype=torch.int32, device=device)
+        self.compact_ws = torch.empty(kv_compact_inplace_workspace_size(H * self.capacity),
+                                      dtype=torch.uint8, device=device)
         self.n = 0          # rows held per head
         self.next_pos = 0   # position of the next appended row
         self.lse = None
@@ -490,7 +503,7 @@ class ChunkedCache:
 
     def compact(self, idx: torch.Tensor, offsets: torch.Tensor) -> None:
         """Move the kept rows to the front of every head's region, in place."""
-        kv_compact_inplace(self.k, self.v, idx, offsets, self.pos)
+        kv_compact_inplace(self.k, self.v, idx, offsets, self.pos, workspace=self.compact_ws)
         self.n = int(idx.numel()) // (self.B * self.Hkv)
 
     def compress(self) -> Tuple[Optional[torch.Tensor], Optional[torch.Tensor]]:

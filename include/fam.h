@@ -417,11 +417,13 @@ fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H
  *     row r of head h  <-  row idx[offsets_dev[h] + r] of head h (K, V, pos)
  *
  * Rows n_h and beyond keep stale contents. The rows of a head must be
- * ascending (as evict_select writes them); then idx[...+r] >= r and a sweep
- * in increasing r never reads a row it has already overwritten. Unsorted
- * indices give unspecified row contents (never an access out of bounds);
- * an index outside [0, S) yields a zero row and position -1; rows r >= S
- * (offsets that do not fit the region) are skipped.
+ * ascending (as evict_select writes them); then idx[...+r] >= r, and the
+ * kept rows are moved in chunks, each written only after the chunks that
+ * read its rows have loaded them (no grid-wide barrier, no cooperative
+ * launch). Unsorted indices give unspecified row contents (never an access
+ * out of bounds, never a wait that does not end); an index outside [0, S)
+ * yields a zero row and position -1; rows r >= S (offsets that do not fit
+ * the region) are skipped.
  *
  *   k, v         device in/out, [H, S, d], strides (k_sh, k_ss), (v_sh, v_ss)
  *   idx          device, [total_rows] int32 (evict_select's output)
@@ -430,16 +432,25 @@ fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H
  *   total_rows   host copy of offsets_dev[H], <= H * S
  *   pos          optional device in/out int32 [H, S] with head stride pos_sh,
  *                moved with the rows
+ *   workspace    device scratch of kv_compact_inplace_workspace_size(total_rows)
+ *                bytes (4-byte aligned, caller-owned, contents irrelevant on
+ *                entry and unspecified on return): the chunk tickets and
+ *                flags, cleared by the call itself. Calls sharing a
+ *                workspace must be ordered on one stream.
  * Requirements: elem_bytes == 2; d in {64, 128, 256}; k, v 16-byte aligned;
- * strides multiples of 8 elements; pos 4-byte aligned with pos_sh >= S; a
- * device that supports cooperative launches (the grid meets at a grid-wide
- * barrier between the reads and the writes of each pass).
- * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ * strides multiples of 8 elements; pos 4-byte aligned with pos_sh >= S.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
+ * FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
 fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, int d,
                               int64_t k_sh, int64_t k_ss, int64_t v_sh, int64_t v_ss,
                               const int32_t* idx, const int64_t* offsets_dev,
-                              int64_t total_rows, int32_t* pos, int64_t pos_sh, void* stream);
+                              int64_t total_rows, int32_t* pos, int64_t pos_sh,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace kv_compact_inplace needs for total_rows kept rows (about
+ * one byte per 32 rows; 0 for total_rows < 0). */
+size_t kv_compact_inplace_workspace_size(int64_t total_rows);
 
 /* ------------------------------------------------------------------------
  * fam_rank_order -- each head's entries ordered best first.

@@ -246,7 +246,14 @@ def test_kv_append_and_inplace_validation():
     assert lib.kv_append(*bad) == INVALID                          # misaligned cache
     bad = list(args); bad[4] = 0
     assert lib.kv_append(*bad) == 0                                # nothing to copy
-    ip = [FAKE, FAKE, 2, 2, 100, 128, 100 * 128, 128, 100 * 128, 128, FAKE, FAKE, 150, None, 0, None]
+    ip = [FAKE, FAKE, 2, 2, 100, 128, 100 * 128, 128, 100 * 128, 128, FAKE, FAKE, 150, None, 0,
+          FAKE, lib.kv_compact_inplace_workspace_size(150), None]
+    bad = list(ip); bad[15] = None
+    assert lib.kv_compact_inplace(*bad) == WORKSPACE
+    bad = list(ip); bad[16] -= 1
+    assert lib.kv_compact_inplace(*bad) == WORKSPACE
+    bad = list(ip); bad[15] = FAKE + 2
+    assert lib.kv_compact_inplace(*bad) == INVALID                 # misaligned workspace
     bad = list(ip); bad[10] = None
     assert lib.kv_compact_inplace(*bad) == INVALID
     bad = list(ip); bad[5] = 72
@@ -261,6 +268,20 @@ def test_kv_append_and_inplace_validation():
     assert lib.kv_compact_inplace(*bad) == 0                       # no heads
     bad = list(ip); bad[12] = 0
     assert lib.kv_compact_inplace(*bad) == 0                       # nothing kept
+    bad[15] = None
+    assert lib.kv_compact_inplace(*bad) == 0                       # no workspace needed for nothing
+
+
+def test_inplace_workspace_size():
+    """A ticket counter and padding (32 words), then one flag word per chunk
+    of at least 128 rows."""
+    lib = fam.load()
+    assert lib.kv_compact_inplace_workspace_size(0) == 128
+    assert lib.kv_compact_inplace_workspace_size(1) == 132
+    assert lib.kv_compact_inplace_workspace_size(128) == 132
+    assert lib.kv_compact_inplace_workspace_size(129) == 136
+    assert lib.kv_compact_inplace_workspace_size(8 * 20480) == 128 + 4 * 1280
+    assert lib.kv_compact_inplace_workspace_size(-1) == 0
 
 
 def test_ranking_validation():

@@ -230,6 +230,71 @@ def test_compact_inplace_matches_out_of_place_compact():
         assert torch.equal(v[h, :m], v_new[off[h]:off[h + 1]])
 
 
+def inplace_bitwise(H, S, d, keeps, seed, workspace=None):
+    """kv_compact_inplace of keeps[h] (ascending rows of head h) against a
+    numpy gather of the original cache, K, V and positions bit for bit."""
+    g = torch.Generator().manual_seed(seed)
+    k = torch.randn(H, S, d, generator=g).to(torch.bfloat16)
+    v = torch.randn(H, S, d, generator=g).to(torch.bfloat16)
+    pos = torch.randint(0, 1 << 30, (H, S), generator=g, dtype=torch.int32)
+    kd, vd, pd = k.to(DEV), v.to(DEV), pos.to(DEV)
+    idx = torch.from_numpy(np.concatenate(keeps).astype(np.int32)).to(DEV)
+    offsets = torch.tensor(np.concatenate([[0], np.cumsum([x.size for x in keeps])]), dtype=torch.int64,
+                           device=DEV)
+    fam.kv_compact_inplace(kd, vd, idx, offsets, pd, workspace=workspace)
+    torch.cuda.synchronize()
+    k2, v2, p2 = kd.cpu(), vd.cpu(), pd.cpu()
+    for h, keep in enumerate(keeps):
+        rows = torch.from_numpy(keep.astype(np.int64))
+        m = keep.size
+        assert torch.equal(k2[h, :m].view(torch.int16), k[h, rows].view(torch.int16)), f"head {h}"
+        assert torch.equal(v2[h, :m].view(torch.int16), v[h, rows].view(torch.int16)), f"head {h}"
+        assert torch.equal(p2[h, :m], pos[h, rows]), f"head {h}"
+        # only rows below m are written
+        assert torch.equal(k2[h, m:].view(torch.int16), k[h, m:].view(torch.int16)), f"head {h}"
+        assert torch.equal(p2[h, m:], pos[h, m:]), f"head {h}"
+
+
+def test_compact_inplace_chunked_loop_shape_twice():
+    """The 128k loop's compression (8 heads of 20480 rows keeping 16384, sinks
+    and window forced): every chunk of 256 rows waits for up to 17 earlier
+    ones. Two calls on one workspace, the second with fewer rows, check that
+    each call clears its tickets and flags."""
+    say("kv_compact_inplace 8 x 20480 -> 16384, twice on one workspace")
+    H, S, keep = 8, 20480, 16384
+    rng = np.random.default_rng(11)
+    ws = torch.empty(fam.kv_compact_inplace_workspace_size(H * keep), dtype=torch.uint8, device=DEV)
+    keeps = [np.concatenate([np.arange(4), np.sort(rng.choice(np.arange(4, S - 512), keep - 516, replace=False)),
+                             np.arange(S - 512, S)]) for _ in range(H)]
+    inplace_bitwise(H, S, 128, keeps, seed=1, workspace=ws)
+    keeps = [sorted_subset(rng, S, int(rng.integers(0, 9000))) for _ in range(H)]
+    inplace_bitwise(H, S, 128, keeps, seed=2, workspace=ws)
+
+
+def test_compact_inplace_long_shift():
+    """A head whose kept rows all lie 20000 rows further on: each chunk waits
+    for about 80 earlier chunks (more than one batch of 64 flag polls)."""
+    say("kv_compact_inplace shift of 20000 rows")
+    H, S = 2, 40960
+    rng = np.random.default_rng(12)
+    keeps = [np.concatenate([np.arange(4), np.arange(20004, S)]), sorted_subset(rng, S, 30000)]
+    inplace_bitwise(H, S, 128, keeps, seed=3)
+
+
+@pytest.mark.parametrize("H,S,d", [(600, 300, 64), (40, 700, 256)])
+def test_compact_inplace_many_small_heads(H, S, d):
+    """Chunks that span many heads (offsets beyond the 512 kept in LDS for
+    H = 600), empty heads, whole heads kept and heads keeping one row."""
+    say(f"kv_compact_inplace H={H} S={S} d={d}")
+    rng = np.random.default_rng(H)
+    keeps = []
+    for h in range(H):
+        kind = h % 4
+        n = {0: 0, 1: S, 2: 1, 3: int(rng.integers(1, S))}[kind]
+        keeps.append(np.arange(S) if n == S else sorted_subset(rng, S, n))
+    inplace_bitwise(H, S, d, keeps, seed=4)
+
+
 def run_loop_checked(q, k, v, chunk, budget, sinks, W):
     """Drive ChunkedCache chunk by chunk, checking every step."""
     B, Hq, S, d = q.shape
