@@ -186,21 +186,23 @@ struct CutoffArgs {
   int32_t* tau;          // [H, S] out
   void* ws;              // wavelet matrix (cutoff_workspace_bytes after rank)
   int H, S, w, k;
-  int L, nw, ntiles;     // levels, words per level (with a terminal word), 4096-position tiles
+  int L, nw, ntiles;     // levels, words per level (with a terminal word), 1024-position tiles
 };
-constexpr int kCutoffMaxS = 1 << 18;  // at most 64 tiles of 4096 positions
+constexpr int kCutoffMaxS = 1 << 18;  // at most 256 tiles of 1024 positions
+constexpr int kCutoffTile = 1024;
 // Levels (bits of a rank - 1), words per level and tiles for S positions, and
-// the workspace bytes after the ranks.
+// the workspace bytes after the ranks: per-tile counts of ones [L][H][ntiles],
+// two level sequences [H][S], and bit words and word counts [H][L][nw].
 inline void cutoff_shape(int S, int& L, int& nw, int& ntiles) {
   L = 1;
   while ((1 << L) < S) ++L;
-  ntiles = (S + 4095) / 4096;
-  nw = ntiles * 128 + 1;
+  ntiles = (S + kCutoffTile - 1) / kCutoffTile;
+  nw = ntiles * (kCutoffTile / 32) + 1;
 }
 inline size_t cutoff_workspace_bytes(int H, int S) {
   int L, nw, ntiles;
   cutoff_shape(S, L, nw, ntiles);
-  return 4 * ((size_t)2 * H * S + (size_t)2 * H * L * nw + (size_t)H * ntiles);
+  return 4 * ((size_t)L * H * ntiles + (size_t)2 * H * S + (size_t)2 * H * L * nw);
 }
 hipError_t launch_cutoff(const CutoffArgs& a, hipStream_t s);
 

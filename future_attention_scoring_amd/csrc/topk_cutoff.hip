@@ -20,11 +20,19 @@
 //   * a query walks the L levels with its prefix [lo, hi): if the zeros in
 //     the range number at least k it follows them, otherwise it counts them
 //     off, sets the bit and follows the ones. Two counts per level.
-// Build: ranks_kernel inverts fam_rank_order's order into a rank per
-// position; per level, wt_bits writes the bit words and each 4096-position
-// tile's count of ones, and wt_scatter adds the tile prefix to the word
-// counts and moves every value to its place in the next level. Then
-// wt_query answers all queries of all heads at once.
+// Build: a fill kernel clears the per-tile counts of ones; wt_ranks
+// inverts fam_rank_order's order into a rank per position and counts, per
+// 1024-position tile, the ones of the first level (LDS histogram, one
+// atomic per touched tile). Then one launch per level (wt_level), one
+// workgroup per tile: the tile's ones come first from the counts of the
+// earlier tiles, so the kernel writes the bit words and the word counts and
+// moves every value to its place in the next level at once; the zeros of the
+// next level come first, and their number is known in advance, because the
+// values are the ranks - 1, a permutation of 0 .. S-1. While moving, it
+// counts the next level's ones per destination tile: a tile's zeros land in
+// at most two consecutive tiles and its ones in at most two, so four
+// counters in LDS and four atomics per workgroup. Then wt_query answers all
+// queries of all heads at once.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -32,134 +40,171 @@ namespace fam {
 namespace {
 
 constexpr int kWtThreads = 256;
-constexpr int kWtPer = 16;                         // positions per thread and tile
-constexpr int kWtTile = kWtThreads * kWtPer;       // 4096 positions
-constexpr int kWtTileWords = kWtTile / 32;         // 128 words
-
-__global__ __launch_bounds__(256) void ranks_kernel(const int32_t* order, int32_t* rank, int H, int S) {
-  const int64_t n = (int64_t)H * S;
-  const int64_t stride = (int64_t)gridDim.x * 256;
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += stride) {
-    const int64_t h = i / S;
-    const int r = (int)(i - h * S);
-    const int pos = order[i];
-    if (pos >= 0 && pos < S) rank[h * S + pos] = r + 1;
-  }
-}
+constexpr int kWtPer = kCutoffTile / kWtThreads;   // positions per thread and tile
+constexpr int kWtTileWords = kCutoffTile / 32;     // 32 words
+constexpr int kWtRanksPer = 16;                    // order entries per thread in wt_ranks
+constexpr int kWtMaxTiles = kCutoffMaxS / kCutoffTile;
 
 struct WtLayout {
+  uint32_t* tile1;   // [L][H][ntiles] ones per tile of each level
   int32_t* seq[2];   // [H][S] value sequences of the levels (ping-pong)
   uint32_t* words;   // [H][L][nw] bit words
   uint32_t* cnt;     // [H][L][nw] ones before each word
-  int32_t* tile1;    // [H][ntiles] ones per tile of the current level
 };
 
 __device__ __forceinline__ WtLayout wt_layout(const CutoffArgs& p) {
   WtLayout w;
-  char* b = reinterpret_cast<char*>(p.ws);
   const size_t hs = (size_t)p.H * p.S;
-  w.seq[0] = reinterpret_cast<int32_t*>(b);
+  w.tile1 = reinterpret_cast<uint32_t*>(p.ws);
+  w.seq[0] = reinterpret_cast<int32_t*>(w.tile1 + (size_t)p.L * p.H * p.ntiles);
   w.seq[1] = w.seq[0] + hs;
   w.words = reinterpret_cast<uint32_t*>(w.seq[1] + hs);
   w.cnt = w.words + (size_t)p.H * p.L * p.nw;
-  w.tile1 = reinterpret_cast<int32_t*>(w.cnt + (size_t)p.H * p.L * p.nw);
   return w;
 }
 
-// value of position i at level l (0 .. S-1; level 0 reads the ranks)
+__global__ __launch_bounds__(256) void wt_fill_kernel(uint32_t* w, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) w[i] = 0u;
+}
+
+// Ranks of a block of 4096 order entries of head blockIdx.y, and the first
+// level's ones (bit L-1 of rank - 1) per tile of the positions they land on.
+__global__ __launch_bounds__(256) void wt_ranks(CutoffArgs p) {
+  __shared__ uint32_t hist[kWtMaxTiles];
+  const WtLayout w = wt_layout(p);
+  const int h = blockIdx.y, tid = threadIdx.x;
+  for (int b = tid; b < p.ntiles; b += 256) hist[b] = 0u;
+  __syncthreads();
+#pragma unroll 4
+  for (int j = 0; j < kWtRanksPer; ++j) {
+    const int r = (blockIdx.x * kWtRanksPer + j) * 256 + tid;
+    if (r < p.S) {
+      const int pos = p.order[(int64_t)h * p.S + r];
+      if (pos >= 0 && pos < p.S) {
+        p.rank[(int64_t)h * p.S + pos] = r + 1;
+        if ((r >> (p.L - 1)) & 1) atomicAdd(&hist[pos / kCutoffTile], 1u);
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t* t1 = w.tile1 + (size_t)h * p.ntiles;   // level 0
+  for (int b = tid; b < p.ntiles; b += 256)
+    if (hist[b]) __hip_atomic_fetch_add(t1 + b, hist[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// value of position i at level l (0 .. S-1 for a permutation; level 0 reads the ranks)
 __device__ __forceinline__ int wt_value(const CutoffArgs& p, const WtLayout& w, int h, int l, int i) {
   return l == 0 ? p.rank[(int64_t)h * p.S + i] - 1 : w.seq[l & 1][(int64_t)h * p.S + i];
 }
 
-// Level l: bit words of the tile and its count of ones.
-__global__ __launch_bounds__(kWtThreads) void wt_bits(CutoffArgs p, int l) {
-  __shared__ int red[kWtThreads / 64];
-  const int tile = blockIdx.x, h = blockIdx.y;
-  const WtLayout w = wt_layout(p);
-  const int shift = p.L - 1 - l;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t* words = w.words + ((size_t)h * p.L + l) * p.nw;
-  int ones = 0;
-#pragma unroll 4
-  for (int j = 0; j < kWtPer; ++j) {
-    // wave `wave` covers positions tile*4096 + wave*1024 + j*64 + lane
-    const int i = tile * kWtTile + wave * (kWtTile / 4) + j * 64 + lane;
-    const bool bit = i < p.S && ((wt_value(p, w, h, l, i) >> shift) & 1);
-    const uint64_t m = __ballot(bit);
-    // lanes 0 and 32 store the wave's two words (positions past S are 0)
-    if ((lane & 31) == 0) words[i >> 5] = (uint32_t)(lane == 0 ? m : (m >> 32));
-    ones += lane == 0 ? __popcll(m) : 0;
-  }
-  if (lane == 0) red[wave] = ones;
-  __syncthreads();
-  if (threadIdx.x == 0) w.tile1[(size_t)h * p.ntiles + tile] = red[0] + red[1] + red[2] + red[3];
+// How many of 0 .. S-1 have bit b set.
+__device__ __forceinline__ int ones_below(int S, int b) {
+  const int period = 2 << b, half = 1 << b;
+  const int rest = S % period;
+  return (S / period) * half + (rest > half ? rest - half : 0);
 }
 
-// Level l: word counts (tile prefix added) and the stable partition by the
-// level's bit into the next level's sequence.
-__global__ __launch_bounds__(kWtThreads) void wt_scatter(CutoffArgs p, int l) {
+// One level for one tile of one head: bit words, word counts, and the stable
+// partition by the level's bit into the next level's sequence, counting the
+// next level's ones per destination tile.
+__global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
   __shared__ uint32_t wl[kWtTileWords];
   __shared__ uint32_t cl[kWtTileWords];
-  __shared__ int sh[2];
-  const int tile = blockIdx.x, h = blockIdx.y;
+  __shared__ uint32_t nxt[4];      // next level's ones: zeros' two tiles, then ones' two tiles
+  __shared__ int sh_before, sh_total;
   const WtLayout w = wt_layout(p);
+  const int tile = blockIdx.x, h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int shift = p.L - 1 - l;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const uint32_t* words = w.words + ((size_t)h * p.L + l) * p.nw;
+  uint32_t* words = w.words + ((size_t)h * p.L + l) * p.nw;
   uint32_t* cnt = w.cnt + ((size_t)h * p.L + l) * p.nw;
-  const int32_t* t1 = w.tile1 + (size_t)h * p.ntiles;
-  // ones before this tile and in total (at most 64 tiles)
+  const uint32_t* t1 = w.tile1 + ((size_t)l * p.H + h) * p.ntiles;
+
+  // ones of the head before this tile and in all (wave 0), with the values
+  // of the tile in flight
   if (wave == 0) {
-    const int a = lane < p.ntiles ? t1[lane] : 0;
-    int before = lane < tile ? a : 0, all = a;
+    int before = 0, total = 0;
+    for (int b = lane; b < p.ntiles; b += 64) {
+      const int c = (int)t1[b];
+      total += c;
+      before += b < tile ? c : 0;
+    }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
       before += __shfl_xor(before, o);
-      all += __shfl_xor(all, o);
+      total += __shfl_xor(total, o);
     }
     if (lane == 0) {
-      sh[0] = before;
-      sh[1] = all;
+      sh_before = before;
+      sh_total = total;
     }
+    if (lane < 4) nxt[lane] = 0u;
   }
-  // the tile's words and their exclusive prefix counts (wave 0: 2 per lane)
-  const int w0 = tile * kWtTileWords;
-  if (wave == 0) {
-    const uint32_t a = words[w0 + 2 * lane];
-    const uint32_t b = words[w0 + 2 * lane + 1];
-    const int pa = __popc(a), pb = __popc(b);
-    int incl = pa + pb;
+  // wave `wave` covers positions tile*1024 + wave*256 + j*64 + lane
+  int v[kWtPer];
+  bool bit[kWtPer];
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
+  for (int j = 0; j < kWtPer; ++j) {
+    const int i = tile * kCutoffTile + wave * (kCutoffTile / 4) + j * 64 + lane;
+    v[j] = i < p.S ? wt_value(p, w, h, l, i) : 0;
+    bit[j] = i < p.S && ((v[j] >> shift) & 1);
+    const uint64_t m = __ballot(bit[j]);
+    if (lane == 0) {
+      wl[wave * 8 + j * 2] = (uint32_t)m;
+      wl[wave * 8 + j * 2 + 1] = (uint32_t)(m >> 32);
     }
-    const int ex = incl - pa - pb;
-    wl[2 * lane] = a;
-    wl[2 * lane + 1] = b;
-    cl[2 * lane] = (uint32_t)ex;
-    cl[2 * lane + 1] = (uint32_t)(ex + pa);
   }
   __syncthreads();
-  const int before = sh[0];
-  const int zeros = p.S - sh[1];
-  for (int j = threadIdx.x; j < kWtTileWords; j += kWtThreads) cnt[w0 + j] = (uint32_t)before + cl[j];
-  if (tile == p.ntiles - 1 && threadIdx.x == 0) {   // terminal entry: rank1(S) and the level's ones
-    uint32_t* wr = w.words + ((size_t)h * p.L + l) * p.nw;
-    wr[p.nw - 1] = 0u;
-    cnt[p.nw - 1] = (uint32_t)sh[1];
+  const int before = sh_before;
+  // word counts of the tile: exclusive scan of the 32 words' ones
+  if (wave == 0 && lane < kWtTileWords) {
+    const uint32_t word = wl[lane];
+    const int pc = __popc(word);
+    int incl = pc;
+#pragma unroll
+    for (int o = 1; o < kWtTileWords; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    cl[lane] = (uint32_t)(incl - pc);
+    cnt[tile * kWtTileWords + lane] = (uint32_t)(before + incl - pc);
+    words[tile * kWtTileWords + lane] = word;
+    if (tile == p.ntiles - 1 && lane == 0) {   // terminal entry: rank1(S) and the level's ones
+      words[p.nw - 1] = 0u;
+      cnt[p.nw - 1] = (uint32_t)sh_total;
+    }
   }
   if (l + 1 == p.L) return;   // the last level needs no next sequence
+  __syncthreads();
+  const int zeros = p.S - ones_below(p.S, shift);
+  const int nshift = shift - 1;   // the next level's bit
+  const int tz = (tile * kCutoffTile - before) / kCutoffTile;   // first tile of the zeros' run
+  const int to = (zeros + before) / kCutoffTile;                 // first tile of the ones' run
   int32_t* next = w.seq[(l + 1) & 1] + (int64_t)h * p.S;
-#pragma unroll 4
+#pragma unroll
   for (int j = 0; j < kWtPer; ++j) {
-    const int i = tile * kWtTile + wave * (kWtTile / 4) + j * 64 + lane;
+    const int i = tile * kCutoffTile + wave * (kCutoffTile / 4) + j * 64 + lane;
+    int slot = -1;
     if (i < p.S) {
-      const int v = wt_value(p, w, h, l, i);
-      const int lw = (i >> 5) - w0;
-      const int ones = before + (int)cl[lw] + __popc(wl[lw] & ((1u << (i & 31)) - 1u));
-      next[((v >> shift) & 1) ? zeros + ones : i - ones] = v;
+      const int lw = wave * 8 + j * 2 + (lane >> 5);
+      const int ob = before + (int)cl[lw] + __popc(wl[lw] & ((1u << (i & 31)) - 1u));
+      int dst = bit[j] ? zeros + ob : i - ob;
+      dst = dst < 0 ? 0 : (dst >= p.S ? p.S - 1 : dst);   // only a non-permutation can leave [0, S)
+      next[dst] = v[j];
+      const int rel = dst / kCutoffTile - (bit[j] ? to : tz);
+      if (((v[j] >> nshift) & 1) && rel >= 0 && rel < 2) slot = (bit[j] ? 2 : 0) + rel;
     }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const int c = __popcll(__ballot(slot == s));
+      if (lane == 0 && c) atomicAdd(&nxt[s], (uint32_t)c);
+    }
+  }
+  __syncthreads();
+  if (tid < 4 && nxt[tid]) {
+    const int dt = (tid < 2 ? tz : to) + (tid & 1);
+    uint32_t* t1n = w.tile1 + ((size_t)(l + 1) * p.H + h) * p.ntiles;
+    if (dt < p.ntiles) __hip_atomic_fetch_add(t1n + dt, nxt[tid], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -211,20 +256,20 @@ hipError_t launch_cutoff(const CutoffArgs& a0, hipStream_t s) {
   if (a0.H == 0) return hipSuccess;
   CutoffArgs a = a0;
   const int64_t n = (int64_t)a.H * a.S;
-  const int64_t blocks = (n + 255) / 256;
-  const unsigned gq = (unsigned)(blocks < 8192 ? blocks : 8192);
-  hipLaunchKernelGGL(ranks_kernel, dim3(gq < 4096 ? gq : 4096), dim3(256), 0, s, a.order, a.rank, a.H, a.S);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (a.k > 0 && a.w < a.S) {   // otherwise every answer is 0 or S
-    const dim3 grid((unsigned)a.ntiles, (unsigned)a.H);
-    for (int l = 0; l < a.L; ++l) {
-      hipLaunchKernelGGL(wt_bits, grid, dim3(kWtThreads), 0, s, a, l);
-      hipLaunchKernelGGL(wt_scatter, grid, dim3(kWtThreads), 0, s, a, l);
-    }
-    e = hipGetLastError();
+  if (a.k > 0 && a.w < a.S) {   // otherwise every answer is 0 or S and no matrix is needed
+    const int64_t ncount = (int64_t)a.L * a.H * a.ntiles;
+    const int64_t fb = (ncount + 255) / 256;
+    hipLaunchKernelGGL(wt_fill_kernel, dim3((unsigned)(fb < 2048 ? fb : 2048)), dim3(256), 0, s,
+                       static_cast<uint32_t*>(a.ws), ncount);
+    const int rb = (a.S + kWtRanksPer * 256 - 1) / (kWtRanksPer * 256);
+    hipLaunchKernelGGL(wt_ranks, dim3((unsigned)rb, (unsigned)a.H), dim3(256), 0, s, a);
+    for (int l = 0; l < a.L; ++l)
+      hipLaunchKernelGGL(wt_level, dim3((unsigned)a.ntiles, (unsigned)a.H), dim3(kWtThreads), 0, s, a, l);
+    const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  const int64_t blocks = (n + 255) / 256;
+  const unsigned gq = (unsigned)(blocks < 8192 ? blocks : 8192);
   hipLaunchKernelGGL(wt_query, dim3(gq), dim3(256), 0, s, a);
   return hipGetLastError();
 }

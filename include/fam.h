@@ -544,9 +544,10 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
  *              unspecified cut-offs, never an access out of bounds)
  *   tau        device out, [H, S] int32, fully overwritten
  *   workspace  device scratch of fam_topk_cutoff_workspace_size(H, S) bytes
- *              (the ranks, two level sequences and the bit words and
- *              counts of ceil(log2 S) levels: about 16 bytes per entry at
- *              S = 131072), 4-byte aligned, owned by the caller
+ *              (the ranks, two level sequences, the bit words and counts
+ *              of ceil(log2 S) levels and per-tile counts of ones: about 16
+ *              bytes per entry at S = 131072), 4-byte aligned, owned by the
+ *              caller, contents irrelevant on entry
  * Requirements: S <= 262144; H <= 65535; w >= 0, k >= 0.
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
  * FAM_ERR_HIP.

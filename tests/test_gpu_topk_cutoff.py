@@ -5,7 +5,10 @@ Ranks come from fam_rank_order on scores with ties; the oracle ranks the
 same scores itself. Cases: the page's Fenwick-tree example, random shapes
 (S not a multiple of the 2048-query chunk), k = 0, k > S, w >= S, S = 1,
 several heads, and at 131072 positions the closed forms (older or newer
-tokens ranked best) plus sampled queries of a random ranking.
+tokens ranked best) plus sampled queries of a random ranking; at the
+largest S (262144: 256 tiles of 1024 positions, so the look-back over the
+earlier tiles takes several rounds of 64), with many heads, on tile
+boundaries, and twice on one workspace.
 """
 import json
 import os
@@ -82,3 +85,39 @@ def test_random_ranking_sampled_at_131072():
             assert got[h, q] == want, (h, q)
         full = got[h, w + k - 1:]
         assert np.all(np.diff(full) <= 0)
+
+
+@pytest.mark.parametrize("H,S", [(33, 3000), (3, 1024), (3, 1025), (2, 65536 + 7)])
+def test_tile_boundaries_and_many_heads(H, S):
+    say(f"fam_topk_cutoff H={H} S={S}")
+    rng = np.random.default_rng(S + H)
+    scores = rng.standard_normal((H, S)).astype(np.float32)
+    w, k = 3, max(1, S // 7)
+    got = gpu_cutoffs(scores, w, k)
+    for h in range(H):
+        ranks = tc.ranks_from_scores(scores[h].astype(np.float64))
+        np.testing.assert_array_equal(got[h], tc.cutoffs(ranks, w, k))
+
+
+def test_largest_s_sampled_and_workspace_reuse():
+    """S = 262144 on two heads, then a small call on the same workspace: each
+    call clears its tile status words and tickets."""
+    S, w, k, H = 262144, 100, 50000, 2
+    say(f"fam_topk_cutoff S={S} then S=3000 on one workspace")
+    ws = torch.empty(fam.fam_topk_cutoff_workspace_size(H, S), dtype=torch.uint8, device=DEV)
+    scores = np.random.default_rng(12).standard_normal((H, S)).astype(np.float32)
+    order = fam.fam_rank_order(torch.from_numpy(scores).to(DEV))
+    got = fam.fam_topk_cutoff(order, w, k, workspace=ws).cpu().numpy()
+    qs = np.array([w + k - 2, w + k - 1, 70000, 131071, 131072, 200003, S - 1])
+    for h in range(H):
+        ranks = tc.ranks_from_scores(scores[h].astype(np.float64))
+        for q in qs:
+            elig = ranks[: max(0, q - w + 1)]
+            want = np.partition(elig, k - 1)[k - 1] if elig.size >= k else S
+            assert got[h, q] == want, (h, q)
+        assert np.all(np.diff(got[h, w + k - 1:]) <= 0)
+    small = np.random.default_rng(13).standard_normal((3, 3000)).astype(np.float32)
+    order = fam.fam_rank_order(torch.from_numpy(small).to(DEV))
+    got = fam.fam_topk_cutoff(order, 5, 200, workspace=ws).cpu().numpy()
+    for h in range(3):
+        np.testing.assert_array_equal(got[h], tc.cutoffs(tc.ranks_from_scores(small[h].astype(np.float64)), 5, 200))
