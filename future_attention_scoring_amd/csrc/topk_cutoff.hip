@@ -75,26 +75,24 @@ __global__ __launch_bounds__(256) void wt_ranks(CutoffArgs p) {
   const int h = blockIdx.y, tid = threadIdx.x;
   for (int b = tid; b < p.ntiles; b += 256) hist[b] = 0u;
   __syncthreads();
-#pragma unroll 4
+  int pos[kWtRanksPer];   // all loads in flight (clamped index, no branch between them)
+#pragma unroll
   for (int j = 0; j < kWtRanksPer; ++j) {
     const int r = (blockIdx.x * kWtRanksPer + j) * 256 + tid;
-    if (r < p.S) {
-      const int pos = p.order[(int64_t)h * p.S + r];
-      if (pos >= 0 && pos < p.S) {
-        p.rank[(int64_t)h * p.S + pos] = r + 1;
-        if ((r >> (p.L - 1)) & 1) atomicAdd(&hist[pos / kCutoffTile], 1u);
-      }
+    pos[j] = p.order[(int64_t)h * p.S + (r < p.S ? r : p.S - 1)];
+  }
+#pragma unroll
+  for (int j = 0; j < kWtRanksPer; ++j) {
+    const int r = (blockIdx.x * kWtRanksPer + j) * 256 + tid;
+    if (r < p.S && pos[j] >= 0 && pos[j] < p.S) {
+      p.rank[(int64_t)h * p.S + pos[j]] = r + 1;
+      if ((r >> (p.L - 1)) & 1) atomicAdd(&hist[pos[j] / kCutoffTile], 1u);
     }
   }
   __syncthreads();
   uint32_t* t1 = w.tile1 + (size_t)h * p.ntiles;   // level 0
   for (int b = tid; b < p.ntiles; b += 256)
     if (hist[b]) __hip_atomic_fetch_add(t1 + b, hist[b], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// value of position i at level l (0 .. S-1 for a permutation; level 0 reads the ranks)
-__device__ __forceinline__ int wt_value(const CutoffArgs& p, const WtLayout& w, int h, int l, int i) {
-  return l == 0 ? p.rank[(int64_t)h * p.S + i] - 1 : w.seq[l & 1][(int64_t)h * p.S + i];
 }
 
 // How many of 0 .. S-1 have bit b set.
@@ -122,10 +120,22 @@ __global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
 
   // ones of the head before this tile and in all (wave 0), with the values
   // of the tile in flight
+  // the level's sequence and the next one (explicit selects: a runtime index
+  // into the pointer pair would put it in memory and serialise the loads)
+  const int32_t* cur = l == 0 ? p.rank + (int64_t)h * p.S : ((l & 1) ? w.seq[1] : w.seq[0]) + (int64_t)h * p.S;
+  const int off = l == 0 ? 1 : 0;   // level 0 holds rank = value + 1
+  int v[kWtPer];
+#pragma unroll
+  for (int j = 0; j < kWtPer; ++j) {
+    const int i = tile * kCutoffTile + wave * (kCutoffTile / 4) + j * 64 + lane;
+    v[j] = cur[i < p.S ? i : p.S - 1] - off;   // clamped: no branch between the loads
+  }
   if (wave == 0) {
     int before = 0, total = 0;
-    for (int b = lane; b < p.ntiles; b += 64) {
-      const int c = (int)t1[b];
+#pragma unroll
+    for (int u = 0; u < kWtMaxTiles / 64; ++u) {
+      const int b = lane + 64 * u;
+      const int c = b < p.ntiles ? (int)t1[b] : 0;
       total += c;
       before += b < tile ? c : 0;
     }
@@ -141,12 +151,10 @@ __global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
     if (lane < 4) nxt[lane] = 0u;
   }
   // wave `wave` covers positions tile*1024 + wave*256 + j*64 + lane
-  int v[kWtPer];
   bool bit[kWtPer];
 #pragma unroll
   for (int j = 0; j < kWtPer; ++j) {
     const int i = tile * kCutoffTile + wave * (kCutoffTile / 4) + j * 64 + lane;
-    v[j] = i < p.S ? wt_value(p, w, h, l, i) : 0;
     bit[j] = i < p.S && ((v[j] >> shift) & 1);
     const uint64_t m = __ballot(bit[j]);
     if (lane == 0) {
@@ -180,7 +188,7 @@ __global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
   const int nshift = shift - 1;   // the next level's bit
   const int tz = (tile * kCutoffTile - before) / kCutoffTile;   // first tile of the zeros' run
   const int to = (zeros + before) / kCutoffTile;                 // first tile of the ones' run
-  int32_t* next = w.seq[(l + 1) & 1] + (int64_t)h * p.S;
+  int32_t* next = (((l + 1) & 1) ? w.seq[1] : w.seq[0]) + (int64_t)h * p.S;
 #pragma unroll
   for (int j = 0; j < kWtPer; ++j) {
     const int i = tile * kCutoffTile + wave * (kCutoffTile / 4) + j * 64 + lane;
