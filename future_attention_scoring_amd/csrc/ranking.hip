@@ -52,17 +52,29 @@ __device__ __forceinline__ uint64_t digit_peers(uint32_t d, bool live) {
   return peers;
 }
 
-// Key and position of entry e at pass `pass` (pass 0 reads the scores).
-__device__ __forceinline__ void rank_entry(const RankArgs& p, int h, int pass, int e, uint32_t& key,
-                                           uint32_t& pos) {
+// Keys and positions of the entries e0 + j * stride (j < kRankSteps) at pass
+// `pass` (pass 0 reads the scores). Entries past n are read at n - 1 (the
+// callers mark them invalid); the pass branch sits outside the loads, so
+// all of them are in flight at once.
+__device__ __forceinline__ void rank_entries(const RankArgs& p, int h, int pass, int e0, int stride,
+                                             uint32_t (&key)[kRankSteps], uint32_t (&pos)[kRankSteps]) {
   if (pass == 0) {
-    key = ~order_key(p.scores[h * p.row_stride + e]);
-    pos = (uint32_t)e;
+    const float* sc = p.scores + h * p.row_stride;
+#pragma unroll
+    for (int j = 0; j < kRankSteps; ++j) {
+      const int e = e0 + j * stride;
+      key[j] = ~order_key(sc[e < p.n ? e : p.n - 1]);
+      pos[j] = (uint32_t)e;
+    }
   } else {
     const u32x2_t* src = static_cast<const u32x2_t*>(p.ws) + ((int64_t)((pass & 1) ? 0 : p.H) + h) * p.n;
-    const u32x2_t kv = src[e];
-    key = kv.x;
-    pos = kv.y;
+#pragma unroll
+    for (int j = 0; j < kRankSteps; ++j) {
+      const int e = e0 + j * stride;
+      const u32x2_t kv = src[e < p.n ? e : p.n - 1];
+      key[j] = kv.x;
+      pos[j] = kv.y;
+    }
   }
 }
 
@@ -79,14 +91,11 @@ __global__ __launch_bounds__(kRankThreads) void rank_count(RankArgs p, int pass)
   if (threadIdx.x < kDigits) cnt[threadIdx.x] = 0;
   __syncthreads();
   const int e0 = tile * kRankTile;
-  for (int i = threadIdx.x; i < kRankTile; i += kRankThreads) {
-    const int e = e0 + i;
-    if (e < p.n) {
-      uint32_t key, pos;
-      rank_entry(p, h, pass, e, key, pos);
-      atomicAdd(&cnt[(key >> shift) & 255u], 1);
-    }
-  }
+  uint32_t key[kRankSteps], pos[kRankSteps];
+  rank_entries(p, h, pass, e0 + (int)threadIdx.x, kRankThreads, key, pos);
+#pragma unroll
+  for (int j = 0; j < kRankSteps; ++j)
+    if (e0 + j * kRankThreads + (int)threadIdx.x < p.n) atomicAdd(&cnt[(key[j] >> shift) & 255u], 1);
   __syncthreads();
   if (threadIdx.x < kDigits) rank_hist(p, h)[(int64_t)threadIdx.x * p.ntiles + tile] = cnt[threadIdx.x];
 }
@@ -150,13 +159,9 @@ __global__ __launch_bounds__(kRankThreads) void rank_place(RankArgs p, int pass)
   uint32_t key[kRankSteps], pos[kRankSteps], dg[kRankSteps];
   int rank[kRankSteps];
   const int e0 = tile * kRankTile + wave * 64 * kRankSteps;
-#pragma unroll
-  for (int st = 0; st < kRankSteps; ++st) {
-    const int e = e0 + st * 64 + lane;
-    key[st] = 0;
-    pos[st] = 0;
-    if (e < p.n) rank_entry(p, h, pass, e, key[st], pos[st]);
-  }
+  // every load of the thread in flight: clamped entries, no branch between
+  // the loads (entries past n are marked invalid below)
+  rank_entries(p, h, pass, e0 + lane, 64, key, pos);
 #pragma unroll
   for (int st = 0; st < kRankSteps; ++st) {
     const bool valid = e0 + st * 64 + lane < p.n;
@@ -226,6 +231,7 @@ __global__ __launch_bounds__(kCostThreads) void cost_kernel(CostArgs p) {
 
 constexpr int kOverlapThreads = 1024;
 
+constexpr int kOverlapBatch = 8;   // list entries per thread and batch
 __global__ __launch_bounds__(kOverlapThreads) void overlap_kernel(OverlapArgs p) {
   extern __shared__ uint32_t bits[];
   __shared__ int64_t part[kOverlapThreads / 64];
@@ -233,18 +239,39 @@ __global__ __launch_bounds__(kOverlapThreads) void overlap_kernel(OverlapArgs p)
   const int words = (p.S + 31) / 32;
   for (int w = threadIdx.x; w < words; w += kOverlapThreads) bits[w] = 0u;
   __syncthreads();
-  for (int64_t i = p.off_a[h] + threadIdx.x; i < p.off_a[h + 1]; i += kOverlapThreads) {
-    const int x = p.idx_a[i];
-    if (x >= 0 && x < p.S) atomicOr(&bits[x >> 5], 1u << (x & 31));
+  // batches of kOverlapBatch entries per thread, all loads in flight (clamped
+  // indices; entries past the list are dropped after the loads)
+  const int64_t a0 = p.off_a[h], a1 = p.off_a[h + 1];
+  for (int64_t i0 = a0 + threadIdx.x; i0 < a1; i0 += (int64_t)kOverlapThreads * kOverlapBatch) {
+    int x[kOverlapBatch];
+#pragma unroll
+    for (int u = 0; u < kOverlapBatch; ++u) {
+      const int64_t i = i0 + (int64_t)u * kOverlapThreads;
+      x[u] = p.idx_a[i < a1 ? i : a1 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kOverlapBatch; ++u)
+      if (i0 + (int64_t)u * kOverlapThreads < a1 && x[u] >= 0 && x[u] < p.S)
+        atomicOr(&bits[x[u] >> 5], 1u << (x[u] & 31));
   }
   __syncthreads();
   int64_t cnt = 0;
-  for (int64_t i = p.off_b[h] + threadIdx.x; i < p.off_b[h + 1]; i += kOverlapThreads) {
-    const int x = p.idx_b[i];
-    if (x >= 0 && x < p.S && ((bits[x >> 5] >> (x & 31)) & 1u)) {
-      // count each position of b once: clear it after the first hit
-      const uint32_t old = atomicAnd(&bits[x >> 5], ~(1u << (x & 31)));
-      if ((old >> (x & 31)) & 1u) ++cnt;
+  const int64_t b0 = p.off_b[h], b1 = p.off_b[h + 1];
+  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)kOverlapThreads * kOverlapBatch) {
+    int x[kOverlapBatch];
+#pragma unroll
+    for (int u = 0; u < kOverlapBatch; ++u) {
+      const int64_t i = i0 + (int64_t)u * kOverlapThreads;
+      x[u] = p.idx_b[i < b1 ? i : b1 - 1];
+    }
+#pragma unroll
+    for (int u = 0; u < kOverlapBatch; ++u) {
+      const int y = x[u];
+      if (i0 + (int64_t)u * kOverlapThreads < b1 && y >= 0 && y < p.S && ((bits[y >> 5] >> (y & 31)) & 1u)) {
+        // count each position of b once: clear it after the first hit
+        const uint32_t old = atomicAnd(&bits[y >> 5], ~(1u << (y & 31)));
+        if ((old >> (y & 31)) & 1u) ++cnt;
+      }
     }
   }
 #pragma unroll
