@@ -127,6 +127,27 @@ def test_target_worked_example_on_gpu():
     assert torch.isneginf(got[0, 0, :t]).all() and torch.isneginf(got[0, 0, t + 1:]).all()
 
 
+@pytest.mark.parametrize("Hq,Hkv,S,offset", [(3, 1, 400, 0), (5, 1, 401, 0), (16, 1, 64, 0), (8, 2, 4096, 0),
+                                              (4, 2, 1000, 1), (2, 1, 8, 0), (6, 3, 12, 0)])
+def test_target_vector_and_scalar_paths(Hq, Hkv, S, offset):
+    """Both aggregates against the oracle's epilogue on random masses: four
+    keys per thread (S % 4 == 0, 16-byte aligned rows) and one key per thread
+    (S odd, or rows shifted by one float), for group sizes with a
+    compile-time loop (1, 2, 4, 8) and without one (3, 5, 16)."""
+    say(f"kvpop target paths Hq={Hq} Hkv={Hkv} S={S} offset={offset}")
+    g = torch.Generator().manual_seed(Hq * 1000 + S)
+    flat = torch.rand(Hq * S + offset, generator=g) ** 4   # masses over many orders of magnitude
+    flat[::7] = 0.0                                          # zero masses: log(eps) or -inf
+    mass_q = flat.to(DEV)[offset:].view(1, Hq, S)
+    W, gq = 5, Hq // Hkv
+    for agg in ("max", "mean"):
+        for eps in (0.0, 1e-6):
+            got = fam.fam_kvpop_target(mass_q, Hkv, W, eps=eps, aggregate=agg).cpu().numpy()[0]
+            mq = mass_q[0].double().cpu().numpy()
+            for h in range(Hkv):
+                check_target(got[h], kt.target(mq[h * gq:(h + 1) * gq], W, eps=eps, aggregate=agg))
+
+
 def test_counts_floor_at_one_on_gpu():
     """N_j = max(1, S - (j + W)): keys in and past the window divide by 1."""
     say("count floor")
