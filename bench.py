@@ -253,6 +253,7 @@ def ranking_row(runs, mass, wl, stream):
     order = torch.empty((H, S), dtype=torch.int32, device=m.device)
     ws = torch.empty(max(8, fam.fam_rank_order_workspace_size(H, S)), dtype=torch.uint8, device=m.device)
     cost = torch.empty(H, dtype=torch.float64, device=m.device)
+    cost_ws = torch.empty(max(8, fam.fam_eviction_cost_workspace_size(H, S)), dtype=torch.uint8, device=m.device)
     budgets = [S // 8] * H
     ia, oa = fam.evict_select(m, budgets, wl.sinks, wl.recent)
     ib, ob = fam.evict_select(recency, budgets, wl.sinks, wl.recent)
@@ -266,7 +267,7 @@ def ranking_row(runs, mass, wl, stream):
         fam.fam_rank_order(m, order=order, workspace=ws)
         if e:
             e[1].record(stream)
-        fam.fam_eviction_cost(m, order, cost=cost)
+        fam.fam_eviction_cost(m, order, cost=cost, workspace=cost_ws)
         if e:
             e[2].record(stream)
         common = fam.fam_retention_overlap(ia, oa, ib, ob, S)

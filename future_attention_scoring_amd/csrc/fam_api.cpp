@@ -578,8 +578,14 @@ fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n,
   return hip_status(fam::launch_rank(a, static_cast<hipStream_t>(stream)), "fam_rank_order launch");
 }
 
+size_t fam_eviction_cost_workspace_size(int H, int n) {
+  if (H < 0 || n < 0) return 0;
+  return (size_t)H * fam::cost_blocks(n) * sizeof(double);
+}
+
 fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const int32_t* order, int H,
-                             int n, double* cost, void* stream) {
+                             int n, double* cost, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   if (H < 0 || n < 0) return fail(FAM_ERR_INVALID_ARG, "H and n must be >= 0");
   if (n > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "n = %d exceeds %d", n, kMaxSeq);
   if (H == 0) return ok();
@@ -590,7 +596,14 @@ fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const 
   if ((reinterpret_cast<uintptr_t>(importance) | reinterpret_cast<uintptr_t>(order)) & 3u ||
       (reinterpret_cast<uintptr_t>(cost) & 7u))
     return fail(FAM_ERR_INVALID_ARG, "importance and order must be 4-byte, cost 8-byte aligned");
-  fam::CostArgs a{importance, row_stride, order, cost, H, n};
+  const size_t need = fam_eviction_cost_workspace_size(H, n);
+  if (need > 0 && (!workspace || workspace_bytes < need))
+    return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
+  fam::CostArgs a{importance, row_stride, order, cost, static_cast<double*>(workspace), H, n};
   return hip_status(fam::launch_cost(a, static_cast<hipStream_t>(stream)), "fam_eviction_cost launch");
 }
 

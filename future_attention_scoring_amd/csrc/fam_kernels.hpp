@@ -164,8 +164,11 @@ struct CostArgs {
   int64_t row_stride;
   const int32_t* order;  // [H, n]
   double* cost;          // [H]
+  double* part;          // [H][cost_blocks(n)] workspace: partial sums per block of entries
   int H, n;
 };
+constexpr int kCostBlock = 4096;   // entries per workgroup
+inline int cost_blocks(int n) { return (n + kCostBlock - 1) / kCostBlock; }
 hipError_t launch_cost(const CostArgs& a, hipStream_t s);
 
 struct OverlapArgs {

@@ -23,8 +23,10 @@
 //
 // cost_kernel: cost[h] = sum_r (r + 1) * importance[h, order[h, r]], which
 // equals the sum over budgets b = 0 .. n of the importance evicted at b
-// (the entry ranked r is evicted for the r + 1 budgets b <= r). fp64
-// partial sums in a fixed order, so the result is deterministic.
+// (the entry ranked r is evicted for the r + 1 budgets b <= r). One
+// workgroup per block of 4096 entries of a head (all gathers of a thread in
+// flight) writes an fp64 partial sum; cost_reduce_kernel adds a head's
+// partials in block order, so the result is deterministic.
 //
 // overlap_kernel: common[h] = |set(a_h) & set(b_h)| for two kept-index lists
 // per head, with a bitmap of the head's positions in LDS.
@@ -197,36 +199,54 @@ __global__ __launch_bounds__(kRankThreads) void rank_place(RankArgs p, int pass)
   }
 }
 
-constexpr int kCostThreads = 1024;
-constexpr int kCostUnroll = 4;   // gathers in flight per thread
+constexpr int kCostThreads = 256;
+constexpr int kCostPer = kCostBlock / kCostThreads;   // entries per thread, all gathers in flight
+static_assert(kCostPer * kCostThreads == kCostBlock, "cost block");
 
+// Partial sum of (r + 1) * importance[order[r]] over one block of entries of
+// one head, in fp64 with a fixed reduction order.
 __global__ __launch_bounds__(kCostThreads) void cost_kernel(CostArgs p) {
-  __shared__ double part[kCostThreads];
-  const int h = blockIdx.x;
+  __shared__ double red[kCostThreads / 64];
+  const int blk = blockIdx.x, h = blockIdx.y;
   const float* imp = p.importance + h * p.row_stride;
   const int32_t* ord = p.order + (int64_t)h * p.n;
+  const int r0 = blk * kCostBlock + threadIdx.x;
+  int j[kCostPer];
+  float x[kCostPer];
+#pragma unroll
+  for (int u = 0; u < kCostPer; ++u) {   // clamped entries: no branch between the loads
+    const int r = r0 + u * kCostThreads;
+    j[u] = ord[r < p.n ? r : p.n - 1];
+  }
+#pragma unroll
+  for (int u = 0; u < kCostPer; ++u) x[u] = imp[j[u] >= 0 && j[u] < p.n ? j[u] : 0];
   double acc = 0.0;
-  for (int r0 = threadIdx.x; r0 < p.n; r0 += kCostThreads * kCostUnroll) {
-    int j[kCostUnroll];
-    float x[kCostUnroll];
 #pragma unroll
-    for (int u = 0; u < kCostUnroll; ++u) {
-      const int r = r0 + u * kCostThreads;
-      j[u] = r < p.n ? ord[r] : -1;
-    }
-#pragma unroll
-    for (int u = 0; u < kCostUnroll; ++u) x[u] = (j[u] >= 0 && j[u] < p.n) ? imp[j[u]] : 0.f;
-#pragma unroll
-    for (int u = 0; u < kCostUnroll; ++u)
-      acc = fma((double)(r0 + u * kCostThreads + 1), (double)x[u], acc);
+  for (int u = 0; u < kCostPer; ++u) {
+    const int r = r0 + u * kCostThreads;
+    const bool ok = r < p.n && j[u] >= 0 && j[u] < p.n;
+    acc = fma((double)(r + 1), ok ? (double)x[u] : 0.0, acc);
   }
-  part[threadIdx.x] = acc;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = acc;
   __syncthreads();
-  for (int s = kCostThreads / 2; s > 0; s >>= 1) {
-    if ((int)threadIdx.x < s) part[threadIdx.x] += part[threadIdx.x + s];
-    __syncthreads();
+  if (threadIdx.x == 0) {
+    double t = 0.0;
+#pragma unroll
+    for (int w = 0; w < kCostThreads / 64; ++w) t += red[w];
+    p.part[(int64_t)h * gridDim.x + blk] = t;
   }
-  if (threadIdx.x == 0) p.cost[h] = part[0];
+}
+
+// cost[h] = the sum of the head's block partial sums, in block order.
+__global__ __launch_bounds__(64) void cost_reduce_kernel(CostArgs p, int nb) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= p.H) return;
+  const double* part = p.part + (int64_t)h * nb;
+  double t = 0.0;
+  for (int b = 0; b < nb; ++b) t += part[b];
+  p.cost[h] = t;
 }
 
 constexpr int kOverlapThreads = 1024;
@@ -300,7 +320,9 @@ hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
 
 hipError_t launch_cost(const CostArgs& a, hipStream_t s) {
   if (a.H == 0) return hipSuccess;
-  hipLaunchKernelGGL(cost_kernel, dim3((unsigned)a.H), dim3(kCostThreads), 0, s, a);
+  const int nb = cost_blocks(a.n);
+  if (nb > 0) hipLaunchKernelGGL(cost_kernel, dim3((unsigned)nb, (unsigned)a.H), dim3(kCostThreads), 0, s, a);
+  hipLaunchKernelGGL(cost_reduce_kernel, dim3((unsigned)((a.H + 63) / 64)), dim3(64), 0, s, a, nb);
   return hipGetLastError();
 }
 

@@ -54,7 +54,8 @@ _SIGNATURES = {
     "kv_compact_inplace_workspace_size": (ctypes.c_size_t, [_i64]),
     "fam_rank_order": (_i, [_p, _i64, _i, _i, _p, _p, ctypes.c_size_t, _p]),
     "fam_rank_order_workspace_size": (ctypes.c_size_t, [_i, _i]),
-    "fam_eviction_cost": (_i, [_p, _i64, _p, _i, _i, _p, _p]),
+    "fam_eviction_cost": (_i, [_p, _i64, _p, _i, _i, _p, _p, ctypes.c_size_t, _p]),
+    "fam_eviction_cost_workspace_size": (ctypes.c_size_t, [_i, _i]),
     "fam_retention_overlap": (_i, [_p, _p, _p, _p, _i, _i, _p, _p]),
     "fam_topk_cutoff": (_i, [_p, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]),
     "fam_topk_cutoff_workspace_size": (ctypes.c_size_t, [_i, _i]),
@@ -565,16 +566,25 @@ def fam_rank_order(scores: torch.Tensor, order: Optional[torch.Tensor] = None,
     return order
 
 
+def fam_eviction_cost_workspace_size(H: int, n: int) -> int:
+    return int(load().fam_eviction_cost_workspace_size(int(H), int(n)))
+
+
 def fam_eviction_cost(importance: torch.Tensor, order: torch.Tensor,
-                      cost: Optional[torch.Tensor] = None) -> torch.Tensor:
+                      cost: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Importance evicted by `order`, summed over all budgets: [H] fp64."""
     H, n = _score_rows(importance, "importance")
     if order.dtype != torch.int32 or tuple(order.shape) != (H, n) or not order.is_contiguous():
         raise FamError(1, "order must be a contiguous int32 [H, n] tensor")
     if cost is None:
         cost = torch.empty(H, dtype=torch.float64, device=importance.device)
+    if workspace is None:
+        workspace = torch.empty(max(fam_eviction_cost_workspace_size(H, n), 8), dtype=torch.uint8,
+                                device=importance.device)
     _check(load().fam_eviction_cost(importance.data_ptr(), _row_stride(importance), order.data_ptr(), H,
-                                    n, cost.data_ptr(), _stream(importance)))
+                                    n, cost.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel() * workspace.element_size(), _stream(importance)))
     return cost
 
 

@@ -496,11 +496,19 @@ size_t fam_rank_order_workspace_size(int H, int n);
  *   importance  device, [H] rows of n fp32, row stride row_stride (>= n when
  *               H > 1)
  *   order       device, [H, n] int32 (entries outside [0, n) are skipped)
- *   cost        device out, [H] fp64 (sums in fp64, fixed order)
- * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
+ *   cost        device out, [H] fp64 (sums in fp64, fixed order: per block
+ *               of 4096 entries, then the blocks in order)
+ *   workspace   device scratch of fam_eviction_cost_workspace_size(H, n)
+ *               bytes (one fp64 partial sum per head and block), 8-byte
+ *               aligned, owned by the caller; may be NULL when that is 0
+ * Requirements: H <= 65535.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
+ * FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
 fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const int32_t* order,
-                             int H, int n, double* cost, void* stream);
+                             int H, int n, double* cost, void* workspace, size_t workspace_bytes,
+                             void* stream);
+size_t fam_eviction_cost_workspace_size(int H, int n);
 
 /* ------------------------------------------------------------------------
  * fam_retention_overlap -- entries two kept sets share, per head.

@@ -292,8 +292,13 @@ def test_ranking_validation():
     assert lib.fam_rank_order(FAKE, 99, 2, 100, FAKE, FAKE, ws, None) == INVALID       # stride < n
     assert lib.fam_rank_order(FAKE, 100, 2, 100, FAKE, FAKE + 4, ws, None) == INVALID  # workspace alignment
     assert lib.fam_rank_order(None, 100, 0, 100, None, None, 0, None) == 0             # H == 0
-    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, None, None) == INVALID
-    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE + 4, None) == INVALID   # cost alignment
+    cws = lib.fam_eviction_cost_workspace_size(2, 100)
+    assert cws == 2 * 1 * 8 and lib.fam_eviction_cost_workspace_size(8, 131072) == 8 * 32 * 8
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, None, FAKE, cws, None) == INVALID
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE + 4, FAKE, cws, None) == INVALID   # cost alignment
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE, FAKE, cws - 1, None) == WORKSPACE
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE, None, cws, None) == WORKSPACE
+    assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE, FAKE + 4, cws, None) == INVALID   # workspace alignment
     assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 2, 300000, FAKE, None) == UNSUPPORTED
     assert lib.fam_retention_overlap(FAKE, FAKE, None, FAKE, 2, 100, FAKE, None) == INVALID
     assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 0, 100, None, None) == 0
