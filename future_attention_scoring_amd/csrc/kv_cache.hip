@@ -6,9 +6,9 @@
 // (conclusion: a static cache can keep a fixed region per head and overwrite
 // old entries in place instead of copying into a new tensor).
 //
-// Append. One 16-byte piece per thread and pass over (head, row, piece);
-// every head's rows row0 .. row0+n-1 are written, and optionally their
-// positions pos0 .. pos0+n-1.
+// Append. Four 16-byte pieces of (row, piece) per thread, all loads in
+// flight, grid (pieces / 1024, heads); every head's rows row0 .. row0+n-1
+// are written, and optionally their positions pos0 .. pos0+n-1.
 //
 // In-place compaction. Head h keeps the rows idx[offsets[h] + r] (ascending,
 // as evict_select writes them) and moves row idx[...+r] to row r. Every read
@@ -43,22 +43,36 @@ namespace fam {
 namespace {
 
 constexpr int kAppendThreads = 256;
+constexpr int kAppendPer = 4;   // pieces per thread
 constexpr int kInplaceThreads = 512;
 constexpr int kInplaceUnroll = 8;   // rows per thread and chunk (loads in flight: 2 x 8)
 constexpr int kInplaceSpinLimit = 1 << 22;   // polls per flag batch (a bound; waits end long before)
 
 template <int CPR>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs p) {
+  // kAppendPer pieces per thread, kAppendThreads apart, all loads in flight
+  // (clamped pieces past the end are loaded and not stored)
   const int h = blockIdx.y;
   const int64_t pieces = (int64_t)p.n * CPR;
-  const int64_t stride = (int64_t)gridDim.x * kAppendThreads;
-  for (int64_t e = (int64_t)blockIdx.x * kAppendThreads + threadIdx.x; e < pieces; e += stride) {
-    const int r = (int)(e / CPR), ch = (int)(e % CPR);
-    const u32x4_t kv = load16(p.k_src + h * p.ks_sh + (int64_t)r * p.ks_ss + ch * 8);
-    const u32x4_t vv = load16(p.v_src + h * p.vs_sh + (int64_t)r * p.vs_ss + ch * 8);
-    store16(p.k + h * p.k_sh + (int64_t)(p.row0 + r) * p.k_ss + ch * 8, kv);
-    store16(p.v + h * p.v_sh + (int64_t)(p.row0 + r) * p.v_ss + ch * 8, vv);
-    if (p.pos && ch == 0) p.pos[h * p.pos_sh + p.row0 + r] = p.pos0 + r;
+  const int64_t e0 = (int64_t)blockIdx.x * kAppendThreads * kAppendPer + threadIdx.x;
+  u32x4_t kv[kAppendPer], vv[kAppendPer];
+#pragma unroll
+  for (int u = 0; u < kAppendPer; ++u) {
+    const int64_t e = e0 + (int64_t)u * kAppendThreads;
+    const int64_t ec = e < pieces ? e : pieces - 1;
+    const int r = (int)(ec / CPR), ch = (int)(ec % CPR);
+    kv[u] = load16(p.k_src + h * p.ks_sh + (int64_t)r * p.ks_ss + ch * 8);
+    vv[u] = load16(p.v_src + h * p.vs_sh + (int64_t)r * p.vs_ss + ch * 8);
+  }
+#pragma unroll
+  for (int u = 0; u < kAppendPer; ++u) {
+    const int64_t e = e0 + (int64_t)u * kAppendThreads;
+    if (e < pieces) {
+      const int r = (int)(e / CPR), ch = (int)(e % CPR);
+      store16(p.k + h * p.k_sh + (int64_t)(p.row0 + r) * p.k_ss + ch * 8, kv[u]);
+      store16(p.v + h * p.v_sh + (int64_t)(p.row0 + r) * p.v_ss + ch * 8, vv[u]);
+      if (p.pos && ch == 0) p.pos[h * p.pos_sh + p.row0 + r] = p.pos0 + r;
+    }
   }
 }
 
@@ -174,8 +188,8 @@ hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.n == 0 || a.H == 0) return hipSuccess;
   const int cpr = a.d / 8;
   const int64_t pieces = (int64_t)a.n * cpr;
-  int64_t bx = (pieces + kAppendThreads - 1) / kAppendThreads;
-  if (bx > 4096) bx = 4096;
+  const int64_t bx = (pieces + kAppendThreads * kAppendPer - 1) / (kAppendThreads * kAppendPer);
+  if (bx > 0x7fffffff) return hipErrorInvalidConfiguration;
   if (a.H > 65535) return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)bx, (unsigned)a.H);
   switch (cpr) {
