@@ -235,7 +235,7 @@ int fam_key_norm_parts(int S) { return S < 1 ? 0 : (S < fam::kNormParts ? S : fa
 
 fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, int d,
                          int64_t k_sb, int64_t k_sh, int64_t k_ss, float* knorm, void* stream) {
-  const ScoreShape s{B, Hkv, Hkv, S, d, k_sb, k_sh, k_ss, k_sb, k_sh, k_ss};
+  const ScoreShape s{B, Hkv, Hkv, S, d, k_sb, k_sh, k_ss, k_sb, k_sh, k_ss, 0};
   fam_status st = check_scores(k, k, dtype, s);
   if (st != FAM_OK) return st;
   if (!knorm) return fail(FAM_ERR_INVALID_ARG, "knorm must be non-null");
@@ -247,7 +247,7 @@ fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, 
 fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
                    int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
                    int64_t k_ss, float scale, const float* knorm, float* lse, void* stream) {
-  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   if (!lse) return fail(FAM_ERR_INVALID_ARG, "lse must be non-null");
@@ -274,7 +274,7 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
                     int Hkv, int S, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb,
                     int64_t k_sh, int64_t k_ss, int W, float scale, float* mass, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   return mass_group(q, k, lse, dtype, s, W, scale, mass, workspace, workspace_bytes,
@@ -285,7 +285,7 @@ fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam
                              int Hq, int Hkv, int S, int d, int64_t q_sb, int64_t q_sh,
                              int64_t q_ss, int64_t k_sb, int64_t k_sh, int64_t k_ss, int W,
                              float scale, float* mass_q, void* stream) {
-  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   if (!lse || !mass_q) return fail(FAM_ERR_INVALID_ARG, "lse and mass_q must be non-null");
@@ -316,7 +316,7 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int
                        int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
                        int64_t k_ss, int W, float scale, float* lse, float* mass,
                        void* workspace, size_t workspace_bytes, void* stream) {
-  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss};
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   return compute_all(q, k, dtype, s, W, scale, lse, mass, workspace, workspace_bytes,

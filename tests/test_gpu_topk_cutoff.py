@@ -6,9 +6,9 @@ same scores itself. Cases: the page's Fenwick-tree example, random shapes
 (S not a multiple of the 2048-query chunk), k = 0, k > S, w >= S, S = 1,
 several heads, and at 131072 positions the closed forms (older or newer
 tokens ranked best) plus sampled queries of a random ranking; at the
-largest S (262144: 256 tiles of 1024 positions, so the look-back over the
-earlier tiles takes several rounds of 64), with many heads, on tile
-boundaries, and twice on one workspace.
+largest S (262144: 256 tiles of 1024 positions, the most tile counts a
+level sums), with many heads, on tile boundaries, and twice on one
+workspace.
 """
 import json
 import os
@@ -101,7 +101,7 @@ def test_tile_boundaries_and_many_heads(H, S):
 
 def test_largest_s_sampled_and_workspace_reuse():
     """S = 262144 on two heads, then a small call on the same workspace: each
-    call clears its tile status words and tickets."""
+    call clears its per-tile counts of ones."""
     S, w, k, H = 262144, 100, 50000, 2
     say(f"fam_topk_cutoff S={S} then S=3000 on one workspace")
     ws = torch.empty(fam.fam_topk_cutoff_workspace_size(H, S), dtype=torch.uint8, device=DEV)
