@@ -302,6 +302,75 @@ def ranking_row(runs, mass, wl, stream):
     }
 
 
+def decode_row(runs, stream):
+    """Time the decode-time eviction sweep apart from the step: a
+    Qwen2.5-1.5B-like cache (28 layers x 2 KV heads = 56 slices, d = 128,
+    fp16 K/V), given fp32 scores ~ Exp(1), 4 sinks + 32 recent + the best of
+    the rest to budgets {4096, 2048, 1024, 512} at contexts {512, 4096,
+    32768, 120000}: evict_select + kv_compact into a new cache per cell.
+    K/V are seeded normal values drawn on the device (only their size
+    matters for the timing); the scores come from the same seeded generator
+    as the parity tests."""
+    dev = torch.device("cuda:0")
+    cells = workloads.decode_sweep()
+    rows, tot_bytes, tot_us = [], 0, 0.0
+    for S in workloads.DECODE_CONTEXTS:
+        first = [c for c in cells if c.S == S][0]
+        H, d = first.H, first.d
+        gen = torch.Generator(device=dev).manual_seed(first.seed * 1000003 + S)
+        k = torch.randn((H, S, d), generator=gen, device=dev, dtype=torch.float32).to(first.dtype)
+        v = torch.randn((H, S, d), generator=gen, device=dev, dtype=torch.float32).to(first.dtype)
+        scores = torch.from_numpy(first.scores()).to(dev)
+        for cell in [c for c in cells if c.S == S]:
+            budgets = [cell.budget] * H
+            _, off = fam.evict_plan(budgets, S, cell.sinks, cell.recent)
+            total = int(off[-1])
+            idx = torch.empty(total, dtype=torch.int32, device=dev)
+            offd = torch.empty(H + 1, dtype=torch.int64, device=dev)
+            ws = torch.empty(max(16, fam.evict_select_workspace_size(H, S, cell.sinks, cell.recent)),
+                             dtype=torch.uint8, device=dev)
+            kn = torch.empty((total, d), dtype=k.dtype, device=dev)
+            vn = torch.empty_like(kn)
+
+            def run(e=None):
+                if e:
+                    e[0].record(stream)
+                fam.evict_select(scores, budgets, cell.sinks, cell.recent, idx=idx, offsets=offd, workspace=ws)
+                if e:
+                    e[1].record(stream)
+                fam.kv_compact(k, v, idx, offd, total, k_new=kn, v_new=vn)
+                if e:
+                    e[2].record(stream)
+
+            for _ in range(2):
+                run()
+            torch.cuda.synchronize()
+            # all timed runs enqueued before one synchronisation, so that the
+            # host's per-call work overlaps the GPU's and the events time the
+            # GPU alone
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(runs)]
+            for e in evs:
+                run(e)
+            torch.cuda.synchronize()
+            sel = [e[0].elapsed_time(e[1]) * 1e3 for e in evs]
+            cmp_ = [e[1].elapsed_time(e[2]) * 1e3 for e in evs]
+            s_us, c_us = float(np.median(sel)), float(np.median(cmp_))
+            # scores read, indices written, kept K and V rows read and written
+            nbytes = 4 * H * S + 4 * total + 2 * 2 * total * d * k.element_size()
+            tot_bytes += nbytes
+            tot_us += s_us + c_us
+            rows.append({"S": S, "budget": cell.budget, "kept_rows": total, "select_us": round(s_us, 1),
+                         "compact_us": round(c_us, 1), "bytes": nbytes,
+                         "GBps": round(nbytes / ((s_us + c_us) * 1e-6) / 1e9, 1)})
+        del k, v
+        torch.cuda.empty_cache()
+    return {"workload": "qwen2.5-1.5b-like decode-time eviction sweep (28 layers x 2 KV heads, d=128, fp16)",
+            "runs": runs, "cells": rows,
+            "all_cells": {"bound": "hbm", "bytes": tot_bytes, "us": round(tot_us, 1),
+                          "achieved": round(tot_bytes / (tot_us * 1e-6) / 1e9, 3), "peak": PEAK_HBM_BYTES / 1e9,
+                          "unit": "GB/s", "frac": round(tot_bytes / (tot_us * 1e-6) / PEAK_HBM_BYTES, 4)}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -315,6 +384,8 @@ def main():
                     help="timed runs of the chunked prefill-compress loop; 0 skips it")
     ap.add_argument("--ranking-runs", type=int, default=3,
                     help="timed runs of the ranking-quality row; 0 skips it")
+    ap.add_argument("--decode-runs", type=int, default=5,
+                    help="timed runs per cell of the decode-time eviction sweep; 0 skips it")
     ap.add_argument("--chunked-only", action="store_true",
                     help="run only the chunked prefill-compress row (for a kernel trace of it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -443,6 +514,8 @@ def main():
         out["ranking"] = ranking_row(args.ranking_runs, mass, wl, stream)
     if args.chunked_runs > 0:
         out["chunked_prefill"] = chunked_row(args.chunked_runs, q, k, v, wl, stream)
+    if args.decode_runs > 0:
+        out["decode_sweep"] = decode_row(args.decode_runs, stream)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(out), flush=True)
