@@ -581,8 +581,15 @@ size_t select_workspace_bytes(int slots, int nchunk) { return ws_bytes(slots, nc
 hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   const int groups = (a.nheads + kXcds - 1) / kXcds;
   const dim3 grid(kXcds * a.nchunk * groups);
-  hipLaunchKernelGGL(sel_hist, grid, dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(sel_collect, grid, dim3(kThreads), 0, s, a);
+  // heads that keep all their candidates or none need no threshold: when
+  // every head is such, the last launch alone writes the lists
+  bool all_trivial = true;
+  for (int i = 0; i < a.nheads; ++i)
+    if (a.n_choose[i] != 0 && a.n_choose[i] != a.c1 - a.c0) all_trivial = false;
+  if (!all_trivial) {
+    hipLaunchKernelGGL(sel_hist, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(sel_collect, grid, dim3(kThreads), 0, s, a);
+  }
   hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }

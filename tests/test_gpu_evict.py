@@ -76,6 +76,18 @@ def test_select_ties_and_degenerate_budgets():
     assert_select_equal(scores, [S] * 6, 4, 32)                      # everything
 
 
+@pytest.mark.parametrize("budgets", [[0, 0, 0], [5000, 9000, 4096], [0, 4096, 1], [4096, 0, 70]])
+def test_select_every_head_trivial(budgets):
+    """Heads that keep only the forced rows or every row need no threshold;
+    when all heads are such, only the last launch runs (the last two cases
+    mix trivial heads with ones that need a threshold, so all three run)."""
+    say(f"select with trivial heads {budgets}")
+    S = 4096
+    rng = np.random.default_rng(17)
+    scores = rng.standard_normal((3, S)).astype(np.float32)
+    assert_select_equal(scores, budgets, 4, 32)
+
+
 def test_select_unaligned_row_stride():
     say("unaligned score rows")
     rng = np.random.default_rng(9)
