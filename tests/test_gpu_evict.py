@@ -88,6 +88,35 @@ def test_select_every_head_trivial(budgets):
     assert_select_equal(scores, budgets, 4, 32)
 
 
+def test_select_more_heads_than_a_batch():
+    """150 heads run as batches of 64, 64 and 22 (the last batch's heads are
+    offset into the same idx and offsets); some batches mix trivial heads
+    (budget 0 or >= S) with ones that need a threshold, one batch has only
+    trivial heads. Compaction of the result is checked too."""
+    H, S, d = 150, 2000, 64
+    say(f"select + compact H={H} S={S}")
+    rng = np.random.default_rng(23)
+    scores = nasty(rng, H, S)
+    budgets = [int(x) for x in rng.integers(0, S + 8, H)]
+    for h in range(64, 128):          # the second batch: trivial heads only
+        budgets[h] = 0 if h % 2 else S + 5
+    idx, off = assert_select_equal(scores, budgets, 4, 32)
+    g = torch.Generator().manual_seed(23)
+    k = torch.randn(H, S, d, generator=g).to(torch.float16)
+    v = torch.randn(H, S, d, generator=g).to(torch.float16)
+    idx_d = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(DEV)
+    off_d = torch.from_numpy(np.ascontiguousarray(off, dtype=np.int64)).to(DEV)
+    k_new, v_new = fam.kv_compact(k.to(DEV), v.to(DEV), idx_d, off_d)
+    torch.cuda.synchronize()
+    o = np.asarray(off, dtype=np.int64)
+    ih = np.asarray(idx, dtype=np.int64)
+    kn, vn = k_new.cpu(), v_new.cpu()
+    for h in range(H):
+        rows = torch.from_numpy(ih[o[h]:o[h + 1]])
+        assert torch.equal(kn[o[h]:o[h + 1]].view(torch.int16), k[h, rows].view(torch.int16))
+        assert torch.equal(vn[o[h]:o[h + 1]].view(torch.int16), v[h, rows].view(torch.int16))
+
+
 def test_select_unaligned_row_stride():
     say("unaligned score rows")
     rng = np.random.default_rng(9)
