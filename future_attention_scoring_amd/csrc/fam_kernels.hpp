@@ -195,7 +195,7 @@ constexpr int kCutoffMaxS = 1 << 18;  // at most 256 tiles of 1024 positions
 constexpr int kCutoffTile = 1024;
 // Levels (bits of a rank - 1), words per level and tiles for S positions, and
 // the workspace bytes after the ranks: per-tile counts of ones [L][H][ntiles],
-// two level sequences [H][S], and bit words and word counts [H][L][nw].
+// two level sequences [H][S], and (bit word, word count) pairs [H][L][nw].
 inline void cutoff_shape(int S, int& L, int& nw, int& ntiles) {
   L = 1;
   while ((1 << L) < S) ++L;
@@ -205,7 +205,8 @@ inline void cutoff_shape(int S, int& L, int& nw, int& ntiles) {
 inline size_t cutoff_workspace_bytes(int H, int S) {
   int L, nw, ntiles;
   cutoff_shape(S, L, nw, ntiles);
-  return 4 * ((size_t)L * H * ntiles + (size_t)2 * H * S + (size_t)2 * H * L * nw);
+  // + 8: slack to align the interleaved (word, count) pairs to 8 bytes
+  return 4 * ((size_t)L * H * ntiles + (size_t)2 * H * S + (size_t)2 * H * L * nw) + 8;
 }
 hipError_t launch_cutoff(const CutoffArgs& a, hipStream_t s);
 

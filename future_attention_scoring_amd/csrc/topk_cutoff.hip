@@ -48,8 +48,7 @@ constexpr int kWtMaxTiles = kCutoffMaxS / kCutoffTile;
 struct WtLayout {
   uint32_t* tile1;   // [L][H][ntiles] ones per tile of each level
   int32_t* seq[2];   // [H][S] value sequences of the levels (ping-pong)
-  uint32_t* words;   // [H][L][nw] bit words
-  uint32_t* cnt;     // [H][L][nw] ones before each word
+  u32x2_t* wc;       // [H][L][nw] {bit word, ones before the word}: one 8-byte load per rank
 };
 
 __device__ __forceinline__ WtLayout wt_layout(const CutoffArgs& p) {
@@ -58,8 +57,8 @@ __device__ __forceinline__ WtLayout wt_layout(const CutoffArgs& p) {
   w.tile1 = reinterpret_cast<uint32_t*>(p.ws);
   w.seq[0] = reinterpret_cast<int32_t*>(w.tile1 + (size_t)p.L * p.H * p.ntiles);
   w.seq[1] = w.seq[0] + hs;
-  w.words = reinterpret_cast<uint32_t*>(w.seq[1] + hs);
-  w.cnt = w.words + (size_t)p.H * p.L * p.nw;
+  const uintptr_t a = reinterpret_cast<uintptr_t>(w.seq[1] + hs);
+  w.wc = reinterpret_cast<u32x2_t*>((a + 7) & ~(uintptr_t)7);   // 8-byte aligned (the size has the slack)
   return w;
 }
 
@@ -114,8 +113,7 @@ __global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
   const int tile = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int shift = p.L - 1 - l;
-  uint32_t* words = w.words + ((size_t)h * p.L + l) * p.nw;
-  uint32_t* cnt = w.cnt + ((size_t)h * p.L + l) * p.nw;
+  u32x2_t* wc = w.wc + ((size_t)h * p.L + l) * p.nw;
   const uint32_t* t1 = w.tile1 + ((size_t)l * p.H + h) * p.ntiles;
 
   // ones of the head before this tile and in all (wave 0), with the values
@@ -175,11 +173,9 @@ __global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
       if (lane >= o) incl += u;
     }
     cl[lane] = (uint32_t)(incl - pc);
-    cnt[tile * kWtTileWords + lane] = (uint32_t)(before + incl - pc);
-    words[tile * kWtTileWords + lane] = word;
+    wc[tile * kWtTileWords + lane] = u32x2_t{word, (uint32_t)(before + incl - pc)};
     if (tile == p.ntiles - 1 && lane == 0) {   // terminal entry: rank1(S) and the level's ones
-      words[p.nw - 1] = 0u;
-      cnt[p.nw - 1] = (uint32_t)sh_total;
+      wc[p.nw - 1] = u32x2_t{0u, (uint32_t)sh_total};
     }
   }
   if (l + 1 == p.L) return;   // the last level needs no next sequence
@@ -216,10 +212,10 @@ __global__ __launch_bounds__(kWtThreads) void wt_level(CutoffArgs p, int l) {
   }
 }
 
-// rank1 of level words/counts at position i (0 <= i <= S)
-__device__ __forceinline__ int wt_rank1(const uint32_t* words, const uint32_t* cnt, int i) {
-  const int wi = i >> 5;
-  return (int)cnt[wi] + __popc(words[wi] & ((1u << (i & 31)) - 1u));
+// rank1 of a level at position i (0 <= i <= S): the ones before i
+__device__ __forceinline__ int wt_rank1(const u32x2_t* wc, int i) {
+  const u32x2_t e = wc[i >> 5];
+  return (int)e.y + __popc(e.x & ((1u << (i & 31)) - 1u));
 }
 
 __global__ __launch_bounds__(256) void wt_query(CutoffArgs p) {
@@ -237,9 +233,8 @@ __global__ __launch_bounds__(256) void wt_query(CutoffArgs p) {
     } else {
       int lo = 0, hi = m, k = p.k, val = 0;
       for (int l = 0; l < p.L; ++l) {
-        const uint32_t* words = w.words + ((size_t)h * p.L + l) * p.nw;
-        const uint32_t* cnt = w.cnt + ((size_t)h * p.L + l) * p.nw;
-        const int o_lo = wt_rank1(words, cnt, lo), o_hi = wt_rank1(words, cnt, hi);
+        const u32x2_t* wc = w.wc + ((size_t)h * p.L + l) * p.nw;
+        const int o_lo = wt_rank1(wc, lo), o_hi = wt_rank1(wc, hi);
         const int z = (hi - lo) - (o_hi - o_lo);
         if (k <= z) {
           lo -= o_lo;
@@ -247,9 +242,9 @@ __global__ __launch_bounds__(256) void wt_query(CutoffArgs p) {
         } else {
           k -= z;
           val |= 1 << (p.L - 1 - l);
-          const int zeros = p.S - (int)cnt[p.nw - 1];   // the level's zeros come first
-          lo = zeros + o_lo;
-          hi = zeros + o_hi;
+          const int zeros = p.S - ones_below(p.S, p.L - 1 - l);   // the level's zeros come first (as placed)
+          lo = min(zeros + o_lo, p.S);   // the clamp only acts on a non-permutation order
+          hi = min(zeros + o_hi, p.S);
         }
       }
       out = val + 1;

@@ -316,8 +316,9 @@ def test_topk_cutoff_validation():
     assert lib.fam_topk_cutoff_workspace_size(8, 300000) == 0
     ws = lib.fam_topk_cutoff_workspace_size(2, 100)
     # ranks (2 x 100 ints), then 7 levels: ones per tile 7 x 2 x 1, two
-    # sequences 2 x 2 x 100, bit words and counts 2 x 2 x 7 x 33
-    assert ws == 4 * (2 * 100 + 7 * 2 * 1 + 2 * 2 * 100 + 2 * 2 * 7 * 33)
+    # sequences 2 x 2 x 100, (bit word, count) pairs 2 x 2 x 7 x 33, and 8
+    # bytes of slack to align the pairs
+    assert ws == 4 * (2 * 100 + 7 * 2 * 1 + 2 * 2 * 100 + 2 * 2 * 7 * 33) + 8
     assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, 10, FAKE, FAKE, ws - 1, None) == WORKSPACE
     assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, 10, FAKE, FAKE + 2, ws, None) == INVALID   # 4-byte alignment
     assert lib.fam_topk_cutoff(FAKE, 2, 100, -1, 10, FAKE, FAKE, ws, None) == INVALID
