@@ -169,7 +169,8 @@ def test_llama_128k_sampled():
     sampled_checks(wl, t, lse, mass, group=5, n_rows=8, tail=640)
 
 
-@pytest.mark.parametrize("S,Hq,Hkv,d", [(8192, 32, 8, 128), (131072, 32, 8, 128), (5000, 6, 2, 64)])
+@pytest.mark.parametrize("S,Hq,Hkv,d", [(8192, 32, 8, 128), (131072, 32, 8, 128), (5000, 6, 2, 64),
+                                        (524288, 4, 1, 128)])
 def test_w0_invariant_full_size(S, Hq, Hkv, d):
     say(f"W=0 invariant S={S} Hq={Hq} Hkv={Hkv} d={d}")
     gen = torch.Generator(device=DEV).manual_seed(S)
@@ -185,7 +186,7 @@ def harmonic_prefix(n):
     return np.concatenate([[0.0], np.cumsum(1.0 / np.arange(1, n + 1, dtype=np.float64))])
 
 
-@pytest.mark.parametrize("S,W", [(131072, 512), (32768, 256), (3000, 0)])
+@pytest.mark.parametrize("S,W", [(131072, 512), (32768, 256), (3000, 0), (524288, 1024)])
 def test_uniform_logits_closed_form_full_size(S, W):
     say(f"uniform closed form S={S} W={W}")
     Hq, Hkv, d = 8, 2, 128
