@@ -86,7 +86,9 @@ __device__ __forceinline__ int* rank_hist(const RankArgs& p, int h) {
 }
 
 // Pass `pass`: digit counts of one tile of one head.
-__global__ __launch_bounds__(kRankThreads) void rank_count(RankArgs p, int pass) {
+// tile_major: counts stored [tile][digit] (read by a fused rank_place)
+// instead of [digit][tile] (read by rank_scan).
+__global__ __launch_bounds__(kRankThreads) void rank_count(RankArgs p, int pass, int tile_major) {
   __shared__ int cnt[kDigits];
   const int tile = blockIdx.x, h = blockIdx.y;
   const int shift = 8 * pass;
@@ -99,7 +101,9 @@ __global__ __launch_bounds__(kRankThreads) void rank_count(RankArgs p, int pass)
   for (int j = 0; j < kRankSteps; ++j)
     if (e0 + j * kRankThreads + (int)threadIdx.x < p.n) atomicAdd(&cnt[(key[j] >> shift) & 255u], 1);
   __syncthreads();
-  if (threadIdx.x < kDigits) rank_hist(p, h)[(int64_t)threadIdx.x * p.ntiles + tile] = cnt[threadIdx.x];
+  if (threadIdx.x < kDigits)
+    rank_hist(p, h)[tile_major ? (int64_t)tile * kDigits + threadIdx.x : (int64_t)threadIdx.x * p.ntiles + tile] =
+        cnt[threadIdx.x];
 }
 
 // Pass `pass`: the counts of every (digit, tile) of a head, digit-major,
@@ -146,14 +150,47 @@ __global__ __launch_bounds__(kScanThreads) void rank_scan(RankArgs p) {
 // Pass `pass`: place one tile's entries after the slots rank_scan reserved;
 // inside the tile, (wave, step, lane) order is entry order, so equal digits
 // keep their order and the sort is stable.
+// FUSED: rank_scan did not run, the digit counts are raw and tile-major; with at most
+// kFusedTiles tiles a head, every workgroup forms its own first slots: digit
+// d's slot = entries of smaller digits in all tiles + entries of digit d in
+// earlier tiles (one exclusive scan over the digits).
+constexpr int kFusedTiles = 64;
+template <bool FUSED>
 __global__ __launch_bounds__(kRankThreads) void rank_place(RankArgs p, int pass) {
   __shared__ int base[kDigits];                // this tile's first slot per digit
   __shared__ int wcnt[kRankWaves][kDigits];    // per wave: running count, then exclusive prefix
+  __shared__ int ssh[kRankWaves];
   const int tile = blockIdx.x, h = blockIdx.y;
   const int shift = 8 * pass;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const uint64_t below = (1ull << lane) - 1ull;
-  base[tid] = rank_hist(p, h)[(int64_t)tid * p.ntiles + tile];
+  if constexpr (FUSED) {
+    const int* cnt = rank_hist(p, h) + tid;   // digit tid of every tile: [tile][digit], coalesced
+    int c[kFusedTiles];
+#pragma unroll
+    for (int t = 0; t < kFusedTiles; ++t) c[t] = cnt[(t < p.ntiles ? t : p.ntiles - 1) * kDigits];   // all in flight
+    int all = 0, before = 0;
+#pragma unroll
+    for (int t = 0; t < kFusedTiles; ++t) {
+      all += t < p.ntiles ? c[t] : 0;
+      before += t < tile ? c[t] : 0;
+    }
+    // exclusive scan of the digit totals over the 256 threads
+    int incl = all;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int u = __shfl_up(incl, o);
+      if (lane >= o) incl += u;
+    }
+    if (lane == 63) ssh[wave] = incl;
+    __syncthreads();
+    int prev = 0;
+#pragma unroll
+    for (int w = 0; w < kRankWaves; ++w) prev += w < wave ? ssh[w] : 0;
+    base[tid] = prev + incl - all + before;
+  } else {
+    base[tid] = rank_hist(p, h)[(int64_t)tid * p.ntiles + tile];
+  }
 #pragma unroll
   for (int w = 0; w < kRankWaves; ++w) wcnt[w][tid] = 0;
   __syncthreads();
@@ -310,10 +347,15 @@ __global__ __launch_bounds__(kOverlapThreads) void overlap_kernel(OverlapArgs p)
 hipError_t launch_rank(const RankArgs& a, hipStream_t s) {
   if (a.H == 0 || a.n == 0) return hipSuccess;
   const dim3 grid((unsigned)a.ntiles, (unsigned)a.H);
+  const bool fused = a.ntiles <= kFusedTiles;   // the place launch forms its own slots
   for (int pass = 0; pass < 4; ++pass) {
-    hipLaunchKernelGGL(rank_count, grid, dim3(kRankThreads), 0, s, a, pass);
-    hipLaunchKernelGGL(rank_scan, dim3((unsigned)a.H), dim3(kScanThreads), 0, s, a);
-    hipLaunchKernelGGL(rank_place, grid, dim3(kRankThreads), 0, s, a, pass);
+    hipLaunchKernelGGL(rank_count, grid, dim3(kRankThreads), 0, s, a, pass, fused ? 1 : 0);
+    if (fused) {
+      hipLaunchKernelGGL(rank_place<true>, grid, dim3(kRankThreads), 0, s, a, pass);
+    } else {
+      hipLaunchKernelGGL(rank_scan, dim3((unsigned)a.H), dim3(kScanThreads), 0, s, a);
+      hipLaunchKernelGGL(rank_place<false>, grid, dim3(kRankThreads), 0, s, a, pass);
+    }
   }
   return hipGetLastError();
 }

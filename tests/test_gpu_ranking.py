@@ -36,7 +36,10 @@ def special_rows(seed, H, n):
 
 
 @pytest.mark.parametrize("seed,H,n", [(1, 1, 1), (2, 3, 1000), (3, 2, 1025), (4, 10, 4097),
-                                      (5, 1, 70001), (6, 8, 3000)])
+                                      (5, 1, 70001), (6, 8, 3000),
+                                      # up to 64 tiles of 4096 the place launch forms its own
+                                      # digit slots; beyond, a scan launch does
+                                      (10, 2, 262144), (11, 2, 262145), (12, 1, 300007)])
 def test_rank_order_matches_oracle(seed, H, n):
     say(f"fam_rank_order seed={seed} H={H} n={n}")
     s = special_rows(seed, H, n)
