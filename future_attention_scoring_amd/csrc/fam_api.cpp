@@ -151,6 +151,30 @@ size_t lse_split_bytes(const ScoreShape& s, int nks) {
 
 fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
 
+// Partial slices of the group-sum mass pass. From kMassRangeMinS keys on
+// (and while at most kMassMaxRanges ranges cover the query rows) split s owns
+// the query tiles [s * R, (s + 1) * R), R = kMassRangeTiles: the workgroups
+// resident together then read the same few MB of Q, which stay in cache,
+// instead of each re-reading its own share from HBM. Shorter sequences
+// divide each key block's steps evenly over mass_splits workgroups.
+struct MassPlan {
+  int nsplit;
+  int range_tiles;   // 0: even shares
+};
+MassPlan mass_plan(const ScoreShape& s) {
+  if (s.S >= fam::kMassRangeMinS) {
+    const int64_t nt = ((int64_t)s.rows() + fam::kMassQTile - 1) / fam::kMassQTile;
+    const int64_t nr = (nt + fam::kMassRangeTiles - 1) / fam::kMassRangeTiles;
+    if (nr > 1 && nr <= fam::kMassMaxRanges) return {(int)nr, fam::kMassRangeTiles};
+  }
+  return {mass_splits(s.B, s.Hkv, s.S), 0};
+}
+
+// Bytes of the mass pass's partial slices: nsplit * B * Hkv * S floats.
+size_t mass_split_bytes(const ScoreShape& s, int nsplit) {
+  return nsplit > 1 ? (size_t)nsplit * s.B * s.Hkv * s.S * sizeof(float) : 0;
+}
+
 // Group-sum mass pass on a validated shape: as many splits as wanted and as
 // the workspace holds (none without one).
 fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype dtype,
@@ -162,6 +186,14 @@ fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype 
   if (workspace && !aligned16(workspace))
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const size_t per_split = (size_t)s.B * s.Hkv * s.S * sizeof(float);
+  const MassPlan plan = mass_plan(s);
+  if (workspace && plan.range_tiles > 0 && mass_split_bytes(s, plan.nsplit) <= workspace_bytes) {
+    fam::MassArgs a = mass_args(q, k, lse, s, W, scale, mass, nullptr, static_cast<float*>(workspace),
+                                plan.nsplit);
+    a.range_tiles = plan.range_tiles;
+    return hip_status(fam::launch_mass(a, elem_of(dtype), stream), what);
+  }
+  // even shares, as many as wanted and as the workspace holds
   int nsplit = mass_splits(s.B, s.Hkv, s.S);
   if (!workspace) nsplit = 1;
   if ((size_t)nsplit * per_split > workspace_bytes) nsplit = (int)(workspace_bytes / per_split);
@@ -258,15 +290,15 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq,
 
 size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S) {
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0) return 0;
-  const int n = mass_splits(B, Hkv, S);
-  return n > 1 ? (size_t)n * B * Hkv * S * sizeof(float) : 0;
+  const ScoreShape s{B, Hq, Hkv, S, 64, 0, 0, 0, 0, 0, 0, 0};   // Sq = 0: every row is a query
+  return mass_split_bytes(s, mass_plan(s).nsplit);
 }
 
 size_t fam_compute_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk) {
   if (B < 1 || Hq < 1 || Hkv < 1 || Sk < 1 || Sq < 1 || Sq > Sk || Hq % Hkv != 0) return 0;
   const ScoreShape s{B, Hq, Hkv, Sk, 64, 0, 0, 0, 0, 0, 0, Sq};
   const size_t lse_bytes = lse_split_bytes(s, lse_splits(s));
-  const size_t mass_bytes = fam_mass_workspace_size(B, Hq, Hkv, Sk);
+  const size_t mass_bytes = mass_split_bytes(s, mass_plan(s).nsplit);
   return lse_bytes > mass_bytes ? lse_bytes : mass_bytes;
 }
 

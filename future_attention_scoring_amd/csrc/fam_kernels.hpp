@@ -58,8 +58,16 @@ struct MassArgs {
   // and a reduction adds them into `mass` in a fixed order.
   float* part;
   int nsplit;
+  // Range mode (range_tiles > 0, group-sum mode only): split s owns the
+  // query tiles [s * range_tiles, (s + 1) * range_tiles) of every key block
+  // instead of an even share of the block's steps.
+  int range_tiles;
 };
 constexpr int kMassKeysPerWG = 256;   // keys owned by one mass-pass workgroup
+constexpr int kMassQTile = 64;        // query rows per mass-pass step
+constexpr int kMassRangeTiles = 64;   // query tiles per range in range mode
+constexpr int kMassRangeMinS = 65536; // range mode from this many keys on
+constexpr int kMassMaxRanges = 128;   // at most this many ranges (partial slices)
 hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s);
 
 // KVpop supervision target from per-query-head mass.

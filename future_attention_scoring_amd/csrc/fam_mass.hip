@@ -47,6 +47,7 @@ constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWG = kKeysPerWave * kWaves;
 static_assert(kKeysPerWG == kMassKeysPerWG, "host and kernel key-block size");
 constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
+static_assert(kQTile == kMassQTile, "host and kernel query-tile size");
 
 // Sum of exp2(c*s - L) over one 32x32 block, no window predicate.
 __device__ __forceinline__ float block_sum_full(const f32x16_t& acc, const float (&lv)[16], float c) {
@@ -86,8 +87,12 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   const int nbh = p.B * p.Hkv;
   const int bh = blockIdx.x % nbh;
   const int rest = blockIdx.x / nbh;
-  const int split = PER_HEAD ? 0 : rest % p.nsplit;
-  const int kbi = PER_HEAD ? rest : rest / p.nsplit;
+  // range mode numbers the workgroups range-major, latest range first, so
+  // that the workgroups resident together read the same query tiles
+  const int rtiles = PER_HEAD ? 0 : p.range_tiles;
+  const int nkb_all = (p.S + kKeysPerWG - 1) / kKeysPerWG;
+  const int split = PER_HEAD ? 0 : (rtiles > 0 ? p.nsplit - 1 - rest / nkb_all : rest % p.nsplit);
+  const int kbi = PER_HEAD ? rest : (rtiles > 0 ? rest % nkb_all : rest / p.nsplit);
   const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -95,12 +100,23 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   const int j0 = kbi * kKeysPerWG;
   const int jw = j0 + wave * kKeysPerWave;
 
+  // query row r (position off + r) sees key j iff r >= j + Wr; the block's
+  // future queries lie in the tiles [t_first, t_last)
+  const int Wr = p.W - (p.S - p.Sq);
+  const int i_first = max(0, j0 + Wr);
+  const int t_first = i_first / kQTile;
+  const int t_last = (p.Sq + kQTile - 1) / kQTile;
+  // range mode: the tiles [split * rtiles, (split + 1) * rtiles) of this
+  // workgroup's range that hold future queries of the block, [r_lo, r_hi)
+  const int r_lo = rtiles > 0 ? max(t_first, split * rtiles) : t_first;
+  const int r_hi = rtiles > 0 ? min(t_last, (split + 1) * rtiles) : t_last;
+
   const uint16_t* kbase = p.k + b * p.k_sb + h * p.k_sh;
   u32x4_t kf[2][KS];
 #pragma unroll
   for (int blk = 0; blk < 2; ++blk) {
     const int key = jw + 32 * blk + col;
-    const bool ok = key < p.S;
+    const bool ok = key < p.S && r_lo < r_hi;   // an empty range only writes zeros
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks)
       kf[blk][ks] = ok ? load16(kbase + (int64_t)key * p.k_ss + ks * 16 + half * 8) : zero16();
@@ -117,13 +133,10 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       if (half == 0 && key < p.S) dst[key] = tot;
     }
   };
-  // query row r (position off + r) sees key j iff r >= j + Wr
-  const int Wr = p.W - (p.S - p.Sq);
-  const int i_first = max(0, j0 + Wr);
   if (i_first < p.Sq) {
     const int g = p.g;
-    const int t0 = i_first / kQTile;
-    const int t1 = (p.Sq + kQTile - 1) / kQTile;
+    const int t0 = t_first;
+    const int t1 = t_last;
     const int ntiles = t1 - t0;
     const int nsteps = ntiles * g;
     // tiles t >= t_full have every row r >= j0 + 255 + Wr: no predicate needed
@@ -171,9 +184,14 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       if (tid < kQTile) sl[buf][tid] = lst * kLog2e;
     };
 
-    // this workgroup's share of the key block's steps
-    const int u_begin = PER_HEAD ? 0 : (int)((int64_t)nsteps * split / p.nsplit);
-    const int u_end = PER_HEAD ? nsteps : (int)((int64_t)nsteps * (split + 1) / p.nsplit);
+    // this workgroup's share of the key block's steps: its range's tiles, or
+    // an even share of all steps
+    int u_begin = PER_HEAD ? 0 : (int)((int64_t)nsteps * split / p.nsplit);
+    int u_end = PER_HEAD ? nsteps : (int)((int64_t)nsteps * (split + 1) / p.nsplit);
+    if (rtiles > 0) {
+      u_begin = r_lo < r_hi ? (t1 - r_hi) * g : 0;
+      u_end = r_lo < r_hi ? (t1 - r_lo) * g : 0;
+    }
     if (u_begin < u_end) {
       load_step(u_begin);
       store_step(u_begin & 1);

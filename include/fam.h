@@ -133,11 +133,16 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype,
  *   workspace, workspace_bytes
  *          optional device scratch (16-byte aligned, owned by the caller,
  *          contents irrelevant on entry and unspecified on return). With
- *          fam_mass_workspace_size(B, Hq, Hkv, S) bytes, short sequences
- *          split each key block's queries over several workgroups and add
- *          the parts in a fixed order (same result up to fp32 rounding;
- *          deterministic). NULL or fewer bytes: fewer or no splits. Calls
- *          sharing a workspace must be ordered on one stream.
+ *          fam_mass_workspace_size(B, Hq, Hkv, S) bytes, each key block's
+ *          queries are split over several workgroups whose parts are added
+ *          in a fixed order (same result up to fp32 rounding;
+ *          deterministic): short sequences split to fill the chip; from
+ *          65536 keys on (up to 524288 query rows) every range of 4096
+ *          query rows gets its own workgroup per key block, so that
+ *          workgroups running together read the same queries. With fewer
+ *          bytes the long-sequence ranges give way to the short-sequence
+ *          splits, as many as fit; NULL: no splits. Calls sharing a
+ *          workspace must be ordered on one stream.
  *   other arguments and requirements as for fam_lse.
  * ---------------------------------------------------------------------- */
 fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype,
@@ -147,8 +152,8 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
                     int W, float scale, float* mass,
                     void* workspace, size_t workspace_bytes, void* stream);
 
-/* Bytes of workspace fam_mass and fam_compute use for these sizes (0 when
- * the sequence fills the chip without splitting, or for invalid sizes). */
+/* Bytes of workspace fam_mass uses for these sizes: splits * B * Hkv * S
+ * floats (0 when the pass does not split, or for invalid sizes). */
 size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S);
 
 /* ------------------------------------------------------------------------
@@ -260,8 +265,9 @@ fam_status fam_compute_chunk(const void* q, const void* k, fam_dtype dtype,
 
 /* Bytes of workspace fam_compute (Sq == Sk == S) and fam_compute_chunk use
  * for these sizes: the larger of the first pass's split partial sums
- * ((splits + 1) floats per query row) and fam_mass_workspace_size(B, Hq,
- * Hkv, Sk). 0 when neither pass splits, or for invalid sizes. */
+ * ((splits + 1) floats per query row) and the mass pass's split parts
+ * (splits * B * Hkv * Sk floats, the splits chosen for Sq query rows as in
+ * fam_mass). 0 when neither pass splits, or for invalid sizes. */
 size_t fam_compute_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk);
 
 /* ------------------------------------------------------------------------

@@ -141,7 +141,12 @@ def test_fam_mass_and_compute_validation():
 
 def test_mass_workspace_size():
     lib = fam.load()
-    assert lib.fam_mass_workspace_size(1, 32, 8, 131072) == 0          # fills the chip unsplit
+    # from 65536 keys on, one part per range of 64 query tiles of 64 rows
+    assert lib.fam_mass_workspace_size(1, 32, 8, 131072) == 32 * 8 * 131072 * 4
+    assert lib.fam_mass_workspace_size(1, 32, 8, 65536 + 1) == 17 * 8 * 65537 * 4   # ragged last range
+    assert lib.fam_mass_workspace_size(2, 4, 1, 524288) == 128 * 2 * 524288 * 4    # the most ranges
+    # beyond 128 ranges: 1M keys fill the chip unsplit
+    assert lib.fam_mass_workspace_size(1, 32, 8, 1 << 20) == 0
     n8k = lib.fam_mass_workspace_size(1, 32, 8, 8192)
     assert n8k > 0 and n8k % (8 * 8192 * 4) == 0 and n8k // (8 * 8192 * 4) <= 16
     assert lib.fam_mass_workspace_size(1, 3, 2, 100) == 0                # Hq % Hkv != 0
@@ -157,8 +162,13 @@ def test_compute_workspace_size():
     # pass's 5 splits of 8 x 20480 keys need less
     assert lib.fam_compute_workspace_size(1, 32, 8, 4096, 20480) == 7 * 32 * 4096 * 4
     assert lib.fam_mass_workspace_size(1, 32, 8, 20480) == 5 * 8 * 20480 * 4
-    # the full 128k square fills the chip with neither pass split
-    assert lib.fam_compute_workspace_size(1, 32, 8, 131072, 131072) == 0
+    # the full 128k square: the first pass fills the chip unsplit, the mass
+    # pass takes one part per range of 4096 query rows
+    assert lib.fam_compute_workspace_size(1, 32, 8, 131072, 131072) == 32 * 8 * 131072 * 4
+    # a 4096-query chunk over 131072 keys is one range, and 512 key blocks of
+    # 8 heads fill the chip: the mass pass does not split, the first pass's 6
+    # key-range splits remain
+    assert lib.fam_compute_workspace_size(1, 32, 8, 4096, 131072) == 7 * 32 * 4096 * 4
     # fewer than 32 key tiles: no key-range split, the mass pass's need remains
     assert lib.fam_compute_workspace_size(1, 8, 2, 100, 1000) == lib.fam_mass_workspace_size(1, 8, 2, 1000)
     for bad in ((1, 8, 2, 0, 100), (1, 8, 2, 101, 100), (1, 3, 2, 10, 10), (0, 4, 2, 10, 10)):

@@ -201,6 +201,64 @@ def test_uniform_logits_closed_form_full_size(S, W):
     check_mass(mass.cpu().numpy()[0], np.broadcast_to(ref, (Hkv, S)), S, W)
 
 
+def mass_parts(t):
+    """Per-launch ranges of the mass pass in range mode: 64 tiles of 64 query rows each."""
+    return -(-(-(-t // 64)) // 64)
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,S,d,W", [(51, 1, 8, 2, 65613, 128, 300), (52, 2, 4, 1, 70000, 64, 0),
+                                                 (53, 1, 4, 2, 65536, 128, 4095)])
+def test_range_mass_matches_even_splits_and_unsplit(seed, B, Hq, Hkv, S, d, W):
+    """From 65536 keys on, with fam_mass_workspace_size bytes, every range of
+    4096 query rows gets its own workgroup per key block; with room for fewer
+    parts the pass splits each block's steps evenly, and without a workspace
+    it runs unsplit. The three agree to fp32 rounding (the same products,
+    added in another order), unreachable keys are exactly 0 in each, and at
+    W = 0 every query head's mass sums to S."""
+    say(f"range mass seed={seed} B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} W={W}")
+    per = B * Hkv * S * 4
+    nr = mass_parts(S)
+    assert fam.fam_mass_workspace_size(B, Hq, Hkv, S) == nr * per
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    q = torch.randn(B, Hq, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    lse = fam.fam_lse(q, k, knorm=fam.fam_key_norms(k))
+    ranged = fam.fam_mass(q, k, lse, W)
+    even = fam.fam_mass(q, k, lse, W, workspace=torch.empty((nr - 1) * per, dtype=torch.uint8, device=DEV))
+    whole = fam.fam_mass(q, k, lse, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    pos = whole > 0
+    assert torch.all(whole[..., S - W:] == 0) and torch.all(ranged[..., S - W:] == 0)
+    for other, name in ((ranged, "ranges"), (even, "even splits")):
+        assert torch.equal(other[~pos], whole[~pos]), name
+        rel = ((other - whole).abs()[pos] / whole[pos]).max().item()
+        assert rel <= 1e-5, f"{name}: max rel diff {rel}"
+    if W == 0:
+        tot = ranged.double().sum(dim=-1).cpu().numpy()
+        np.testing.assert_allclose(tot, np.full((B, Hkv), S * (Hq // Hkv)), rtol=1e-4)
+
+
+@pytest.mark.parametrize("Sq,Sk,W", [(8256, 70000, 0), (12288, 65536, 200)])
+def test_range_mass_of_a_chunk(Sq, Sk, W):
+    """A chunk of Sq >= 4096 queries over Sk >= 65536 cache rows runs the mass
+    pass in ranges of the chunk's own rows; it agrees with the call without a
+    workspace, and at W = 0 each query head's mass sums to Sq."""
+    B, Hq, Hkv, d = 1, 8, 2, 128
+    say(f"range mass of a chunk Sq={Sq} Sk={Sk} W={W}")
+    gen = torch.Generator(device=DEV).manual_seed(Sq + Sk)
+    q = torch.randn(B, Hq, Sq, d, device=DEV, generator=gen).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, Sk, d, device=DEV, generator=gen).to(torch.bfloat16)
+    assert fam.fam_compute_workspace_size(B, Hq, Hkv, Sq, Sk) >= mass_parts(Sq) * B * Hkv * Sk * 4
+    lse_r, ranged = fam.fam_compute_chunk(q, k, W)
+    lse_w, whole = fam.fam_compute_chunk(q, k, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    assert (lse_r - lse_w).abs().max().item() <= 1e-5
+    pos = whole > 0
+    assert torch.equal(ranged[~pos], whole[~pos])
+    assert ((ranged - whole).abs()[pos] / whole[pos]).max().item() <= 2e-5
+    if W == 0:
+        tot = ranged.double().sum(dim=-1).cpu().numpy()
+        np.testing.assert_allclose(tot, np.full((B, Hkv), Sq * (Hq // Hkv)), rtol=1e-4)
+
+
 @pytest.mark.parametrize("S,W,a,b", [(65536, 100, 4.0, 4.0), (777, 3, 8.0, 2.0)])
 def test_single_sink_closed_form(S, W, a, b):
     say(f"single sink S={S} W={W}")
