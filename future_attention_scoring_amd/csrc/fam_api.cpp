@@ -175,6 +175,11 @@ size_t mass_split_bytes(const ScoreShape& s, int nsplit) {
   return nsplit > 1 ? (size_t)nsplit * s.B * s.Hkv * s.S * sizeof(float) : 0;
 }
 
+// Bytes of the per-query-head mass pass's range slices: nsplit * B * Hq * S floats.
+size_t per_head_split_bytes(const ScoreShape& s, int nsplit) {
+  return nsplit > 1 ? (size_t)nsplit * s.B * s.Hq * s.S * sizeof(float) : 0;
+}
+
 // Group-sum mass pass on a validated shape: as many splits as wanted and as
 // the workspace holds (none without one).
 fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype dtype,
@@ -316,16 +321,34 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
 fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype, int B,
                              int Hq, int Hkv, int S, int d, int64_t q_sb, int64_t q_sh,
                              int64_t q_ss, int64_t k_sb, int64_t k_sh, int64_t k_ss, int W,
-                             float scale, float* mass_q, void* stream) {
+                             float scale, float* mass_q, void* workspace, size_t workspace_bytes,
+                             void* stream) {
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
   if (!lse || !mass_q) return fail(FAM_ERR_INVALID_ARG, "lse and mass_q must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
-  const fam::MassArgs a = mass_args(q, k, lse, s, W, scale, nullptr, mass_q, nullptr, 1);
+  if (workspace && !aligned16(workspace))
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  fam::MassArgs a = mass_args(q, k, lse, s, W, scale, nullptr, mass_q, nullptr, 1);
+  // ranges of query rows as for the group sum, one [B, Hq, S] slice each
+  const MassPlan plan = mass_plan(s);
+  const size_t need = per_head_split_bytes(s, plan.nsplit);
+  if (workspace && plan.range_tiles > 0 && need <= workspace_bytes) {
+    a.part = static_cast<float*>(workspace);
+    a.nsplit = plan.nsplit;
+    a.range_tiles = plan.range_tiles;
+  }
   return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
                     "fam_mass_per_head launch");
+}
+
+size_t fam_mass_per_head_workspace_size(int B, int Hq, int Hkv, int S) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || Hq % Hkv != 0) return 0;
+  const ScoreShape s{B, Hq, Hkv, S, 64, 0, 0, 0, 0, 0, 0, 0};   // Sq = 0: every row is a query
+  const MassPlan plan = mass_plan(s);
+  return plan.range_tiles > 0 ? per_head_split_bytes(s, plan.nsplit) : 0;
 }
 
 fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, int W, float eps,

@@ -58,9 +58,10 @@ struct MassArgs {
   // and a reduction adds them into `mass` in a fixed order.
   float* part;
   int nsplit;
-  // Range mode (range_tiles > 0, group-sum mode only): split s owns the
-  // query tiles [s * range_tiles, (s + 1) * range_tiles) of every key block
-  // instead of an even share of the block's steps.
+  // Range mode (range_tiles > 0): split s owns the query tiles
+  // [s * range_tiles, (s + 1) * range_tiles) of every key block instead of an
+  // even share of the block's steps. In per-query-head mode (the only split
+  // it has) the parts are [nsplit, B*Hq*S] and the reduction writes mass_q.
   int range_tiles;
 };
 constexpr int kMassKeysPerWG = 256;   // keys owned by one mass-pass workgroup

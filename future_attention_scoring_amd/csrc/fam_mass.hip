@@ -89,10 +89,10 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   const int rest = blockIdx.x / nbh;
   // range mode numbers the workgroups range-major, latest range first, so
   // that the workgroups resident together read the same query tiles
-  const int rtiles = PER_HEAD ? 0 : p.range_tiles;
+  const int rtiles = p.range_tiles;
   const int nkb_all = (p.S + kKeysPerWG - 1) / kKeysPerWG;
-  const int split = PER_HEAD ? 0 : (rtiles > 0 ? p.nsplit - 1 - rest / nkb_all : rest % p.nsplit);
-  const int kbi = PER_HEAD ? rest : (rtiles > 0 ? rest % nkb_all : rest / p.nsplit);
+  const int split = rtiles > 0 ? p.nsplit - 1 - rest / nkb_all : (PER_HEAD ? 0 : rest % p.nsplit);
+  const int kbi = rtiles > 0 ? rest % nkb_all : (PER_HEAD ? rest : rest / p.nsplit);
   const int b = bh / p.Hkv, h = bh % p.Hkv;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
@@ -100,6 +100,12 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   const int j0 = kbi * kKeysPerWG;
   const int jw = j0 + wave * kKeysPerWave;
 
+  // PER_HEAD: query head gi's column sums go to mass_q, or in range mode to
+  // its slice of the partial sums [nsplit][B][Hq][S]
+  auto head_dst = [&](int gi) {
+    const int64_t row = (int64_t)b * p.Hq + h * p.g + gi;
+    return rtiles > 0 ? p.part + ((int64_t)split * p.B * p.Hq + row) * p.S : p.mass_q + row * p.S;
+  };
   // query row r (position off + r) sees key j iff r >= j + Wr; the block's
   // future queries lie in the tiles [t_first, t_last)
   const int Wr = p.W - (p.S - p.Sq);
@@ -141,11 +147,15 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const int nsteps = ntiles * g;
     // tiles t >= t_full have every row r >= j0 + 255 + Wr: no predicate needed
     const int t_full = (max(0, j0 + kKeysPerWG - 1 + Wr) + kQTile - 1) / kQTile;
-    const int nfull_h = max(0, t1 - max(t_full, t0));   // per query head
+    // PER_HEAD walks the tiles [r_lo, r_hi) (all of [t0, t1) outside range
+    // mode) once per query head
+    const int ntw = r_hi - r_lo;
+    const int nfull_h = PER_HEAD ? max(0, r_hi - max(t_full, r_lo))   // per query head
+                                 : max(0, t1 - max(t_full, t0));
     // step u -> (tile, query head of the group); the latest tiles come first
-    auto tile_of = [&](int u) { return PER_HEAD ? t1 - 1 - u % ntiles : t1 - 1 - u / g; };
-    auto head_of = [&](int u) { return PER_HEAD ? u / ntiles : u % g; };
-    auto is_full = [&](int u) { return PER_HEAD ? u % ntiles < nfull_h : u < nfull_h * g; };
+    auto tile_of = [&](int u) { return PER_HEAD ? r_hi - 1 - u % ntw : t1 - 1 - u / g; };
+    auto head_of = [&](int u) { return PER_HEAD ? u / ntw : u % g; };
+    auto is_full = [&](int u) { return PER_HEAD ? u % ntw < nfull_h : u < nfull_h * g; };
 
     // staging offsets (elements) inside a tile: chunk c of this thread is
     // off0 + c * pass_stride (the host guarantees kQTile * q_ss < 2^31)
@@ -181,14 +191,20 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     auto store_step = [&](int buf) {
 #pragma unroll
       for (int c = 0; c < CHUNKS; ++c) store16(&sq[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
-      if (tid < kQTile) sl[buf][tid] = lst * kLog2e;
+      if (tid < kQTile) {
+        // the slot's address is formed here from the thread index (an opaque
+        // copy, so that it is not hoisted out of the loop into a spilled register)
+        int t = tid;
+        asm volatile("" : "+v"(t));
+        sl[buf][t] = lst * kLog2e;
+      }
     };
 
     // this workgroup's share of the key block's steps: its range's tiles, or
     // an even share of all steps
     int u_begin = PER_HEAD ? 0 : (int)((int64_t)nsteps * split / p.nsplit);
-    int u_end = PER_HEAD ? nsteps : (int)((int64_t)nsteps * (split + 1) / p.nsplit);
-    if (rtiles > 0) {
+    int u_end = PER_HEAD ? max(0, ntw) * g : (int)((int64_t)nsteps * (split + 1) / p.nsplit);
+    if (!PER_HEAD && rtiles > 0) {
       u_begin = r_lo < r_hi ? (t1 - r_hi) * g : 0;
       u_end = r_lo < r_hi ? (t1 - r_lo) * g : 0;
     }
@@ -238,8 +254,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         mid[0] = 0.f;
         mid[1] = 0.f;
       }
-      if (PER_HEAD && u % ntiles == ntiles - 1) {  // this query head is complete
-        write_cols(p.mass_q + ((int64_t)b * p.Hq + h * g + head_of(u)) * p.S);
+      if (PER_HEAD && u % ntw == ntw - 1) {  // this query head is complete
+        write_cols(head_dst(head_of(u)));
         top[0] = top[1] = mid[0] = mid[1] = 0.f;
       }
       if (more) store_step((u + 1) & 1);
@@ -250,8 +266,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   if (!PER_HEAD) {
     write_cols(p.nsplit > 1 ? p.part + ((int64_t)split * nbh + bh) * p.S
                             : p.mass + ((int64_t)b * p.Hkv + h) * p.S);
-  } else if (i_first >= p.Sq) {  // no future query: every head's mass is 0
-    for (int gi = 0; gi < p.g; ++gi) write_cols(p.mass_q + ((int64_t)b * p.Hq + h * p.g + gi) * p.S);
+  } else if (i_first >= p.Sq || r_lo >= r_hi) {  // no future query here: every head's part is 0
+    for (int gi = 0; gi < p.g; ++gi) write_cols(head_dst(gi));
   }
 }
 
@@ -269,19 +285,20 @@ __global__ __launch_bounds__(kThreads) void mass_reduce_kernel(const float* part
 template <int D, typename T>
 hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   const int nkb = (a.S + kKeysPerWG - 1) / kKeysPerWG;
-  const int nsplit = a.mass_q ? 1 : a.nsplit;
+  const bool per_head = a.mass_q != nullptr;
+  // per-query-head mass splits only in range mode
+  const int nsplit = per_head && a.range_tiles == 0 ? 1 : a.nsplit;
   const int64_t grid = (int64_t)nkb * nsplit * a.B * a.Hkv;
   if (grid > 0x7fffffff) return hipErrorInvalidConfiguration;
-  if (a.mass_q) {
+  if (per_head)
     hipLaunchKernelGGL((mass_kernel<D, T, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  } else {
+  else
     hipLaunchKernelGGL((mass_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-    if (nsplit > 1) {
-      const int64_t n = (int64_t)a.B * a.Hkv * a.S;
-      const int64_t blocks = (n + kThreads - 1) / kThreads;
-      hipLaunchKernelGGL(mass_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
-                         dim3(kThreads), 0, s, a.part, a.mass, n, nsplit);
-    }
+  if (nsplit > 1) {
+    const int64_t n = (int64_t)a.B * (per_head ? a.Hq : a.Hkv) * a.S;
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(mass_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                       dim3(kThreads), 0, s, a.part, per_head ? a.mass_q : a.mass, n, nsplit);
   }
   return hipGetLastError();
 }

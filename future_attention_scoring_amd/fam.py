@@ -35,7 +35,8 @@ _SIGNATURES = {
     "fam_mass_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fam_compute_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i, _i]),
     "fam_mass_per_head": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
-                               _i64, _i, _f, _p, _p]),
+                               _i64, _i, _f, _p, _p, ctypes.c_size_t, _p]),
+    "fam_mass_per_head_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
     "fam_kvpop_target": (_i, [_p, _i, _i, _i, _i, _i, _f, _i, _p, _p]),
     "fam_compute": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
                          _i, _f, _p, _p, _p, ctypes.c_size_t, _p]),
@@ -216,18 +217,32 @@ def fam_mass(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
     return mass if q.dim() == 4 else mass[0]
 
 
+def fam_mass_per_head_workspace_size(B: int, Hq: int, Hkv: int, S: int) -> int:
+    return int(load().fam_mass_per_head_workspace_size(int(B), int(Hq), int(Hkv), int(S)))
+
+
 def fam_mass_per_head(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
-                      scale: Optional[float] = None, mass_q: Optional[torch.Tensor] = None
-                      ) -> torch.Tensor:
+                      scale: Optional[float] = None, mass_q: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Per-query-head mass [B, Hq, S]. Without a workspace one of
+    fam_mass_per_head_workspace_size bytes is allocated (none below 65536
+    keys); an empty one runs the pass unsplit."""
     q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
     lse = lse.contiguous()
     if lse.numel() != B * Hq * S or lse.dtype != torch.float32:
         raise FamError(1, "lse must be fp32 [B, Hq, S]")
     if mass_q is None:
         mass_q = torch.empty((B, Hq, S), dtype=torch.float32, device=q4.device)
+    if workspace is not None:
+        ws, nbytes = workspace.data_ptr(), workspace.numel() * workspace.element_size()
+    else:
+        nbytes = fam_mass_per_head_workspace_size(B, Hq, Hkv, S)
+        # freed on return: torch's allocator reuses it only in stream order
+        wt = torch.empty(nbytes, dtype=torch.uint8, device=q4.device) if nbytes else None
+        ws = wt.data_ptr() if nbytes else None
     _check(load().fam_mass_per_head(q4.data_ptr(), k4.data_ptr(), lse.data_ptr(), _dtype_code(q4),
                                     B, Hq, Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
-                                    0.0 if scale is None else scale, mass_q.data_ptr(),
+                                    0.0 if scale is None else scale, mass_q.data_ptr(), ws, nbytes,
                                     _stream(q4)))
     return mass_q if q.dim() == 4 else mass_q[0]
 

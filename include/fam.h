@@ -170,13 +170,27 @@ size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S);
  * j > S - 1 - W get exactly 0.
  *
  *   mass_q  device out, [B, Hq, S] fp32, contiguous, fully overwritten
+ *   workspace, workspace_bytes
+ *           optional device scratch (16-byte aligned, owned by the caller,
+ *           contents irrelevant on entry and unspecified on return). With
+ *           fam_mass_per_head_workspace_size(B, Hq, Hkv, S) bytes (non-zero
+ *           from 65536 keys on), every range of 4096 query rows gets its own
+ *           workgroup per key block, as in fam_mass, and a second launch
+ *           adds the ranges' parts in a fixed order (same result up to fp32
+ *           rounding; deterministic). NULL or fewer bytes: no split. Calls
+ *           sharing a workspace must be ordered on one stream.
  *   other arguments, requirements and errors as for fam_mass.
  * ---------------------------------------------------------------------- */
 fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype,
                              int B, int Hq, int Hkv, int S, int d,
                              int64_t q_sb, int64_t q_sh, int64_t q_ss,
                              int64_t k_sb, int64_t k_sh, int64_t k_ss,
-                             int W, float scale, float* mass_q, void* stream);
+                             int W, float scale, float* mass_q,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of workspace fam_mass_per_head uses for these sizes: ranges * B * Hq
+ * * S floats (0 when it does not split, or for invalid sizes). */
+size_t fam_mass_per_head_workspace_size(int B, int Hq, int Hkv, int S);
 
 /* ------------------------------------------------------------------------
  * fam_kvpop_target -- KVpop's supervision target from per-head mass.

@@ -115,7 +115,7 @@ def test_kvpop_target_validation():
 
 def test_mass_per_head_validation():
     lib = fam.load()
-    args = [FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE, None]
+    args = [FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, 0.0, FAKE, None, 0, None]
     bad = list(args); bad[17] = None
     assert lib.fam_mass_per_head(*bad) == INVALID
     bad = list(args); bad[15] = -1
@@ -124,6 +124,21 @@ def test_mass_per_head_validation():
     assert lib.fam_mass_per_head(*bad) == INVALID
     bad = list(args); bad[8] = 96
     assert lib.fam_mass_per_head(*bad) == UNSUPPORTED
+    bad = list(args); bad[18] = FAKE + 8; bad[19] = 1 << 20          # misaligned workspace
+    assert lib.fam_mass_per_head(*bad) == INVALID
+
+
+def test_mass_per_head_workspace_size():
+    """One [B, Hq, S] fp32 slice per range of 64 query tiles of 64 rows from
+    65536 keys on (at most 128 ranges); no split below."""
+    lib = fam.load()
+    assert lib.fam_mass_per_head_workspace_size(1, 32, 8, 131072) == 32 * 32 * 131072 * 4
+    assert lib.fam_mass_per_head_workspace_size(1, 8, 2, 65613) == 17 * 8 * 65613 * 4
+    assert lib.fam_mass_per_head_workspace_size(1, 32, 8, 65535) == 0
+    assert lib.fam_mass_per_head_workspace_size(1, 32, 8, 8192) == 0
+    assert lib.fam_mass_per_head_workspace_size(1, 32, 8, 1 << 20) == 0
+    for bad in ((0, 4, 2, 70000), (1, 3, 2, 70000), (1, 4, 2, 0)):
+        assert lib.fam_mass_per_head_workspace_size(*bad) == 0
 
 
 def test_fam_mass_and_compute_validation():

@@ -158,6 +158,35 @@ def test_counts_floor_at_one_on_gpu():
     np.testing.assert_allclose(got, ref, rtol=0, atol=1e-6)
 
 
+@pytest.mark.parametrize("seed,B,Hq,Hkv,S,d,W", [(61, 1, 8, 2, 65613, 128, 300), (62, 2, 4, 1, 70000, 64, 0)])
+def test_per_head_ranges_match_unsplit(seed, B, Hq, Hkv, S, d, W):
+    """From 65536 keys on, with fam_mass_per_head_workspace_size bytes, each
+    range of 4096 query rows gets its own workgroup per key block and the
+    parts are added per query head. Against the unsplit pass (an empty
+    workspace): equal to fp32 rounding, exactly 0 on the same keys; the
+    group sum equals fam_mass; at W = 0 every query head's mass sums to S."""
+    say(f"per-head ranges seed={seed} B={B} Hq={Hq} Hkv={Hkv} S={S} d={d} W={W}")
+    nr = -(-(-(-S // 64)) // 64)
+    assert fam.fam_mass_per_head_workspace_size(B, Hq, Hkv, S) == nr * B * Hq * S * 4
+    gen = torch.Generator(device=DEV).manual_seed(seed)
+    qd = torch.randn(B, Hq, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    kd = torch.randn(B, Hkv, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    lse = fam.fam_lse(qd, kd, knorm=fam.fam_key_norms(kd))
+    ranged = fam.fam_mass_per_head(qd, kd, lse, W)
+    whole = fam.fam_mass_per_head(qd, kd, lse, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    pos = whole > 0
+    assert torch.all(whole[..., S - W:] == 0)
+    assert torch.equal(ranged[~pos], whole[~pos])
+    assert ((ranged - whole).abs()[pos] / whole[pos]).max().item() <= 1e-5
+    mass = fam.fam_mass(qd, kd, lse, W)
+    summed = ranged.view(B, Hkv, Hq // Hkv, S).double().sum(2)
+    gpos = mass.double() > 0
+    assert torch.all(summed[~gpos] == 0)
+    assert ((summed - mass.double()).abs()[gpos] / mass.double()[gpos]).max().item() <= 1e-5
+    if W == 0:
+        np.testing.assert_allclose(ranged.double().sum(dim=-1).cpu().numpy(), np.full((B, Hq), S), rtol=1e-4)
+
+
 def test_llama_128k_per_head_tail_keys():
     """At full size: every per-head mass sums to the group mass, and the
     per-head masses of the keys whose future queries lie in the last rows
