@@ -468,8 +468,8 @@ def main():
     wall = time.perf_counter() - t0
 
     names = ["fam_lse", "fam_mass", "evict_select", "kv_compact"]
-    ms = {n: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
-          for j, n in enumerate(names)}
+    per_step = {n: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j, n in enumerate(names)}
+    ms = {n: float(np.mean(v)) for n, v in per_step.items()}
     work = algorithmic_work(wl, total)
     ms_step = wall * 1e3 / args.steps
     t_fam = (ms["fam_lse"] + ms["fam_mass"]) * 1e-3
@@ -509,6 +509,8 @@ def main():
         "evict_compact_gbps": round((work["select_bytes"] + work["compact_bytes"]) / t_ec / 1e9, 2),
         "evict_compact_hbm_frac": round((work["select_bytes"] + work["compact_bytes"]) / t_ec / PEAK_HBM_BYTES, 4),
         "kernel_ms": {n: round(ms[n], 4) for n in names},
+        "kernel_ms_median": {n: round(float(np.median(per_step[n])), 4) for n in names},
+        "kernel_ms_min": {n: round(float(np.min(per_step[n])), 4) for n in names},
         "roofline": dict(roof[dominant], kernel=dominant),
         "roofline_all": roof,
     }

@@ -17,9 +17,8 @@
 //     one key and the column sum over queries stays inside a lane (the two
 //     half-waves hold disjoint query rows and are added once at the end).
 //   * The workgroup walks the 64-row query tiles i >= j0 + W of every query
-//     head of the group, latest tile first, so the workgroups of one head that
-//     run at the same time read the same Q tiles (the L2 absorbs most of the
-//     re-reads). Each (tile, head) step stages 64 query rows and their
+//     head of the group, latest tile first. Each (tile, head) step stages 64
+//     query rows and their
 //     normalisers (in base-2 units) through double-buffered LDS; the tile
 //     base is a uniform pointer and a thread's chunks sit at one 32-bit
 //     offset plus multiples of a uniform stride (no per-chunk registers).
@@ -35,6 +34,13 @@
 //     chip, so the host may split each key block's steps over nsplit
 //     workgroups; their partial sums go to a caller workspace and a second
 //     launch adds them in split order (deterministic).
+//   * Long sequences split by ranges of query rows instead: split s of every
+//     key block takes the tiles [s * R, (s + 1) * R) and the workgroups run
+//     range-major, latest range first. Workgroups at different key positions
+//     would otherwise stream different query tiles at the same time, and the
+//     caches would not hold them; within a range they share a few MB of Q.
+//     The per-query-head mode splits the same way, one partial slice per
+//     query head.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 

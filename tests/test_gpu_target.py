@@ -174,6 +174,10 @@ def test_per_head_ranges_match_unsplit(seed, B, Hq, Hkv, S, d, W):
     lse = fam.fam_lse(qd, kd, knorm=fam.fam_key_norms(kd))
     ranged = fam.fam_mass_per_head(qd, kd, lse, W)
     whole = fam.fam_mass_per_head(qd, kd, lse, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    # a workspace one slice short of the ranges runs the unsplit pass
+    short = fam.fam_mass_per_head(qd, kd, lse, W,
+                                  workspace=torch.empty((nr - 1) * B * Hq * S * 4, dtype=torch.uint8, device=DEV))
+    assert torch.equal(short, whole)
     pos = whole > 0
     assert torch.all(whole[..., S - W:] == 0)
     assert torch.equal(ranged[~pos], whole[~pos])
