@@ -152,7 +152,8 @@ size_t lse_split_bytes(const ScoreShape& s, int nks) {
 fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
 
 // Partial slices of the group-sum mass pass. From kMassRangeMinS keys on
-// (and while at most kMassMaxRanges ranges cover the query rows) split s owns
+// (while at most kMassMaxRanges ranges cover the query rows and the grid of
+// key blocks x ranges x B x Hkv workgroups fits one launch) split s owns
 // the query tiles [s * R, (s + 1) * R), R = kMassRangeTiles: the workgroups
 // resident together then read the same few MB of Q, which stay in cache,
 // instead of each re-reading its own share from HBM. Shorter sequences
@@ -165,7 +166,9 @@ MassPlan mass_plan(const ScoreShape& s) {
   if (s.S >= fam::kMassRangeMinS) {
     const int64_t nt = ((int64_t)s.rows() + fam::kMassQTile - 1) / fam::kMassQTile;
     const int64_t nr = (nt + fam::kMassRangeTiles - 1) / fam::kMassRangeTiles;
-    if (nr > 1 && nr <= fam::kMassMaxRanges) return {(int)nr, fam::kMassRangeTiles};
+    const int64_t nkb = ((int64_t)s.S + fam::kMassKeysPerWG - 1) / fam::kMassKeysPerWG;
+    if (nr > 1 && nr <= fam::kMassMaxRanges && nkb * nr * s.B * s.Hkv <= 0x7fffffff)
+      return {(int)nr, fam::kMassRangeTiles};
   }
   return {mass_splits(s.B, s.Hkv, s.S), 0};
 }

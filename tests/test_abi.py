@@ -162,6 +162,9 @@ def test_mass_workspace_size():
     assert lib.fam_mass_workspace_size(2, 4, 1, 524288) == 128 * 2 * 524288 * 4    # the most ranges
     # beyond 128 ranges: 1M keys fill the chip unsplit
     assert lib.fam_mass_workspace_size(1, 32, 8, 1 << 20) == 0
+    # ranges only while 2048 key blocks x 128 ranges x B x Hkv workgroups fit one launch
+    assert lib.fam_mass_workspace_size(1023, 8, 8, 524288) == 128 * 1023 * 8 * 524288 * 4
+    assert lib.fam_mass_workspace_size(1024, 8, 8, 524288) == 0
     n8k = lib.fam_mass_workspace_size(1, 32, 8, 8192)
     assert n8k > 0 and n8k % (8 * 8192 * 4) == 0 and n8k // (8 * 8192 * 4) <= 16
     assert lib.fam_mass_workspace_size(1, 3, 2, 100) == 0                # Hq % Hkv != 0
