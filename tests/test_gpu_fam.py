@@ -237,6 +237,34 @@ def test_range_mass_matches_even_splits_and_unsplit(seed, B, Hq, Hkv, S, d, W):
         np.testing.assert_allclose(tot, np.full((B, Hkv), S * (Hq // Hkv)), rtol=1e-4)
 
 
+@pytest.mark.parametrize("W", [65536, 100000, 65535])
+def test_range_mass_window_edges(W):
+    """Ranges of query rows with a window that leaves no future query (W >= S:
+    every mass is exactly 0) or one (W = S - 1: only key 0, from the last
+    query, in the last range), against the unsplit pass and the oracle's
+    value for the one key."""
+    B, Hq, Hkv, S, d = 1, 4, 2, 65536, 128
+    say(f"range mass window edge S={S} W={W}")
+    gen = torch.Generator(device=DEV).manual_seed(W)
+    q = torch.randn(B, Hq, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    k = torch.randn(B, Hkv, S, d, device=DEV, generator=gen).to(torch.bfloat16)
+    lse = fam.fam_lse(q, k, knorm=fam.fam_key_norms(k))
+    ranged = fam.fam_mass(q, k, lse, W)
+    whole = fam.fam_mass(q, k, lse, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    if W >= S:
+        assert torch.all(ranged == 0) and torch.all(whole == 0)
+        return
+    assert torch.all(ranged[..., 1:] == 0) and torch.all(whole[..., 1:] == 0)
+    g, scale = Hq // Hkv, 1.0 / math.sqrt(d)
+    for h in range(Hkv):
+        qg = to64(q[0, h * g:(h + 1) * g])
+        kh = to64(k[0, h])
+        lse_tail = np.stack([fo.causal_lse_rows(qg[n], kh, np.array([S - 1]), scale) for n in range(g)])
+        ref = fo.future_mass_keys(qg, kh, lse_tail, S - 1, np.array([0]), W, scale)[0]
+        for got in (ranged, whole):
+            assert abs(got[0, h, 0].item() - ref) <= MASS_RTOL * ref
+
+
 @pytest.mark.parametrize("Sq,Sk,W", [(8256, 70000, 0), (12288, 65536, 200)])
 def test_range_mass_of_a_chunk(Sq, Sk, W):
     """A chunk of Sq >= 4096 queries over Sk >= 65536 cache rows runs the mass
