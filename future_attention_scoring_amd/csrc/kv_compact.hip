@@ -60,19 +60,30 @@ __global__ __launch_bounds__(kThreads) void compact_kernel(CompactArgs p) {
   }
   int h = lo;
 
-  u32x4_t kv[PASSES], vv[PASSES];
+  // the head of every row first; then all loads of the thread in flight at
+  // once, unconditional (a row without a valid source reads row 0 of its
+  // head and is written as zeros), so that no load waits for another
+  int hs[PASSES];
+  bool ok[PASSES];
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
     const int64_t r = rfirst + (int64_t)i * ROWS_PER_PASS;
-    kv[i] = zero16();
-    vv[i] = zero16();
-    if (r < rend) {
+    if (r < rend)
       while (h + 1 < p.H && r >= (lds_heads ? offs[h + 1] : p.offsets[h + 1])) ++h;
-      if (src[i] >= 0 && src[i] < p.S) {
-        kv[i] = load16_nt(p.k + h * p.k_sh + (int64_t)src[i] * p.k_ss + ch * 8);
-        vv[i] = load16_nt(p.v + h * p.v_sh + (int64_t)src[i] * p.v_ss + ch * 8);
-      }
-    }
+    hs[i] = h;
+    ok[i] = r < rend && src[i] >= 0 && src[i] < p.S;
+  }
+  u32x4_t kv[PASSES], vv[PASSES];
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    const int64_t row = ok[i] ? src[i] : 0;
+    kv[i] = load16_nt(p.k + hs[i] * p.k_sh + row * p.k_ss + ch * 8);
+    vv[i] = load16_nt(p.v + hs[i] * p.v_sh + row * p.v_ss + ch * 8);
+  }
+#pragma unroll
+  for (int i = 0; i < PASSES; ++i) {
+    kv[i] = ok[i] ? kv[i] : zero16();
+    vv[i] = ok[i] ? vv[i] : zero16();
   }
 #pragma unroll
   for (int i = 0; i < PASSES; ++i) {
