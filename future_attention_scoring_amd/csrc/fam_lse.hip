@@ -249,6 +249,9 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
         const int kb = t * kKeyTile + 32 * kk2;
         if (active && kb <= qp0 + 63 && kb < p.S) {
           f32x16_t acc0 = {}, acc1 = {};
+          // the wave's MFMA block at raised priority: its matrix work issues
+          // while the other waves of the SIMD are in their exp/sum phase
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
@@ -256,6 +259,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
             acc0 = Mma<T>::run(a, qf[0][ks], acc0);
             acc1 = Mma<T>::run(a, qf[1][ks], acc1);
           }
+          __builtin_amdgcn_s_setprio(0);
           bound_update(acc0, kb, qp0, p.S, lane, p.c, M[0], l[0]);
           bound_update(acc1, kb, qp0 + 32, p.S, lane, p.c, M[1], l[1]);
         }
