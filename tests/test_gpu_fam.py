@@ -237,6 +237,37 @@ def test_range_mass_matches_even_splits_and_unsplit(seed, B, Hq, Hkv, S, d, W):
         np.testing.assert_allclose(tot, np.full((B, Hkv), S * (Hq // Hkv)), rtol=1e-4)
 
 
+@pytest.mark.parametrize("dtype,strided", [(torch.float16, False), (torch.bfloat16, True)])
+def test_range_mass_fp16_and_strided_views(dtype, strided):
+    """Ranges of query rows on fp16 inputs, and on bf16 views whose rows sit
+    in wider buffers (row stride 2d, the head dim contiguous) with the head
+    and batch strides of a transposed [B, S, H, 2d] layout: equal to the
+    unsplit pass to fp32 rounding, the same zeros, and the group sum of the
+    per-query-head ranges equal to fam_mass."""
+    B, Hq, Hkv, S, d, W = 1, 4, 2, 65600, 128, 64
+    say(f"range mass {dtype} strided={strided} S={S}")
+    gen = torch.Generator(device=DEV).manual_seed(77)
+    if strided:
+        qb = torch.randn(B, S, Hq, 2 * d, device=DEV, generator=gen).to(dtype)
+        kb = torch.randn(B, S, Hkv, 2 * d, device=DEV, generator=gen).to(dtype)
+        q = qb[..., :d].permute(0, 2, 1, 3)   # [B, Hq, S, d] view, row stride Hq * 2d
+        k = kb[..., d:].permute(0, 2, 1, 3)
+        assert not q.is_contiguous() and q.stride(3) == 1
+    else:
+        q = torch.randn(B, Hq, S, d, device=DEV, generator=gen).to(dtype)
+        k = torch.randn(B, Hkv, S, d, device=DEV, generator=gen).to(dtype)
+    lse = fam.fam_lse(q, k, knorm=fam.fam_key_norms(k))
+    ranged = fam.fam_mass(q, k, lse, W)
+    whole = fam.fam_mass(q, k, lse, W, workspace=torch.empty(0, dtype=torch.uint8, device=DEV))
+    pos = whole > 0
+    assert torch.equal(ranged[~pos], whole[~pos])
+    assert ((ranged - whole).abs()[pos] / whole[pos]).max().item() <= 1e-5
+    per_head = fam.fam_mass_per_head(q, k, lse, W)
+    summed = per_head.view(B, Hkv, Hq // Hkv, S).double().sum(2)
+    assert torch.all(summed[~pos] == 0)
+    assert ((summed - whole.double()).abs()[pos] / whole.double()[pos]).max().item() <= 1e-5
+
+
 @pytest.mark.parametrize("W", [65536, 100000, 65535])
 def test_range_mass_window_edges(W):
     """Ranges of query rows with a window that leaves no future query (W >= S:
