@@ -328,7 +328,7 @@ __device__ uint64_t pick_threshold(int n, int need, F fetch, uint32_t* hist, int
 }
 
 // ---------------------------------------------------------------- launch 1
-__global__ __launch_bounds__(kThreads) void sel_hist(SelectArgs p) {
+__device__ __forceinline__ void hist_phase(const SelectArgs& p) {
   __shared__ uint32_t hist[kBins];
   __shared__ int sh[8];
   int w, hl;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(kThreads) void sel_hist(SelectArgs p) {
 }
 
 // ---------------------------------------------------------------- launch 2
-__global__ __launch_bounds__(kThreads) void sel_collect(SelectArgs p) {
+__device__ __forceinline__ void collect_phase(const SelectArgs& p) {
   __shared__ uint32_t hist[kBins];     // level-2 histogram, then bucket cursors
   __shared__ uint32_t cum[kBins + 1];  // the head's level-1 cumulative counts
   __shared__ int sh[8];
@@ -427,7 +427,7 @@ __global__ __launch_bounds__(kThreads) void sel_collect(SelectArgs p) {
 }
 
 // ---------------------------------------------------------------- launch 3
-__global__ __launch_bounds__(kThreads) void sel_scatter(SelectArgs p) {
+__device__ __forceinline__ void scatter_phase(const SelectArgs& p) {
   __shared__ uint32_t hist[kRadixBins];
   __shared__ uint32_t cum[kBins + 1];
   __shared__ uint64_t lst[kLdsList];
@@ -574,6 +574,21 @@ __global__ __launch_bounds__(kThreads) void sel_scatter(SelectArgs p) {
   }
 }
 
+__global__ __launch_bounds__(kThreads) void sel_hist(SelectArgs p) { hist_phase(p); }
+__global__ __launch_bounds__(kThreads) void sel_collect(SelectArgs p) { collect_phase(p); }
+__global__ __launch_bounds__(kThreads) void sel_scatter(SelectArgs p) { scatter_phase(p); }
+
+// One chunk a head: every phase reads only what its own workgroup wrote in
+// the phase before, so the three run in one launch, separated by barriers
+// (which also make the workgroup's global writes visible to all its threads).
+__global__ __launch_bounds__(kThreads) void sel_one(SelectArgs p) {
+  hist_phase(p);
+  __syncthreads();
+  collect_phase(p);
+  __syncthreads();
+  scatter_phase(p);
+}
+
 }  // namespace
 
 size_t select_workspace_bytes(int slots, int nchunk) { return ws_bytes(slots, nchunk); }
@@ -586,11 +601,15 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   bool all_trivial = true;
   for (int i = 0; i < a.nheads; ++i)
     if (a.n_choose[i] != 0 && a.n_choose[i] != a.c1 - a.c0) all_trivial = false;
-  if (!all_trivial) {
+  if (all_trivial) {
+    hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
+  } else if (a.nchunk == 1) {   // every head one chunk: one launch
+    hipLaunchKernelGGL(sel_one, grid, dim3(kThreads), 0, s, a);
+  } else {
     hipLaunchKernelGGL(sel_hist, grid, dim3(kThreads), 0, s, a);
     hipLaunchKernelGGL(sel_collect, grid, dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
   }
-  hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
