@@ -18,10 +18,10 @@
 //     half-waves hold disjoint query rows and are added once at the end).
 //   * The workgroup walks the 64-row query tiles i >= j0 + W of every query
 //     head of the group, latest tile first. Each (tile, head) step stages 64
-//     query rows and their
-//     normalisers (in base-2 units) through double-buffered LDS; the tile
-//     base is a uniform pointer and a thread's chunks sit at one 32-bit
-//     offset plus multiples of a uniform stride (no per-chunk registers).
+//     query rows and their normalisers (in base-2 units) through
+//     double-buffered LDS; the tile base is a uniform pointer and a thread's
+//     chunks sit at one 32-bit offset plus multiples of a uniform stride (no
+//     per-chunk registers).
 //   * Only band steps (those that contain some i < j + W) evaluate the window
 //     predicate. Keys that no query can reach (j > S - 1 - W) get exactly 0.
 //   * Per-step partial sums are added into a mid-level accumulator that is
