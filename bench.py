@@ -297,7 +297,8 @@ def ranking_row(runs, mass, wl, stream):
                             "queries_per_s": round(H * S / (ms[3] * 1e-3), 1)},
         "fam_rank_order": {"bound": "latency", "bytes": rank_bytes,
                            "achieved": round(rank_bytes / (ms[0] * 1e-3) / 1e9, 3), "unit": "GB/s",
-                           "note": "four stable radix passes of three launches each (tile counts, per-head scan, place)"},
+                           "note": ("four stable radix passes; up to 64 tiles of 4096 a head (this row) each is two launches "
+                                    "(tile counts, place), beyond that three (counts, per-head scan, place)")},
         "recency_vs_mass": {"normalised_cost_mean": round(float(ratio.mean()), 6),
                             "retention_recall_mean_at_S_over_8": round(float(recall.mean()), 6)},
     }
