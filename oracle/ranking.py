@@ -18,7 +18,8 @@ Readings where the pages are silent: the budgets are every b = 0 .. n (keep
 the b best entries, evict the rest); the cost at a budget is the summed
 importance of the evicted entries; the area is the plain sum over budgets;
 normalising divides by the area of the ranking by importance itself (so 1 is
-optimal and larger is worse); rankings order by score descending with ties
+optimal and larger is worse), and is 1 when there is no importance to
+evict at all (both costs 0); rankings order by score descending with ties
 to the lower position, NaN last, -0.0 equal to +0.0 (as in selection); the
 recall divides the overlap by the size of the teacher's kept set.
 """
@@ -54,8 +55,18 @@ def eviction_cost(importance: np.ndarray, order: np.ndarray) -> np.ndarray:
 
 
 def normalized_cost(scores: np.ndarray, importance: np.ndarray) -> np.ndarray:
-    """Cost of ranking by ``scores`` over the cost of ranking by ``importance``."""
-    return eviction_cost(importance, rank_order(scores)) / eviction_cost(importance, rank_order(importance))
+    """Cost of ranking by ``scores`` over the cost of ranking by ``importance``.
+
+    Where the optimal cost is 0 and so is the ranking's cost (no importance
+    to evict at any budget), every ranking is optimal and the ratio is 1;
+    otherwise the ratio is the plain quotient.
+    """
+    c = eviction_cost(importance, rank_order(scores))
+    c_opt = eviction_cost(importance, rank_order(importance))
+    with np.errstate(divide="ignore", invalid="ignore"):
+        ratio = c / c_opt
+    ratio[(c == 0.0) & (c_opt == 0.0)] = 1.0
+    return ratio
 
 
 def retention_recall(kept_teacher, kept_other) -> float:

@@ -68,6 +68,20 @@ def test_uniform_importance_costs_the_same_under_every_order():
     for seed in range(4):
         s = np.random.default_rng(seed).standard_normal((1, n))
         assert rk.eviction_cost(imp, rk.rank_order(s))[0] == pytest.approx(u * n * (n + 1) / 2, rel=1e-14)
+        assert rk.normalized_cost(s, imp)[0] == pytest.approx(1.0, rel=1e-14)   # every order is optimal
+
+
+def test_normalised_cost_without_importance_is_one():
+    """No importance at all: both costs are 0 and the ratio is read as 1
+    (every ranking evicts nothing at every budget); one head with and one
+    without importance keep their own ratios."""
+    s = np.random.default_rng(5).standard_normal((2, 40))
+    imp = np.zeros((2, 40))
+    imp[1, 7] = 1.0                                     # head 1: one entry carries everything
+    r = rk.normalized_cost(s, imp)
+    assert r[0] == 1.0
+    pos = int(np.where(rk.rank_order(s[1:])[0] == 7)[0][0])
+    assert r[1] == pytest.approx((pos + 1) / 1.0, rel=1e-14)   # evicted at budgets 0 .. pos
 
 
 def test_rank_order_ties_nan_and_signed_zero():
