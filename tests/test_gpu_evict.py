@@ -128,9 +128,9 @@ def test_select_unaligned_row_stride():
     assert np.array_equal(idx.cpu().numpy(), ref_idx)
 
 
-@pytest.mark.parametrize("wl_name", ["tiny", "qwen3_4b", "llama_128k"])
+@pytest.mark.parametrize("wl_name", ["tiny", "qwen3_4b", "long_trace", "llama_128k"])
 def test_select_on_gpu_mass_and_compact(wl_name):
-    wl = {"tiny": workloads.tiny, "qwen3_4b": workloads.qwen3_4b_layer,
+    wl = {"tiny": workloads.tiny, "qwen3_4b": workloads.qwen3_4b_layer, "long_trace": workloads.long_trace,
           "llama_128k": workloads.llama31_8b_128k}[wl_name]()
     say(f"fam -> select -> compact {wl.name}")
     t = wl.tensors()

@@ -6,11 +6,11 @@ that no query can reach (j > S - 1 - W) must be exactly 0. The GPU reads bf16
 (or fp16) inputs and the oracle reads the same values converted exactly to
 fp64.
 
-Sizes the oracle finishes in seconds are compared element by element; at the
-32k and 128k workloads the oracle computes sampled rows and the keys whose
-future queries lie in the last rows, and properties that hold at any size
-(the W = 0 column-sum invariant, the uniform and single-sink closed forms)
-are checked on every output.
+Sizes the oracle finishes in seconds are compared element by element (the
+32k and 128k workloads against stored oracle results in
+tests/test_gpu_fullsize.py), and properties that hold at any size (the W = 0
+column-sum invariant, the uniform and single-sink closed forms) are checked
+on every output.
 """
 import math
 
@@ -128,47 +128,6 @@ def test_qwen3_4b_layer_two_groups_full_oracle():
         check_mass(mass[h:h + 1], mass_ref, wl.S, wl.W)
 
 
-def sampled_checks(wl, t, lse, mass, group, n_rows=24, tail=768):
-    """Oracle on sampled LSE rows and on the keys whose queries are all in the tail."""
-    g, S, W = wl.group, wl.S, wl.W
-    rng = np.random.default_rng(wl.seed)
-    qg = to64(t["q"][0, group * g:(group + 1) * g])
-    kh = to64(t["k"][0, group])
-    scale = 1.0 / math.sqrt(wl.d)
-    rows = np.unique(np.concatenate([rng.integers(0, S, n_rows), [0, 1, S - 1]]))
-    for n in range(g):
-        ref = fo.causal_lse_rows(qg[n], kh, rows, scale)
-        check_lse(lse[group * g + n, rows], ref)
-    tail_start = S - tail
-    lse_tail = np.stack([fo.causal_lse_rows(qg[n], kh, np.arange(tail_start, S), scale) for n in range(g)])
-    keys = np.arange(max(0, tail_start - W), S)
-    ref = fo.future_mass_keys(qg, kh, lse_tail, tail_start, keys, W, scale)
-    got = mass[group, keys]
-    full = np.zeros(S)
-    full[keys] = ref
-    gfull = np.zeros(S)
-    gfull[keys] = got
-    check_mass(gfull[None], full[None], S, W)
-
-
-def test_long_trace_sampled():
-    wl = workloads.long_trace()
-    say(wl.name)
-    t = wl.tensors(q_heads=range(wl.Hq), kv_heads=range(wl.Hkv), with_v=False)
-    lse, mass = fam.fam_compute(t["q"].to(DEV), t["k"].to(DEV), wl.W)
-    lse, mass = lse.cpu().numpy()[0], mass.cpu().numpy()[0]
-    sampled_checks(wl, t, lse, mass, group=3)
-
-
-def test_llama_128k_sampled():
-    wl = workloads.llama31_8b_128k()
-    say(wl.name)
-    t = wl.tensors(with_v=False)
-    lse, mass = fam.fam_compute(t["q"].to(DEV), t["k"].to(DEV), wl.W)
-    lse, mass = lse.cpu().numpy()[0], mass.cpu().numpy()[0]
-    sampled_checks(wl, t, lse, mass, group=5, n_rows=8, tail=640)
-
-
 @pytest.mark.parametrize("S,Hq,Hkv,d", [(8192, 32, 8, 128), (131072, 32, 8, 128), (5000, 6, 2, 64),
                                         (524288, 4, 1, 128)])
 def test_w0_invariant_full_size(S, Hq, Hkv, d):
@@ -179,7 +138,9 @@ def test_w0_invariant_full_size(S, Hq, Hkv, d):
     _, mass = fam.fam_compute(q, k, 0)
     tot = mass.double().sum(dim=-1).cpu().numpy()[0]
     g = Hq // Hkv
-    np.testing.assert_allclose(tot, np.full(Hkv, S * g), rtol=1e-4)
+    rel = np.abs(tot / (S * g) - 1.0).max()
+    print(f"W=0 column total: max rel err {rel:.2e}", flush=True)
+    np.testing.assert_allclose(tot, np.full(Hkv, S * g), rtol=1e-5)
 
 
 def harmonic_prefix(n):
