@@ -247,7 +247,8 @@ def ranking_row(runs, mass, wl, stream):
     fam_eviction_cost of both against the masses (KVP's cost over budgets and
     its normalised form), fam_retention_overlap of the two kept sets at a
     budget of S/8 (KVpop's top-k retention recall), and fam_topk_cutoff of the
-    mass order (KVpop's running cut-off, window W, k = S/8)."""
+    mass order (KVpop's running cut-off, the workload's sinks, window W,
+    k = S/8)."""
     m = mass[0]
     H, S = m.shape
     recency = torch.arange(S, dtype=torch.float32, device=m.device).expand(H, S).contiguous()
@@ -274,7 +275,7 @@ def ranking_row(runs, mass, wl, stream):
         common = fam.fam_retention_overlap(ia, oa, ib, ob, S)
         if e:
             e[3].record(stream)
-        fam.fam_topk_cutoff(order, wl.W, S // 8, tau=tau, workspace=cut_ws)
+        fam.fam_topk_cutoff(order, wl.sinks, wl.W, S // 8, tau=tau, workspace=cut_ws)
         if e:
             e[4].record(stream)
         return common
@@ -293,7 +294,7 @@ def ranking_row(runs, mass, wl, stream):
         "heads": H, "entries_per_head": S, "runs": runs,
         "ms": {"fam_rank_order": round(ms[0], 4), "fam_eviction_cost": round(ms[1], 4),
                "fam_retention_overlap": round(ms[2], 4), "fam_topk_cutoff": round(ms[3], 4)},
-        "fam_topk_cutoff": {"window": wl.W, "k": S // 8, "queries_per_head": S,
+        "fam_topk_cutoff": {"sinks": wl.sinks, "window": wl.W, "k": S // 8, "queries_per_head": S,
                             "queries_per_s": round(H * S / (ms[3] * 1e-3), 1)},
         "fam_rank_order": {"bound": "latency", "bytes": rank_bytes,
                            "achieved": round(rank_bytes / (ms[0] * 1e-3) / 1e9, 3), "unit": "GB/s",

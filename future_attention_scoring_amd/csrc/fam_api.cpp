@@ -1,5 +1,6 @@
 // C ABI of libfam.so: argument validation, the host-side budget plan and
-// kernel dispatch. Nothing here allocates device memory or synchronises.
+// kernel dispatch. Nothing here allocates device memory; nothing synchronises
+// except the FAM_SYNC_CHECK debug switch and kv_compact_inplace_status.
 #include "fam.h"
 
 #include <hip/hip_runtime.h>
@@ -8,6 +9,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <string>
 #include <vector>
 
@@ -35,6 +37,24 @@ fam_status ok() {
 fam_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
   return fail(FAM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// FAM_SYNC_CHECK (debug switch, read on every call): set to anything but
+// "" or "0", every device entry point synchronises its stream after its
+// launches, so that a fault in the work it enqueued is reported by that call.
+bool sync_check() {
+  const char* v = std::getenv("FAM_SYNC_CHECK");
+  return v && v[0] && !(v[0] == '0' && v[1] == 0);
+}
+
+// The status of a call whose launches returned e: under FAM_SYNC_CHECK also
+// the outcome of the enqueued work.
+fam_status launched(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess || !sync_check()) return hip_status(e, what);
+  e = hipStreamSynchronize(s);
+  if (e == hipSuccess) e = hipGetLastError();
+  if (e != hipSuccess) return fail(FAM_ERR_HIP, "%s (sync check): %s", what, hipGetErrorString(e));
+  return ok();
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -199,7 +219,7 @@ fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype 
     fam::MassArgs a = mass_args(q, k, lse, s, W, scale, mass, nullptr, static_cast<float*>(workspace),
                                 plan.nsplit);
     a.range_tiles = plan.range_tiles;
-    return hip_status(fam::launch_mass(a, elem_of(dtype), stream), what);
+    return launched(fam::launch_mass(a, elem_of(dtype), stream), stream, what);
   }
   // even shares, as many as wanted and as the workspace holds
   int nsplit = mass_splits(s.B, s.Hkv, s.S);
@@ -208,7 +228,7 @@ fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype 
   if (nsplit < 2) nsplit = 1;
   const fam::MassArgs a = mass_args(q, k, lse, s, W, scale, mass, nullptr,
                                     nsplit > 1 ? static_cast<float*>(workspace) : nullptr, nsplit);
-  return hip_status(fam::launch_mass(a, elem_of(dtype), stream), what);
+  return launched(fam::launch_mass(a, elem_of(dtype), stream), stream, what);
 }
 
 // Key norms, the bounded first pass and the group-sum mass pass. The
@@ -265,6 +285,7 @@ const char* fam_status_string(fam_status st) {
     case FAM_ERR_UNSUPPORTED: return "FAM_ERR_UNSUPPORTED";
     case FAM_ERR_WORKSPACE: return "FAM_ERR_WORKSPACE";
     case FAM_ERR_HIP: return "FAM_ERR_HIP";
+    case FAM_ERR_TIMEOUT: return "FAM_ERR_TIMEOUT";
   }
   return "FAM_ERR_UNKNOWN";
 }
@@ -280,7 +301,7 @@ fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, 
   if (st != FAM_OK) return st;
   if (!knorm) return fail(FAM_ERR_INVALID_ARG, "knorm must be non-null");
   const fam::LseArgs a = lse_args(k, k, s, 0.f, nullptr, knorm);
-  return hip_status(fam::launch_knorm(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
+  return launched(fam::launch_knorm(a, elem_of(dtype), static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
                     "fam_key_norms launch");
 }
 
@@ -293,7 +314,7 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq,
   if (!lse) return fail(FAM_ERR_INVALID_ARG, "lse must be non-null");
   if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
   const fam::LseArgs a = lse_args(q, k, s, scale, lse, const_cast<float*>(knorm));
-  return hip_status(fam::launch_lse(a, elem_of(dtype), static_cast<hipStream_t>(stream)), "fam_lse launch");
+  return launched(fam::launch_lse(a, elem_of(dtype), static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "fam_lse launch");
 }
 
 size_t fam_mass_workspace_size(int B, int Hq, int Hkv, int S) {
@@ -343,7 +364,7 @@ fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam
     a.nsplit = plan.nsplit;
     a.range_tiles = plan.range_tiles;
   }
-  return hip_status(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)),
+  return launched(fam::launch_mass(a, elem_of(dtype), static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
                     "fam_mass_per_head launch");
 }
 
@@ -367,7 +388,7 @@ fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, 
   if ((reinterpret_cast<uintptr_t>(mass_q) | reinterpret_cast<uintptr_t>(target)) & 3u)
     return fail(FAM_ERR_INVALID_ARG, "mass_q and target must be 4-byte aligned");
   const fam::TargetArgs a{mass_q, target, B, Hq, Hkv, S, W, eps, aggregate == FAM_AGG_MEAN ? 1 : 0};
-  return hip_status(fam::launch_target(a, static_cast<hipStream_t>(stream)), "fam_kvpop_target launch");
+  return launched(fam::launch_target(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "fam_kvpop_target launch");
 }
 
 fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
@@ -500,7 +521,7 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
     const hipError_t e = fam::launch_select(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_status(e, "evict_select launch");
   }
-  return ok();
+  return launched(hipSuccess, static_cast<hipStream_t>(stream), "evict_select launch");
 }
 
 fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S, int d,
@@ -523,7 +544,7 @@ fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S
   fam::CompactArgs a{static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), k_sh, k_ss,
                      v_sh, v_ss, idx, offsets_dev, total_rows, static_cast<uint16_t*>(k_new),
                      static_cast<uint16_t*>(v_new), H, S, d};
-  return hip_status(fam::launch_compact(a, static_cast<hipStream_t>(stream)), "kv_compact launch");
+  return launched(fam::launch_compact(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "kv_compact launch");
 }
 
 
@@ -562,7 +583,7 @@ fam_status kv_append(const void* k_src, const void* v_src, int elem_bytes, int H
   a.pos = pos;
   a.pos_sh = pos_sh;
   a.H = H, a.n = n, a.d = d, a.row0 = row0, a.pos0 = pos0;
-  return hip_status(fam::launch_append(a, static_cast<hipStream_t>(stream)), "kv_append launch");
+  return launched(fam::launch_append(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "kv_append launch");
 }
 
 fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, int d, int64_t k_sh,
@@ -602,8 +623,31 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
   a.total = total_rows;
   a.H = H, a.S = S, a.d = d;
   a.ws = static_cast<uint32_t*>(workspace);
-  return hip_status(fam::launch_compact_inplace(a, static_cast<hipStream_t>(stream)),
-                    "kv_compact_inplace launch");
+  a.spin_limit = fam::kInplaceSpinLimit;
+  if (const char* lim = std::getenv("FAM_INPLACE_SPIN_LIMIT")) {   // test and debug switch
+    const long v = std::strtol(lim, nullptr, 10);
+    if (v >= 0 && v < fam::kInplaceSpinLimit) a.spin_limit = (int)v;
+  }
+  const fam_status rc = launched(fam::launch_compact_inplace(a, static_cast<hipStream_t>(stream)),
+                                 static_cast<hipStream_t>(stream), "kv_compact_inplace launch");
+  if (rc != FAM_OK || !sync_check()) return rc;
+  return kv_compact_inplace_status(workspace, stream);
+}
+
+fam_status kv_compact_inplace_status(const void* workspace, void* stream) {
+  if (!workspace) return fail(FAM_ERR_INVALID_ARG, "workspace must be non-null");
+  if (reinterpret_cast<uintptr_t>(workspace) & 3u)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 4-byte aligned");
+  uint32_t word = 0;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(&word, static_cast<const uint32_t*>(workspace) + fam::kInplaceErrorWord,
+                                sizeof word, hipMemcpyDeviceToHost, hs);
+  if (e == hipSuccess) e = hipStreamSynchronize(hs);
+  if (e != hipSuccess) return hip_status(e, "kv_compact_inplace_status");
+  if (word != 0u)
+    return fail(FAM_ERR_TIMEOUT, "kv_compact_inplace: %u chunk(s) gave up waiting for earlier chunks "
+                "and left their rows unwritten", word);
+  return ok();
 }
 
 
@@ -633,7 +677,7 @@ fam_status fam_rank_order(const float* scores, int64_t row_stride, int H, int n,
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
   if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
   fam::RankArgs a{scores, row_stride, order, workspace, H, n, fam::rank_tiles(n)};
-  return hip_status(fam::launch_rank(a, static_cast<hipStream_t>(stream)), "fam_rank_order launch");
+  return launched(fam::launch_rank(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "fam_rank_order launch");
 }
 
 size_t fam_eviction_cost_workspace_size(int H, int n) {
@@ -662,7 +706,49 @@ fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const 
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
   if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
   fam::CostArgs a{importance, row_stride, order, cost, static_cast<double*>(workspace), H, n};
-  return hip_status(fam::launch_cost(a, static_cast<hipStream_t>(stream)), "fam_eviction_cost launch");
+  return launched(fam::launch_cost(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "fam_eviction_cost launch");
+}
+
+static size_t align8(size_t x) { return (x + 7) & ~(size_t)7; }
+
+size_t fam_eviction_cost_ratio_workspace_size(int H, int n) {
+  if (H < 0 || n < 0) return 0;
+  return align8(fam::rank_workspace_bytes(H, n)) + align8((size_t)H * n * sizeof(int32_t)) +
+         2 * fam_eviction_cost_workspace_size(H, n);
+}
+
+fam_status fam_eviction_cost_ratio(const float* scores, int64_t scores_row_stride, const float* importance,
+                                   int64_t importance_row_stride, int H, int n, double* ratio,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  if (H < 0 || n < 0) return fail(FAM_ERR_INVALID_ARG, "H and n must be >= 0");
+  if (n > kMaxSeq) return fail(FAM_ERR_UNSUPPORTED, "n = %d exceeds %d", n, kMaxSeq);
+  if (H == 0) return ok();
+  if (!ratio) return fail(FAM_ERR_INVALID_ARG, "ratio must be non-null");
+  if (n > 0 && (!scores || !importance))
+    return fail(FAM_ERR_INVALID_ARG, "scores and importance must be non-null");
+  if (H > 1 && (scores_row_stride < n || importance_row_stride < n))
+    return fail(FAM_ERR_INVALID_ARG, "row strides must be >= n");
+  if ((reinterpret_cast<uintptr_t>(scores) | reinterpret_cast<uintptr_t>(importance)) & 3u ||
+      (reinterpret_cast<uintptr_t>(ratio) & 7u))
+    return fail(FAM_ERR_INVALID_ARG, "scores and importance must be 4-byte, ratio 8-byte aligned");
+  if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
+  const size_t need = fam_eviction_cost_ratio_workspace_size(H, n);
+  if (!workspace || workspace_bytes < need)
+    return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need,
+                workspace ? workspace_bytes : (size_t)0);
+  if (reinterpret_cast<uintptr_t>(workspace) & 7u)
+    return fail(FAM_ERR_INVALID_ARG, "workspace must be 8-byte aligned");
+  char* ws = static_cast<char*>(workspace);
+  void* rank_ws = ws;
+  int32_t* order = reinterpret_cast<int32_t*>(ws + align8(fam::rank_workspace_bytes(H, n)));
+  double* part = reinterpret_cast<double*>(reinterpret_cast<char*>(order) + align8((size_t)H * n * sizeof(int32_t)));
+  double* part_opt = part + (size_t)H * fam::cost_blocks(n);
+  const int nt = fam::rank_tiles(n);
+  fam::RankArgs rs{scores, scores_row_stride, order, rank_ws, H, n, nt};
+  fam::RankArgs ri{importance, importance_row_stride, order, rank_ws, H, n, nt};
+  fam::CostArgs c{importance, importance_row_stride, order, nullptr, part, H, n};
+  return launched(fam::launch_cost_ratio(rs, ri, c, part_opt, ratio, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
+                    "fam_eviction_cost_ratio launch");
 }
 
 fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a, const int32_t* idx_b,
@@ -678,7 +764,7 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
        reinterpret_cast<uintptr_t>(common)) & 7u)
     return fail(FAM_ERR_INVALID_ARG, "offsets and common must be 8-byte aligned");
   fam::OverlapArgs a{idx_a, offsets_a, idx_b, offsets_b, common, H, S};
-  return hip_status(fam::launch_overlap(a, static_cast<hipStream_t>(stream)),
+  return launched(fam::launch_overlap(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream),
                     "fam_retention_overlap launch");
 }
 
@@ -688,10 +774,10 @@ size_t fam_topk_cutoff_workspace_size(int H, int S) {
   return (size_t)H * S * sizeof(int32_t) + fam::cutoff_workspace_bytes(H, S);
 }
 
-fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int32_t* tau,
+fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int sinks, int w, int k, int32_t* tau,
                            void* workspace, size_t workspace_bytes, void* stream) {
-  if (H < 0 || S < 1 || w < 0 || k < 0)
-    return fail(FAM_ERR_INVALID_ARG, "need H >= 0, S >= 1, w >= 0 and k >= 0");
+  if (H < 0 || S < 1 || sinks < 0 || w < 0 || k < 0)
+    return fail(FAM_ERR_INVALID_ARG, "need H >= 0, S >= 1, sinks >= 0, w >= 0 and k >= 0");
   if (S > fam::kCutoffMaxS)
     return fail(FAM_ERR_UNSUPPORTED, "S = %d exceeds %d positions", S, fam::kCutoffMaxS);
   if (H > 65535) return fail(FAM_ERR_UNSUPPORTED, "H = %d exceeds 65535", H);
@@ -710,9 +796,9 @@ fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int
   a.rank = static_cast<int32_t*>(workspace);
   a.tau = tau;
   a.ws = static_cast<int32_t*>(workspace) + (size_t)H * S;
-  a.H = H, a.S = S, a.w = w, a.k = k;
+  a.H = H, a.S = S, a.sinks = sinks, a.w = w, a.k = k;
   fam::cutoff_shape(S, a.L, a.nw, a.ntiles);
-  return hip_status(fam::launch_cutoff(a, static_cast<hipStream_t>(stream)), "fam_topk_cutoff launch");
+  return launched(fam::launch_cutoff(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "fam_topk_cutoff launch");
 }
 
 

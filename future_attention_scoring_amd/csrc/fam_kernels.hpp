@@ -143,9 +143,12 @@ struct InplaceArgs {
   int64_t pos_sh;
   int64_t total; // offsets[H]: kept rows over all heads
   int H, S, d;   // S: rows per head region
-  uint32_t* ws;  // ticket counter, then one flag per chunk from word kInplaceFlags0
+  uint32_t* ws;  // ticket counter, error word, then one flag per chunk from word kInplaceFlags0
+  int spin_limit;   // polls per flag batch before a chunk gives up (and reports it)
 };
+constexpr int kInplaceErrorWord = 1;        // chunks whose wait gave up (their rows are not written)
 constexpr int kInplaceFlags0 = 32;          // words before the first chunk flag
+constexpr int kInplaceSpinLimit = 1 << 22;  // default bound on the polls (waits end long before)
 constexpr int kInplaceMinChunkRows = 128;   // rows per chunk at d = 256 (more for smaller d)
 inline size_t inplace_workspace_bytes(int64_t total) {
   return 4 * (size_t)(kInplaceFlags0 + (total + kInplaceMinChunkRows - 1) / kInplaceMinChunkRows);
@@ -179,6 +182,10 @@ struct CostArgs {
 constexpr int kCostBlock = 4096;   // entries per workgroup
 inline int cost_blocks(int n) { return (n + kCostBlock - 1) / kCostBlock; }
 hipError_t launch_cost(const CostArgs& a, hipStream_t s);
+// Both rankings' orders into cost.order (scores first, then importance), the
+// two costs' block partial sums into cost.part and part_opt, and the ratio.
+hipError_t launch_cost_ratio(const RankArgs& rank_scores, const RankArgs& rank_imp, const CostArgs& cost,
+                             double* part_opt, double* ratio, hipStream_t s);
 
 struct OverlapArgs {
   const int32_t* idx_a;
@@ -197,10 +204,10 @@ struct CutoffArgs {
   int32_t* rank;         // [H, S] workspace: rank of every position
   int32_t* tau;          // [H, S] out
   void* ws;              // wavelet matrix (cutoff_workspace_bytes after rank)
-  int H, S, w, k;
+  int H, S, sinks, w, k; // the budget (sinks, window, long-range tokens)
   int L, nw, ntiles;     // levels, words per level (with a terminal word), 1024-position tiles
 };
-constexpr int kCutoffMaxS = 1 << 18;  // at most 256 tiles of 1024 positions
+constexpr int kCutoffMaxS = 1 << 20;  // at most 1024 tiles of 1024 positions
 constexpr int kCutoffTile = 1024;
 // Levels (bits of a rank - 1), words per level and tiles for S positions, and
 // the workspace bytes after the ranks: per-tile counts of ones [L][H][ntiles],

@@ -46,7 +46,6 @@ constexpr int kAppendThreads = 256;
 constexpr int kAppendPer = 4;   // pieces per thread
 constexpr int kInplaceThreads = 512;
 constexpr int kInplaceUnroll = 8;   // rows per thread and chunk (loads in flight: 2 x 8)
-constexpr int kInplaceSpinLimit = 1 << 22;   // polls per flag batch (a bound; waits end long before)
 
 template <int CPR>
 __global__ __launch_bounds__(kAppendThreads) void append_kernel(AppendArgs p) {
@@ -87,7 +86,7 @@ __global__ __launch_bounds__(kInplaceThreads) void inplace_kernel(InplaceArgs p)
   constexpr int R = RPP * U;                   // rows per chunk
   static_assert(R >= kInplaceMinChunkRows, "workspace sized for chunks of at least kInplaceMinChunkRows");
   __shared__ int64_t offs[kInplaceThreads];
-  __shared__ int sh_ticket, sh_umin;
+  __shared__ int sh_ticket, sh_umin, sh_gave_up;
   const int tid = threadIdx.x, ch = tid % CPR, rr = tid / CPR;
   const int lane = tid & 63, wave = tid >> 6;
   uint32_t* ticket = p.ws;
@@ -158,19 +157,27 @@ __global__ __launch_bounds__(kInplaceThreads) void inplace_kernel(InplaceArgs p)
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) __hip_atomic_store(flags + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  // wait for the earlier chunks that may read this chunk's output rows
+  // wait for the earlier chunks that may read this chunk's output rows; a
+  // wait that runs out of polls leaves the chunk's rows unwritten and counts
+  // the chunk in the error word (the bound is never reached in practice)
   if (wave == 0) {
-    for (int u0 = sh_umin; u0 < t; u0 += 64) {
+    bool gave_up = false;
+    for (int u0 = sh_umin; u0 < t && !gave_up; u0 += 64) {
       const int u = u0 + lane;
       bool pending = u < t;
-      for (int spin = 0; spin < kInplaceSpinLimit; ++spin) {
+      for (int spin = 0; spin < p.spin_limit && __any(pending); ++spin) {
         if (pending) pending = __hip_atomic_load(flags + u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u;
-        if (!__any(pending)) break;
-        __builtin_amdgcn_s_sleep(1);
+        if (__any(pending)) __builtin_amdgcn_s_sleep(1);
       }
+      gave_up = __any(pending);
+    }
+    if (lane == 0) {
+      sh_gave_up = gave_up ? 1 : 0;
+      if (gave_up) __hip_atomic_fetch_add(p.ws + kInplaceErrorWord, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
   __syncthreads();
+  if (sh_gave_up) return;
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (row[u] < 0) continue;

@@ -286,6 +286,22 @@ __global__ __launch_bounds__(64) void cost_reduce_kernel(CostArgs p, int nb) {
   p.cost[h] = t;
 }
 
+// KVP's normalised cost: each head's two costs summed from their block
+// partial sums in block order (the same sums cost_reduce_kernel forms), then
+// their quotient; 1 where both are 0 (no importance to evict at any budget:
+// every ranking is optimal).
+__global__ __launch_bounds__(64) void cost_ratio_kernel(const double* part, const double* part_opt, int H,
+                                                        int nb, double* ratio) {
+  const int h = blockIdx.x * 64 + threadIdx.x;
+  if (h >= H) return;
+  double c = 0.0, c_opt = 0.0;
+  for (int b = 0; b < nb; ++b) {
+    c += part[(int64_t)h * nb + b];
+    c_opt += part_opt[(int64_t)h * nb + b];
+  }
+  ratio[h] = (c == 0.0 && c_opt == 0.0) ? 1.0 : c / c_opt;
+}
+
 constexpr int kOverlapThreads = 1024;
 
 constexpr int kOverlapBatch = 8;   // list entries per thread and batch
@@ -365,6 +381,23 @@ hipError_t launch_cost(const CostArgs& a, hipStream_t s) {
   const int nb = cost_blocks(a.n);
   if (nb > 0) hipLaunchKernelGGL(cost_kernel, dim3((unsigned)nb, (unsigned)a.H), dim3(kCostThreads), 0, s, a);
   hipLaunchKernelGGL(cost_reduce_kernel, dim3((unsigned)((a.H + 63) / 64)), dim3(64), 0, s, a, nb);
+  return hipGetLastError();
+}
+
+hipError_t launch_cost_ratio(const RankArgs& rank_scores, const RankArgs& rank_imp, const CostArgs& cost,
+                             double* part_opt, double* ratio, hipStream_t s) {
+  if (cost.H == 0) return hipSuccess;
+  const int nb = cost_blocks(cost.n);
+  hipError_t e = launch_rank(rank_scores, s);
+  if (e != hipSuccess) return e;
+  if (nb > 0) hipLaunchKernelGGL(cost_kernel, dim3((unsigned)nb, (unsigned)cost.H), dim3(kCostThreads), 0, s, cost);
+  e = launch_rank(rank_imp, s);   // overwrites the order once the first costs are formed (stream order)
+  if (e != hipSuccess) return e;
+  CostArgs opt = cost;
+  opt.part = part_opt;
+  if (nb > 0) hipLaunchKernelGGL(cost_kernel, dim3((unsigned)nb, (unsigned)cost.H), dim3(kCostThreads), 0, s, opt);
+  hipLaunchKernelGGL(cost_ratio_kernel, dim3((unsigned)((cost.H + 63) / 64)), dim3(64), 0, s, cost.part, part_opt,
+                     cost.H, nb, ratio);
   return hipGetLastError();
 }
 

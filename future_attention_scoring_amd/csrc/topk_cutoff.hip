@@ -1,23 +1,23 @@
 // Running top-k cut-off over static ranks (gfx950).
 //
-// KVpop ("Delayed Memory Scoring" and "Efficient Online Pruning"): tokens
-// carry a static rank (1 = best); at query q the token t = q - w leaves the
-// protected window and becomes eligible, and the cut-off tau_q is the rank of
-// the k-th best eligible token, so that the sparse attention keeps the sinks,
-// the window and the eligible tokens with rank <= tau_q. With fewer than k
-// eligible tokens tau_q = S (every eligible token passes); with k = 0,
-// tau_q = 0.
+// KVpop ("Delayed Memory Scoring", "Efficient Online Pruning" and Algorithm
+// 2): tokens carry a static rank (1 = best); the budget is (s, w, k); at
+// query q the token t = q - w leaves the protected window and joins the
+// eligible set E(q) if it is not a sink (t >= s); tau_q stays -1 until
+// |E(q)| >= k and is then the rank of the k-th best eligible token (0 when
+// k = 0), so that the sparse attention keeps the sinks, the window and the
+// eligible tokens with rank <= tau_q.
 //
-// The page keeps the eligible ranks in a Fenwick tree, inserts one token per
-// query and finds tau_q by binary lifting: a sequential sweep. Here tau_q is
-// read as what it is, the k-th smallest value of the prefix of length
-// q - w + 1 of the per-position rank sequence, and every query is answered
-// independently from a wavelet matrix of that sequence:
+// The page keeps E(q) in a Fenwick tree, inserts one token per query and
+// finds tau_q by binary lifting: a sequential sweep. Here tau_q is read as
+// what it is, the k-th smallest value of the positions [s, q - w] of the
+// per-position rank sequence, and every query is answered independently
+// from a wavelet matrix of that sequence:
 //   * level l holds one bit per position (bit L-1-l of the values, most
 //     significant first) with per-word prefix counts of ones, and the next
 //     level's sequence is the stable partition of this one by that bit
 //     (zeros first);
-//   * a query walks the L levels with its prefix [lo, hi): if the zeros in
+//   * a query walks the L levels with its range [lo, hi): if the zeros in
 //     the range number at least k it follows them, otherwise it counts them
 //     off, sets the bit and follows the ones. Two counts per level.
 // Build: a fill kernel clears the per-tile counts of ones; wt_ranks
@@ -224,14 +224,15 @@ __global__ __launch_bounds__(256) void wt_query(CutoffArgs p) {
   const int64_t stride = (int64_t)gridDim.x * 256;
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += stride) {
     const int h = (int)(e / p.S), q = (int)(e - (int64_t)h * p.S);
-    const int m = q - p.w + 1;   // eligible prefix length
+    const int hi0 = q - p.w + 1;                   // E(q) = positions [sinks, q - w]
+    const int m = hi0 - p.sinks;                   // |E(q)| (negative: none)
     int out;
     if (p.k == 0) {
       out = 0;
     } else if (m < p.k) {
-      out = p.S;
+      out = -1;
     } else {
-      int lo = 0, hi = m, k = p.k, val = 0;
+      int lo = p.sinks, hi = hi0, k = p.k, val = 0;
       for (int l = 0; l < p.L; ++l) {
         const u32x2_t* wc = w.wc + ((size_t)h * p.L + l) * p.nw;
         const int o_lo = wt_rank1(wc, lo), o_hi = wt_rank1(wc, hi);
@@ -259,7 +260,9 @@ hipError_t launch_cutoff(const CutoffArgs& a0, hipStream_t s) {
   if (a0.H == 0) return hipSuccess;
   CutoffArgs a = a0;
   const int64_t n = (int64_t)a.H * a.S;
-  if (a.k > 0 && a.w < a.S) {   // otherwise every answer is 0 or S and no matrix is needed
+  // with k = 0, or fewer than k eligible tokens at the last query, every
+  // answer is 0 or -1 and no matrix is needed
+  if (a.k > 0 && (int64_t)a.sinks + a.w + a.k - 1 < a.S) {
     const int64_t ncount = (int64_t)a.L * a.H * a.ntiles;
     const int64_t fb = (ncount + 255) / 256;
     hipLaunchKernelGGL(wt_fill_kernel, dim3((unsigned)(fb < 2048 ? fb : 2048)), dim3(256), 0, s,

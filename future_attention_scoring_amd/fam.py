@@ -19,7 +19,7 @@ _lib = None
 
 FAM_BF16, FAM_FP16 = 0, 1
 _STATUS = {0: "FAM_OK", 1: "FAM_ERR_INVALID_ARG", 2: "FAM_ERR_UNSUPPORTED",
-           3: "FAM_ERR_WORKSPACE", 4: "FAM_ERR_HIP"}
+           3: "FAM_ERR_WORKSPACE", 4: "FAM_ERR_HIP", 5: "FAM_ERR_TIMEOUT"}
 
 # (name, restype, argtypes) of every exported symbol of include/fam.h
 _i, _i64, _f, _p = ctypes.c_int, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p
@@ -53,12 +53,15 @@ _SIGNATURES = {
     "kv_compact_inplace": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p,
                                 _i64, _p, ctypes.c_size_t, _p]),
     "kv_compact_inplace_workspace_size": (ctypes.c_size_t, [_i64]),
+    "kv_compact_inplace_status": (_i, [_p, _p]),
     "fam_rank_order": (_i, [_p, _i64, _i, _i, _p, _p, ctypes.c_size_t, _p]),
     "fam_rank_order_workspace_size": (ctypes.c_size_t, [_i, _i]),
     "fam_eviction_cost": (_i, [_p, _i64, _p, _i, _i, _p, _p, ctypes.c_size_t, _p]),
     "fam_eviction_cost_workspace_size": (ctypes.c_size_t, [_i, _i]),
     "fam_retention_overlap": (_i, [_p, _p, _p, _p, _i, _i, _p, _p]),
-    "fam_topk_cutoff": (_i, [_p, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]),
+    "fam_eviction_cost_ratio": (_i, [_p, _i64, _p, _i64, _i, _i, _p, _p, ctypes.c_size_t, _p]),
+    "fam_eviction_cost_ratio_workspace_size": (ctypes.c_size_t, [_i, _i]),
+    "fam_topk_cutoff": (_i, [_p, _i, _i, _i, _i, _i, _p, _p, ctypes.c_size_t, _p]),
     "fam_topk_cutoff_workspace_size": (ctypes.c_size_t, [_i, _i]),
 }
 EXPORTED = tuple(_SIGNATURES)
@@ -427,6 +430,12 @@ def kv_compact_inplace_workspace_size(total_rows: int) -> int:
     return int(load().kv_compact_inplace_workspace_size(int(total_rows)))
 
 
+def kv_compact_inplace_status(workspace: torch.Tensor) -> None:
+    """Wait for the current stream and raise FamError(FAM_ERR_TIMEOUT) if the
+    last kv_compact_inplace on `workspace` left rows unwritten."""
+    _check(load().kv_compact_inplace_status(workspace.data_ptr(), _stream(workspace)))
+
+
 def kv_compact_inplace(k_cache: torch.Tensor, v_cache: torch.Tensor, idx: torch.Tensor,
                        offsets: torch.Tensor, pos: Optional[torch.Tensor] = None,
                        total_rows: Optional[int] = None,
@@ -603,12 +612,31 @@ def fam_eviction_cost(importance: torch.Tensor, order: torch.Tensor,
     return cost
 
 
-def eviction_cost_ratio(scores: torch.Tensor, importance: torch.Tensor) -> torch.Tensor:
+def fam_eviction_cost_ratio_workspace_size(H: int, n: int) -> int:
+    return int(load().fam_eviction_cost_ratio_workspace_size(int(H), int(n)))
+
+
+def fam_eviction_cost_ratio(scores: torch.Tensor, importance: torch.Tensor,
+                            ratio: Optional[torch.Tensor] = None,
+                            workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """KVP's normalised eviction cost of ranking by `scores`: cost over the cost
-    of ranking by `importance` itself (>= 1; 1 is optimal), per row."""
-    c = fam_eviction_cost(importance, fam_rank_order(scores))
-    c_opt = fam_eviction_cost(importance, fam_rank_order(importance))
-    return c / c_opt
+    of ranking by `importance` itself (>= 1; 1 is optimal), per row: [H] fp64."""
+    H, n = _score_rows(scores, "scores")
+    if _score_rows(importance, "importance") != (H, n):
+        raise FamError(1, "scores and importance must have the same [H, n] shape")
+    if ratio is None:
+        ratio = torch.empty(H, dtype=torch.float64, device=scores.device)
+    if workspace is None:
+        workspace = torch.empty(max(fam_eviction_cost_ratio_workspace_size(H, n), 8), dtype=torch.uint8,
+                                device=scores.device)
+    _check(load().fam_eviction_cost_ratio(scores.data_ptr(), _row_stride(scores), importance.data_ptr(),
+                                          _row_stride(importance), H, n, ratio.data_ptr(),
+                                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                          _stream(scores)))
+    return ratio
+
+
+eviction_cost_ratio = fam_eviction_cost_ratio
 
 
 def fam_retention_overlap(idx_a: torch.Tensor, offsets_a: torch.Tensor, idx_b: torch.Tensor,
@@ -632,9 +660,10 @@ def fam_topk_cutoff_workspace_size(H: int, S: int) -> int:
     return int(load().fam_topk_cutoff_workspace_size(int(H), int(S)))
 
 
-def fam_topk_cutoff(order: torch.Tensor, w: int, k: int, tau: Optional[torch.Tensor] = None,
+def fam_topk_cutoff(order: torch.Tensor, sinks: int, w: int, k: int, tau: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """KVpop's running cut-off tau [H, S] from fam_rank_order's order [H, S]."""
+    """KVpop's running cut-off tau [H, S] (Algorithm 2, budget (sinks, w, k))
+    from fam_rank_order's order [H, S]; -1 where fewer than k are eligible."""
     if order.dim() != 2 or order.dtype != torch.int32 or not order.is_cuda or not order.is_contiguous():
         raise FamError(1, "order must be a contiguous device int32 [H, S] tensor")
     H, S = order.shape
@@ -643,7 +672,7 @@ def fam_topk_cutoff(order: torch.Tensor, w: int, k: int, tau: Optional[torch.Ten
     if workspace is None:
         workspace = torch.empty(max(fam_topk_cutoff_workspace_size(H, S), 4), dtype=torch.uint8,
                                 device=order.device)
-    _check(load().fam_topk_cutoff(order.data_ptr(), H, S, int(w), int(k), tau.data_ptr(),
+    _check(load().fam_topk_cutoff(order.data_ptr(), H, S, int(sinks), int(w), int(k), tau.data_ptr(),
                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                   _stream(order)))
     return tau

@@ -10,13 +10,23 @@
  *   - The library never allocates or frees device memory and keeps no state
  *     between calls, apart from loaded code objects and a thread-local error
  *     string. The caller owns every buffer.
- *   - Device entry points only enqueue work on `stream` and return; they never
- *     synchronise. Outputs are valid once the caller has synchronised the
- *     stream.
+ *   - Device entry points only enqueue work on `stream` and return; they do
+ *     not synchronise (except under the FAM_SYNC_CHECK debug switch below,
+ *     and kv_compact_inplace_status, which exists to wait). Outputs are valid
+ *     once the caller has synchronised the stream.
  *   - All arguments are validated before anything is launched. On failure an
  *     entry point returns a non-zero fam_status, launches nothing and leaves
  *     every output untouched; fam_last_error() then describes the failure.
  *   - No C++ exception and no abort crosses this boundary.
+ *
+ * Debug switches (environment variables, read on every call)
+ *   FAM_SYNC_CHECK=1  every device entry point synchronises its stream after
+ *                     its launches and reports a fault of the enqueued work
+ *                     (FAM_ERR_HIP) or an incomplete in-place compaction
+ *                     (FAM_ERR_TIMEOUT) as its own status. Off by default.
+ *   FAM_INPLACE_SPIN_LIMIT=n  lowers the bound on the polls of
+ *                     kv_compact_inplace's waits (for tests of the timeout
+ *                     path; 0 makes every wait give up at once).
  *
  * Sources (titles and sections of the pages this library implements)
  *   [KVpop]  "KVpop - Key-Value Cache Compression with Predictive Online
@@ -42,7 +52,9 @@ typedef enum {
   FAM_ERR_INVALID_ARG = 1, /* a size, stride, pointer or budget is invalid   */
   FAM_ERR_UNSUPPORTED = 2, /* valid but not implemented (head dim, dtype...) */
   FAM_ERR_WORKSPACE = 3,   /* the workspace is missing or too small          */
-  FAM_ERR_HIP = 4          /* the HIP runtime reported an error at launch    */
+  FAM_ERR_HIP = 4,         /* the HIP runtime reported an error at launch    */
+  FAM_ERR_TIMEOUT = 5      /* a bounded wait inside a kernel gave up; the
+                              outputs of that call are incomplete            */
 } fam_status;
 
 typedef enum {
@@ -468,6 +480,14 @@ fam_status kv_compact_inplace(void* k, void* v, int elem_bytes, int H, int S, in
                               int64_t total_rows, int32_t* pos, int64_t pos_sh,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/* kv_compact_inplace_status -- whether the last kv_compact_inplace on this
+ * workspace moved every row. Waits for `stream` (the one the compaction was
+ * enqueued on) and reads the workspace's error word: FAM_OK, or
+ * FAM_ERR_TIMEOUT if a chunk's bounded wait for the chunks reading its rows
+ * gave up, in which case that chunk's rows were left unwritten (the other
+ * chunks are complete). The only synchronising call of the library. */
+fam_status kv_compact_inplace_status(const void* workspace, void* stream);
+
 /* Bytes of workspace kv_compact_inplace needs for total_rows kept rows (about
  * one byte per 32 rows; 0 for total_rows < 0). */
 size_t kv_compact_inplace_workspace_size(int64_t total_rows);
@@ -531,6 +551,41 @@ fam_status fam_eviction_cost(const float* importance, int64_t row_stride, const 
 size_t fam_eviction_cost_workspace_size(int H, int n);
 
 /* ------------------------------------------------------------------------
+ * fam_eviction_cost_ratio -- KVP's normalised eviction cost of a scorer.
+ *
+ * [KVP] 3.1.1: the cost-versus-budget area of the importance a ranking
+ * evicts, normalised by the cost of the optimal ranking. Per head h:
+ *
+ *   ratio[h] = cost(importance, order of scores) / cost(importance, order
+ *              of importance)
+ *
+ * with cost and order exactly as fam_eviction_cost and fam_rank_order
+ * define them (the two costs are bit-identical to what those calls return).
+ * The ratio is >= 1 for non-negative importance and 1 for an optimal
+ * order. Where both costs are 0 (no importance anywhere) the ratio is 1:
+ * every ranking is optimal; otherwise it is the plain IEEE quotient (so a
+ * zero optimal cost against a non-zero cost, possible only with negative
+ * importance, gives an infinity).
+ *
+ *   scores      device, [H] rows of n fp32 (the scorer), row stride
+ *               scores_row_stride (>= n when H > 1)
+ *   importance  device, [H] rows of n fp32 (e.g. future-attention mass),
+ *               row stride importance_row_stride (>= n when H > 1)
+ *   ratio       device out, [H] fp64
+ *   workspace   device scratch of fam_eviction_cost_ratio_workspace_size(H,
+ *               n) bytes (rank-order scratch, one order [H, n] int32 and two
+ *               sets of per-block partial sums), 8-byte aligned, owned by the
+ *               caller; contents irrelevant on entry
+ * Requirements: H <= 65535.
+ * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
+ * FAM_ERR_HIP.
+ * ---------------------------------------------------------------------- */
+fam_status fam_eviction_cost_ratio(const float* scores, int64_t scores_row_stride, const float* importance,
+                                   int64_t importance_row_stride, int H, int n, double* ratio,
+                                   void* workspace, size_t workspace_bytes, void* stream);
+size_t fam_eviction_cost_ratio_workspace_size(int H, int n);
+
+/* ------------------------------------------------------------------------
  * fam_retention_overlap -- entries two kept sets share, per head.
  *
  * [KVpop] Figure 7: top-k retention recall is the fraction of the teacher's
@@ -555,32 +610,37 @@ fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,
 /* ------------------------------------------------------------------------
  * fam_topk_cutoff -- the running top-k cut-off of a sparse prefill mask.
  *
- * [KVpop] "Delayed Memory Scoring" and "Efficient Online Pruning": tokens
- * are pre-sorted by a static priority score (rank 1 = best); at query q the
- * token t = q - w leaves the protected window and becomes eligible; tau_q is
- * the rank of the k-th best eligible token, and the attention keeps the
- * sinks, the window and the eligible tokens with rank <= tau_q. The page
- * finds tau_q with a Fenwick tree, one insertion per query; this answers
- * every query independently from a wavelet matrix of the per-position ranks
- * (tau_q is the k-th smallest value of a prefix of that sequence).
+ * [KVpop] "Delayed Memory Scoring", "Efficient Online Pruning" and
+ * Algorithm 2 (running top-k cutoff computation for one KV head): tokens
+ * are pre-sorted by a static priority score (rank 1 = best); the budget is
+ * (s, w, k); at query q the token t = q - w leaves the protected window and
+ * becomes eligible if it is not a sink (t >= s); tau_q starts at -1 and,
+ * once at least k tokens are eligible, is the rank of the k-th best
+ * eligible token. The attention then keeps the sinks, the window and the
+ * eligible tokens with rank <= tau_q. The page finds tau_q with a Fenwick
+ * tree, one insertion per query; this answers every query independently
+ * from a wavelet matrix of the per-position ranks (tau_q is the k-th
+ * smallest value of a range of that sequence).
  *
- *   tau[h, q] = k-th smallest rank among the positions t <= q - w of head h,
- *               S if fewer than k are eligible, 0 if k == 0
+ *   E(q)      = positions t with sinks <= t <= q - w
+ *   tau[h, q] = -1 if |E(q)| < k; otherwise 0 if k == 0, else the k-th
+ *               smallest rank among the positions in E(q) of head h
  *
  *   order      device, [H, S] int32 positions best first (fam_rank_order's
  *              output: every position exactly once; any other content gives
  *              unspecified cut-offs, never an access out of bounds)
+ *   sinks, w, k  the budget: sink tokens, window, long-range tokens
  *   tau        device out, [H, S] int32, fully overwritten
  *   workspace  device scratch of fam_topk_cutoff_workspace_size(H, S) bytes
  *              (the ranks, two level sequences, the bit words and counts
  *              of ceil(log2 S) levels and per-tile counts of ones: about 16
  *              bytes per entry at S = 131072), 4-byte aligned, owned by the
  *              caller, contents irrelevant on entry
- * Requirements: S <= 262144; H <= 65535; w >= 0, k >= 0.
+ * Requirements: S <= 1048576; H <= 65535; sinks, w, k >= 0.
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_WORKSPACE,
  * FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
-fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int w, int k, int32_t* tau,
+fam_status fam_topk_cutoff(const int32_t* order, int H, int S, int sinks, int w, int k, int32_t* tau,
                            void* workspace, size_t workspace_bytes, void* stream);
 size_t fam_topk_cutoff_workspace_size(int H, int S);
 

@@ -338,19 +338,34 @@ def test_every_entry_point_has_a_python_wrapper_of_the_same_name():
     assert missing == []
 
 
+def test_cost_ratio_validation():
+    lib = fam.load()
+    ws = lib.fam_eviction_cost_ratio_workspace_size(3, 5000)
+    assert ws >= 16 * 3 * 5000 + 4 * 3 * 5000 + 2 * 8 * 3 * 2
+    r = lib.fam_eviction_cost_ratio
+    assert r(FAKE, 5000, FAKE, 5000, 3, 5000, FAKE, FAKE, ws - 1, None) == WORKSPACE
+    assert r(FAKE, 4999, FAKE, 5000, 3, 5000, FAKE, FAKE, ws, None) == INVALID       # row stride
+    assert r(FAKE, 5000, FAKE, 5000, 3, 5000, FAKE + 4, FAKE, ws, None) == INVALID   # ratio alignment
+    assert r(FAKE, 5000, None, 5000, 3, 5000, FAKE, FAKE, ws, None) == INVALID
+    assert r(FAKE, 5000, FAKE, 5000, 3, -1, FAKE, FAKE, ws, None) == INVALID
+    assert r(None, 0, None, 0, 0, 10, None, None, 0, None) == 0
+
+
 def test_topk_cutoff_validation():
     lib = fam.load()
     assert lib.fam_topk_cutoff_workspace_size(8, 131072) >= 4 * 8 * 131072 * 3
-    assert lib.fam_topk_cutoff_workspace_size(8, 300000) == 0
+    assert lib.fam_topk_cutoff_workspace_size(8, 300000) >= 4 * 8 * 300000 * 3
+    assert lib.fam_topk_cutoff_workspace_size(8, (1 << 20) + 1) == 0
     ws = lib.fam_topk_cutoff_workspace_size(2, 100)
     # ranks (2 x 100 ints), then 7 levels: ones per tile 7 x 2 x 1, two
     # sequences 2 x 2 x 100, (bit word, count) pairs 2 x 2 x 7 x 33, and 8
     # bytes of slack to align the pairs
     assert ws == 4 * (2 * 100 + 7 * 2 * 1 + 2 * 2 * 100 + 2 * 2 * 7 * 33) + 8
-    assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, 10, FAKE, FAKE, ws - 1, None) == WORKSPACE
-    assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, 10, FAKE, FAKE + 2, ws, None) == INVALID   # 4-byte alignment
-    assert lib.fam_topk_cutoff(FAKE, 2, 100, -1, 10, FAKE, FAKE, ws, None) == INVALID
-    assert lib.fam_topk_cutoff(FAKE, 2, 100, 8, -1, FAKE, FAKE, ws, None) == INVALID
-    assert lib.fam_topk_cutoff(FAKE, 2, 300000, 8, 10, FAKE, FAKE, 1 << 30, None) == UNSUPPORTED
-    assert lib.fam_topk_cutoff(None, 2, 100, 8, 10, FAKE, FAKE, ws, None) == INVALID
-    assert lib.fam_topk_cutoff(None, 0, 100, 8, 10, None, None, 0, None) == 0
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, 4, 8, 10, FAKE, FAKE, ws - 1, None) == WORKSPACE
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, 4, 8, 10, FAKE, FAKE + 2, ws, None) == INVALID   # 4-byte alignment
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, -1, 8, 10, FAKE, FAKE, ws, None) == INVALID   # sinks
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, 4, -1, 10, FAKE, FAKE, ws, None) == INVALID
+    assert lib.fam_topk_cutoff(FAKE, 2, 100, 4, 8, -1, FAKE, FAKE, ws, None) == INVALID
+    assert lib.fam_topk_cutoff(FAKE, 2, (1 << 20) + 1, 4, 8, 10, FAKE, FAKE, 1 << 30, None) == UNSUPPORTED
+    assert lib.fam_topk_cutoff(None, 2, 100, 4, 8, 10, FAKE, FAKE, ws, None) == INVALID
+    assert lib.fam_topk_cutoff(None, 0, 100, 4, 8, 10, None, None, 0, None) == 0

@@ -124,7 +124,7 @@ def test_inplace_compression_and_cutoff_in_a_graph():
         fam.evict_select(scores, budgets, sinks, recent, idx=idx, offsets=offsets, workspace=sel_ws)
         fam.kv_compact_inplace(k, v, idx, offsets, total_rows=total, workspace=ip_ws)
         fam.fam_rank_order(scores, order=order, workspace=rank_ws)
-        fam.fam_topk_cutoff(order, 16, 700, tau=tau, workspace=cut_ws)
+        fam.fam_topk_cutoff(order, sinks, 16, 700, tau=tau, workspace=cut_ws)
 
     step()
     torch.cuda.synchronize()

@@ -75,6 +75,32 @@ def test_eviction_cost_matches_oracle(seed, H, n):
     assert np.all(fam.eviction_cost_ratio(impd, impd).cpu().numpy() == 1.0)
 
 
+def test_cost_ratio_in_library_against_oracle_and_costs():
+    """fam_eviction_cost_ratio against the oracle's normalised cost, against
+    the quotient of the two fam_eviction_cost results (bit for bit, the same
+    sums), on strided rows, and 1 for heads without importance."""
+    say("fam_eviction_cost_ratio")
+    H, n = 6, 9000
+    rng = np.random.default_rng(21)
+    imp = (rng.random((H, n)) ** 4).astype(np.float32)
+    imp[2] = 0.0                                         # no importance: ratio 1
+    imp[4] = 0.0
+    imp[4, 123] = 2.5                                    # importance on one entry
+    s = rng.standard_normal((H, n)).astype(np.float32)
+    s[:, rng.random(n) < 0.05] = 0.5                     # ties
+    big = torch.from_numpy(np.concatenate([s, imp], axis=1)).to(DEV)    # strided rows of both
+    sd, impd = big[:, :n], big[:, n:]
+    ratio = fam.fam_eviction_cost_ratio(sd, impd).cpu().numpy()
+    ref = rk.normalized_cost(s.astype(np.float64), imp.astype(np.float64))
+    np.testing.assert_allclose(ratio, ref, rtol=1e-12)
+    assert ratio[2] == 1.0
+    c = fam.fam_eviction_cost(impd.contiguous(), fam.fam_rank_order(sd.contiguous())).cpu().numpy()
+    c_opt = fam.fam_eviction_cost(impd.contiguous(), fam.fam_rank_order(impd.contiguous())).cpu().numpy()
+    live = c_opt != 0
+    assert np.array_equal(ratio[live], c[live] / c_opt[live])
+    assert np.all(ratio >= 1.0)
+
+
 def test_retention_overlap_on_selections():
     say("fam_retention_overlap of two evict_select outputs")
     H, S = 8, 20000
