@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -522,6 +523,55 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
     if (e != hipSuccess) return hip_status(e, "evict_select launch");
   }
   return launched(hipSuccess, static_cast<hipStream_t>(stream), "evict_select launch");
+}
+
+// evict_select without a caller workspace: the workspace is a static device
+// array (one copy per GPU, kept until the process ends). Host code never
+// passes the array's name to a kernel or a copy: on each device, the first
+// call looks up the array's device address with that device current and
+// keeps it; every later call uses that address.
+static __device__ __align__(256) unsigned char scratch[FAM_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+fam_status scratch_of_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(FAM_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!ptr) return fail(FAM_ERR_HIP, "hipGetSymbolAddress(scratch) returned no address");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return FAM_OK;
+}
+}  // namespace
+
+fam_status evict_select_noalloc(const float* scores, int64_t score_row_stride, int H, int S,
+                                const int64_t* budgets, int sinks, int recent, int32_t* idx,
+                                int64_t* offsets_dev, void* stream) {
+  if (H < 0 || S < 1 || sinks < 0 || recent < 0)
+    return fail(FAM_ERR_INVALID_ARG, "need H >= 0, S >= 1, sinks >= 0 and recent >= 0");
+  if (H == 0) return ok();
+  const size_t need = evict_select_workspace_size(H, S, sinks, recent);
+  if (need > (size_t)FAM_NOALLOC_SCRATCH_BYTES)
+    return fail(FAM_ERR_UNSUPPORTED,
+                "evict_select_noalloc: %d heads of %d positions need %zu bytes of scratch, more than the "
+                "%zu of its static array (use evict_select with a workspace)",
+                H, S, need, (size_t)FAM_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  const fam_status st = scratch_of_current_device(&ws);
+  if (st != FAM_OK) return st;
+  return evict_select(scores, score_row_stride, H, S, budgets, sinks, recent, idx, offsets_dev, ws,
+                      (size_t)FAM_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 fam_status kv_compact(const void* k, const void* v, int elem_bytes, int H, int S, int d,

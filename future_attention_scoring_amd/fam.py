@@ -45,6 +45,7 @@ _SIGNATURES = {
     "fam_soft_topk": (_i, [_p, _i, ctypes.c_double, ctypes.c_double, _p]),
     "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
     "evict_select_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "evict_select_noalloc": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p]),
     "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
     "fam_compute_chunk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
                                _i64, _i, _f, _p, _p, _p, ctypes.c_size_t, _p]),
@@ -346,6 +347,24 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
                                int(sinks), int(recent), idx.data_ptr(), offsets.data_ptr(),
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(scores)))
+    return idx, offsets
+
+
+def evict_select_noalloc(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,
+                         idx: torch.Tensor, offsets: torch.Tensor) -> Tuple[torch.Tensor, torch.Tensor]:
+    """evict_select with the library's static scratch instead of a workspace;
+    the caller passes idx [offsets[H]] int32 and offsets [H + 1] int64."""
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise FamError(1, "scores must be a device fp32 [H, S] tensor")
+    if scores.shape[1] > 1 and scores.stride(1) != 1:
+        raise FamError(1, "scores rows must be contiguous")
+    H, S = scores.shape
+    b = _i64_array(budgets)
+    if b.size != H:
+        raise FamError(1, f"{b.size} budgets for {H} heads")
+    _check(load().evict_select_noalloc(scores.data_ptr(), _row_stride(scores), H, S, b.ctypes.data,
+                                       int(sinks), int(recent), idx.data_ptr(), offsets.data_ptr(),
+                                       _stream(scores)))
     return idx, offsets
 
 

@@ -386,6 +386,34 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
 size_t evict_select_workspace_size(int H, int S, int sinks, int recent);
 
 /* ------------------------------------------------------------------------
+ * evict_select_noalloc -- evict_select for callers that cannot allocate.
+ *
+ * For callers that may not allocate device memory at all (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation):
+ * the same selection, with the same results bit for bit, as evict_select,
+ * whose workspace here is a static device array of
+ * FAM_NOALLOC_SCRATCH_BYTES (64 MiB) that each GPU holds from the library's
+ * first use on it until the process ends. The call allocates nothing and
+ * calls no allocating routine; the caller still passes every input and
+ * output. Every call on one GPU shares that GPU's array: calls that may
+ * overlap on one GPU (different streams without ordering) race and give
+ * unspecified results; calls ordered on one stream are safe. The array
+ * needs no clearing (evict_select's workspace contents on entry do not
+ * matter). On its first call on a device the library looks up and keeps
+ * the array's address there (the one piece of state it keeps besides the
+ * error string).
+ *
+ * Arguments, outputs and errors as evict_select, without the workspace;
+ * FAM_ERR_UNSUPPORTED when evict_select_workspace_size(H, S, sinks, recent)
+ * exceeds FAM_NOALLOC_SCRATCH_BYTES (e.g. 64 heads of 131072 candidates;
+ * 8 such heads, or 56 heads of 120000, fit).
+ * ---------------------------------------------------------------------- */
+#define FAM_NOALLOC_SCRATCH_BYTES (64u << 20)
+fam_status evict_select_noalloc(const float* scores, int64_t score_row_stride, int H, int S,
+                                const int64_t* budgets, int sinks, int recent,
+                                int32_t* idx, int64_t* offsets_dev, void* stream);
+
+/* ------------------------------------------------------------------------
  * kv_compact -- gather kept K and V rows into a new packed cache.
  *
  * [KVP] section 4.1 and A.2 (physical tensor compaction) and [Blog]
