@@ -22,7 +22,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfam.so")
 ARCH = "gfx950"
 
-SOURCES = ["fam_api.cpp", "fam_lse.hip", "fam_mass.hip", "kvpop_target.hip", "kv_cache.hip", "ranking.hip", "topk_cutoff.hip", "evict_select.hip",
+SOURCES = ["fam_api.cpp", "fam_lse.hip", "fam_mass.hip", "kvpop_target.hip", "kv_cache.hip", "ranking.hip", "topk_cutoff.hip", "evict_select.hip", "evict_select_long.hip",
            "kv_compact.hip"]
 
 COMMON = ["-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

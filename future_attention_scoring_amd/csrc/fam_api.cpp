@@ -463,6 +463,7 @@ int select_slots(int H) { return H < fam::kSelectBatch ? (H < 1 ? 1 : H) : fam::
 size_t evict_select_workspace_size(int H, int S, int sinks, int recent) {
   if (H < 0 || S < 1 || sinks < 0 || recent < 0) return 0;
   const Plan p = plan_of(S, sinks, recent);
+  if (p.c1 - p.c0 > fam::kSelectMaxCandidates) return fam::select_long_workspace_bytes(select_slots(H));
   return fam::select_workspace_bytes(select_slots(H), select_chunks(p));
 }
 
@@ -480,9 +481,10 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   for (int h = 0; h < H; ++h)
     if (budgets[h] < 0) return fail(FAM_ERR_INVALID_ARG, "budget of head %d is negative", h);
   const Plan p = plan_of(S, sinks, recent);
-  if (p.c1 - p.c0 > fam::kSelectMaxCandidates)
+  if (p.c1 - p.c0 > fam::kSelectLongMaxCandidates)
     return fail(FAM_ERR_UNSUPPORTED, "%d candidates per head exceed %d", p.c1 - p.c0,
-                fam::kSelectMaxCandidates);
+                fam::kSelectLongMaxCandidates);
+  const bool long_path = p.c1 - p.c0 > fam::kSelectMaxCandidates;
   const size_t need_ws = evict_select_workspace_size(H, S, sinks, recent);
   if (!workspace || workspace_bytes < need_ws)
     return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need_ws,
@@ -493,6 +495,13 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   for (int h = 0; h < H; ++h) {
     int64_t kh = budgets[h] > p.forced ? budgets[h] : p.forced;
     total += kh > S ? S : kh;
+  }
+  int batch = fam::kSelectBatch;
+  if (long_path) {
+    batch = fam::select_long_batch_heads(select_chunks(p));
+    if (batch < 1)
+      return fail(FAM_ERR_UNSUPPORTED, "evict_select: the device cannot hold the %d chunk workgroups of one head",
+                  select_chunks(p));
   }
   fam::SelectArgs a{};
   a.scores = scores;
@@ -508,8 +517,8 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   a.slots = select_slots(H);
   a.nchunk = select_chunks(p);
   int64_t off = 0;
-  for (int h0 = 0; h0 < H; h0 += fam::kSelectBatch) {
-    const int n = H - h0 < fam::kSelectBatch ? H - h0 : fam::kSelectBatch;
+  for (int h0 = 0; h0 < H; h0 += batch) {
+    const int n = H - h0 < batch ? H - h0 : batch;
     a.head0 = h0;
     a.nheads = n;
     for (int i = 0; i < n; ++i) {
@@ -519,10 +528,21 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
       a.n_choose[i] = (int32_t)(kh - p.forced);
       off += kh;
     }
-    const hipError_t e = fam::launch_select(a, static_cast<hipStream_t>(stream));
+    const hipError_t e = long_path ? fam::launch_select_long(a, static_cast<hipStream_t>(stream), h0 == 0)
+                                   : fam::launch_select(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_status(e, "evict_select launch");
   }
-  return launched(hipSuccess, static_cast<hipStream_t>(stream), "evict_select launch");
+  const fam_status rc = launched(hipSuccess, static_cast<hipStream_t>(stream), "evict_select launch");
+  if (rc != FAM_OK || !long_path || !sync_check()) return rc;
+  // under the sync check: the long path's error word counts waits that ran
+  // out of polls
+  uint32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, static_cast<hipStream_t>(stream));
+  if (e == hipSuccess) e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_status(e, "evict_select (sync check)");
+  if (word != 0u)
+    return fail(FAM_ERR_TIMEOUT, "evict_select: %u wait(s) ran out of polls; the index lists are incomplete", word);
+  return ok();
 }
 
 // evict_select without a caller workspace: the workspace is a static device
@@ -531,6 +551,9 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
 // call looks up the array's device address with that device current and
 // keeps it; every later call uses that address.
 static __device__ __align__(256) unsigned char scratch[FAM_NOALLOC_SCRATCH_BYTES];
+static_assert(FAM_NOALLOC_SCRATCH_BYTES >=
+                  4 * ((size_t)fam::kSelectLongHeaderWords + (size_t)fam::kSelectBatch * fam::kSelectLongSlotWordsMax),
+              "the static scratch holds the long path's largest workspace");
 
 namespace {
 constexpr int kMaxDevices = 64;

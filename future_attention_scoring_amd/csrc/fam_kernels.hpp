@@ -83,16 +83,22 @@ hipError_t launch_target(const TargetArgs& a, hipStream_t s);
 
 // Per-head selection. Heads are launched in batches of up to kSelectBatch
 // whose plan travels in the kernel arguments; each head's candidates are
-// split into chunks of kSelectChunk positions.
+// split into chunks of kSelectChunk positions. Up to kSelectMaxCandidates a
+// head: three launches (evict_select.hip); beyond, up to
+// kSelectLongMaxCandidates: one round-based launch (evict_select_long.hip).
 constexpr int kSelectBatch = 64;
 constexpr int kSelectChunk = 4096;
 constexpr int kSelectMaxCandidates = 131072;
+constexpr int kSelectLongMaxCandidates = 1 << 20;
+constexpr int kSelectLongMaxChunks = kSelectLongMaxCandidates / kSelectChunk + 1;   // chunks start 4-aligned
+constexpr int kSelectLongSlotWordsMax = 10240;   // long-path workspace words per head slot (at most)
+constexpr int kSelectLongHeaderWords = 64;
 struct SelectArgs {
   const float* scores;
   int64_t row_stride;
   int32_t* idx;
   int64_t* offsets_dev;
-  void* ws;            // workspace of select_workspace_bytes(slots, nchunk)
+  void* ws;            // workspace of select_workspace_bytes(slots, nchunk) (or the long path's)
   int64_t total;       // offsets[H]
   int S, H;
   int c0, c1;          // candidates are positions [c0, c1)
@@ -103,6 +109,10 @@ struct SelectArgs {
 };
 size_t select_workspace_bytes(int slots, int nchunk);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+size_t select_long_workspace_bytes(int slots);
+// Heads per long-path launch for heads of nchunk chunks (0: the device holds fewer).
+int select_long_batch_heads(int nchunk);
+hipError_t launch_select_long(const SelectArgs& a, hipStream_t s, bool first_batch);
 
 // Row gather of K and V into packed caches.
 struct CompactArgs {

@@ -372,7 +372,10 @@ fam_status fam_budgets_from_ratios(int H, const double* ratios, int64_t t, int64
  *               share a workspace must be ordered on one stream.
  *
  * Requirements: H >= 0, 1 <= S; every head's candidate count (S minus the
- * forced rows) at most 131072. H == 0 is a no-op (nothing is written).
+ * forced rows) at most 2^20 (up to 131072 in three launches over chunks of
+ * 4096 candidates; beyond, one round-based launch after a fill, which waits
+ * across its workgroups and sizes each launch to the workgroups the device
+ * holds at once). H == 0 is a no-op (nothing is written).
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED (too many candidates),
  * FAM_ERR_WORKSPACE (missing or too small workspace), FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
@@ -397,16 +400,16 @@ size_t evict_select_workspace_size(int H, int S, int sinks, int recent);
  * calls no allocating routine; the caller still passes every input and
  * output. Every call on one GPU shares that GPU's array: calls that may
  * overlap on one GPU (different streams without ordering) race and give
- * unspecified results; calls ordered on one stream are safe. The array
- * needs no clearing (evict_select's workspace contents on entry do not
- * matter). On its first call on a device the library looks up and keeps
- * the array's address there (the one piece of state it keeps besides the
- * error string).
+ * unspecified results; calls ordered on one stream are safe. What must
+ * start cleared is cleared by the call's own kernels. On its first call on
+ * a device the library looks up and keeps the array's address there (with
+ * a per-device occupancy figure, the only state it keeps besides the error
+ * string).
  *
  * Arguments, outputs and errors as evict_select, without the workspace;
  * FAM_ERR_UNSUPPORTED when evict_select_workspace_size(H, S, sinks, recent)
  * exceeds FAM_NOALLOC_SCRATCH_BYTES (e.g. 64 heads of 131072 candidates;
- * 8 such heads, or 56 heads of 120000, fit).
+ * 8 such heads, 56 heads of 120000, and heads beyond 131072 candidates fit).
  * ---------------------------------------------------------------------- */
 #define FAM_NOALLOC_SCRATCH_BYTES (64u << 20)
 fam_status evict_select_noalloc(const float* scores, int64_t score_row_stride, int H, int S,

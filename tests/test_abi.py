@@ -204,8 +204,13 @@ def test_evict_select_validation():
     assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, ws, None) == INVALID
     b = np.array([10, 10], dtype=np.int64)
     assert lib.evict_select(FAKE, 99, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, ws, None) == INVALID
-    big = lib.evict_select_workspace_size(2, 200000, 4, 4)
-    assert lib.evict_select(FAKE, 200000, 2, 200000, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, big, None) == UNSUPPORTED
+    S_big = (1 << 20) + 9                       # 2^20 + 1 candidates per head
+    big = lib.evict_select_workspace_size(2, S_big, 4, 4)
+    assert lib.evict_select(FAKE, S_big, 2, S_big, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, big, None) == UNSUPPORTED
+    # beyond 131072 candidates the round-based path's workspace does not grow with S
+    assert (lib.evict_select_workspace_size(8, 300000, 4, 512)
+            == lib.evict_select_workspace_size(8, (1 << 20) + 516, 4, 512)
+            < lib.evict_select_workspace_size(8, 131072 + 516, 4, 512))
     assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE, ws - 1, None) == WORKSPACE
     assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, None, ws, None) == WORKSPACE
     assert lib.evict_select(FAKE, 100, 2, 100, b.ctypes.data, 4, 4, FAKE, FAKE, FAKE + 8, ws, None) == INVALID

@@ -117,6 +117,39 @@ def test_select_more_heads_than_a_batch():
         assert torch.equal(vn[o[h]:o[h + 1]].view(torch.int16), v[h, rows].view(torch.int16))
 
 
+@pytest.mark.parametrize("seed,H,S,sinks,recent,kind", [
+    (20, 8, 300000, 4, 512, "mass"), (21, 3, 131072 + 4 + 512 + 1, 4, 512, "nasty"),
+    (22, 56, 150000, 4, 32, "exp"), (23, 2, (1 << 20) + 516, 4, 512, "ties"),
+    (24, 4, 200003, 0, 0, "split"),
+])
+def test_select_beyond_131072_candidates(seed, H, S, sinks, recent, kind):
+    """The round-based path (more than 131072 candidates a head): mass-like
+    heavy-tailed scores with the 128k layer's Dirichlet budget mix at 300000
+    positions x 8 heads, special values, Exp(1) scores over 56 heads (more
+    heads than one launch holds), all-equal scores at the largest size (every
+    key in one bin, lowest positions win), and scores with few distinct
+    values so that the last level splits equal keys across chunks."""
+    say(f"select long path seed={seed} H={H} S={S} {kind}")
+    rng = np.random.default_rng(seed)
+    if kind == "mass":
+        scores = (rng.exponential(size=(H, S)) ** 3).astype(np.float32)
+        ratios = 8 * 0.15 * rng.dirichlet(np.ones(H))
+        budgets = [int(np.floor(r * S)) for r in ratios]
+    elif kind == "nasty":
+        scores = nasty(rng, H, S)
+        budgets = [int(x) for x in rng.integers(0, S + 8, H)]
+    elif kind == "exp":
+        scores = rng.exponential(size=(H, S)).astype(np.float32)
+        budgets = [4096, 2048, 1024, 512] * (H // 4)
+    elif kind == "ties":
+        scores = np.full((H, S), 0.5, dtype=np.float32)
+        budgets = [S // 3, 777]
+    else:
+        scores = rng.integers(0, 3, size=(H, S)).astype(np.float32)
+        budgets = [S // 2 + 1, S // 3, 100000, 5]
+    assert_select_equal(scores, budgets, sinks, recent)
+
+
 def test_select_unaligned_row_stride():
     say("unaligned score rows")
     rng = np.random.default_rng(9)

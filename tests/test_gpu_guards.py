@@ -111,7 +111,8 @@ def test_score_entry_points_stay_inside_their_outputs(B, Hq, Hkv, S, d, W):
         x.check(n)
 
 
-@pytest.mark.parametrize("H,S,sinks,recent", [(5, 5000, 4, 64), (7, 3001, 4, 32), (3, 100001, 4, 512)])
+@pytest.mark.parametrize("H,S,sinks,recent", [(5, 5000, 4, 64), (7, 3001, 4, 32), (3, 100001, 4, 512),
+                                              (3, 150001, 4, 512)])
 def test_eviction_entry_points_stay_inside_their_outputs(H, S, sinks, recent):
     say(f"guards: select/compact/ranking H={H} S={S}")
     rng = np.random.default_rng(S)
