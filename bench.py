@@ -29,6 +29,7 @@ import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
 import time
 
@@ -120,6 +121,50 @@ def cpu_baseline(wl, prefix=32768):
             "seconds": round(dt, 3),
             "sample": (f"oracle LSE + mass (fp64) on the first {prefix} positions of KV group 0 "
                        f"({g} query heads) of {wl.name}; {pairs} causal pairs")}
+
+
+def oracle_select_compact(wl, host, with_decode):
+    """The oracle's select (lexsort) + compact (fancy-index gather of K and V)
+    timed on the host: on the headline workload's masses and K/V, and on
+    every cell of the decode-time sweep (the cells' K/V drawn on the device
+    as the sweep draws them, copied to the host)."""
+    from oracle import select_oracle  # test infrastructure: only this leg uses it
+    out = {}
+    t0 = time.perf_counter()
+    idx, off = select_oracle.select(host["mass"], host["budgets"], wl.sinks, wl.recent)
+    t1 = time.perf_counter()
+    select_oracle.compact(host["k"], idx, off)
+    select_oracle.compact(host["v"], idx, off)
+    t2 = time.perf_counter()
+    nbytes = 4 * wl.Hkv * wl.S + 4 * int(off[-1]) + 2 * 2 * int(off[-1]) * wl.d * 2
+    out[wl.name] = {"select_s": round(t1 - t0, 4), "compact_s": round(t2 - t1, 4), "bytes": nbytes,
+                    "GBps": round(nbytes / (t2 - t0) / 1e9, 3)}
+    if with_decode:
+        cells = workloads.decode_sweep()
+        dev = torch.device("cuda:0")
+        rows = []
+        for S in workloads.DECODE_CONTEXTS:
+            first = [c for c in cells if c.S == S][0]
+            gen = torch.Generator(device=dev).manual_seed(first.seed * 1000003 + S)
+            kd = torch.randn((first.H, S, first.d), generator=gen, device=dev, dtype=torch.float32).to(first.dtype)
+            vd = torch.randn((first.H, S, first.d), generator=gen, device=dev, dtype=torch.float32).to(first.dtype)
+            kh, vh = kd.cpu().view(torch.int16).numpy(), vd.cpu().view(torch.int16).numpy()
+            del kd, vd
+            scores = first.scores()
+            for cell in [c for c in cells if c.S == S]:
+                budgets = [cell.budget] * cell.H
+                t0 = time.perf_counter()
+                idx, off = select_oracle.select(scores, budgets, cell.sinks, cell.recent)
+                t1 = time.perf_counter()
+                select_oracle.compact(kh, idx, off)
+                select_oracle.compact(vh, idx, off)
+                t2 = time.perf_counter()
+                nbytes = 4 * cell.H * S + 4 * int(off[-1]) + 2 * 2 * int(off[-1]) * cell.d * 2
+                rows.append({"S": S, "budget": cell.budget, "select_s": round(t1 - t0, 4),
+                             "compact_s": round(t2 - t1, 4), "GBps": round(nbytes / (t2 - t0) / 1e9, 3)})
+            del kh, vh
+        out["decode_sweep"] = rows
+    return out
 
 
 def kvpop_target_row(steps, q, k, lse, wl, work, stream):
@@ -379,6 +424,165 @@ def decode_row(runs, stream):
                           "unit": "GB/s", "frac": round(tot_bytes / (tot_us * 1e-6) / PEAK_HBM_BYTES, 4)}}
 
 
+def clock_state():
+    """The GPU's current clocks as the SMI tools report them (None if neither runs)."""
+    for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
+        try:
+            res = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
+        except (OSError, subprocess.TimeoutExpired):
+            continue
+        if res.returncode == 0 and res.stdout.strip():
+            try:
+                rep = json.loads(res.stdout)
+            except ValueError:
+                return {"tool": cmd[0], "report": res.stdout.strip()[:2000]}
+            return {"tool": cmd[0], "clocks_mhz": _clock_values(rep)}
+    return None
+
+
+def _clock_values(rep):
+    """{clock name: [current MHz per instance]} from an SMI JSON report."""
+    out = {}
+
+    def walk(x, name=None):
+        if isinstance(x, dict):
+            if "clk" in x and isinstance(x["clk"], dict) and "value" in x["clk"]:
+                key = (name or "clk").rstrip("_0123456789")
+                out.setdefault(key, []).append(x["clk"]["value"])
+                return
+            for k, v in x.items():
+                walk(v, k)
+        elif isinstance(x, list):
+            for v in x:
+                walk(v, name)
+    walk(rep)
+    return out
+
+
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
+    """Time `steps` steps of the path on one workload (HIP events on the
+    launch stream); optionally repeat select + compact after a 512 MiB fill
+    that evicts the L2s and the MALL. `clocks`, a list, receives the clock
+    state read while the timed steps run."""
+    dev = q.device
+    bi = wl.budget_inputs()
+    budgets = (fam.fam_budgets_from_ratios(bi["ratios"], bi["t"]).tolist() if "ratios" in bi
+               else [bi["uniform"]] * wl.Hkv)
+    kept, offsets_host = fam.evict_plan(budgets, wl.S, wl.sinks, wl.recent)
+    total = int(offsets_host[-1])
+    B, Hq, Hkv, S, d = 1, wl.Hq, wl.Hkv, wl.S, wl.d
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
+    mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    idx = torch.empty(total, dtype=torch.int32, device=dev)
+    offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=dev)
+    ws = torch.empty(max(16, fam.evict_select_workspace_size(Hkv, S, wl.sinks, wl.recent)),
+                     dtype=torch.uint8, device=dev)
+    k_new = torch.empty((total, d), dtype=k.dtype, device=dev)
+    v_new = torch.empty((total, d), dtype=v.dtype, device=dev)
+    knorm = torch.empty((B, Hkv, fam.fam_key_norm_parts(S)), dtype=torch.float32, device=dev)
+    mass_ws = torch.empty(max(16, fam.fam_mass_workspace_size(B, Hq, Hkv, S)), dtype=torch.uint8, device=dev)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+
+    def step(events=None):
+        if events:
+            events[0].record(stream)
+        fam.fam_key_norms(k, knorm=knorm)
+        fam.fam_lse(q, k, lse=lse, knorm=knorm)
+        if events:
+            events[1].record(stream)
+        fam.fam_mass(q, k, lse, wl.W, mass=mass, workspace=mass_ws)
+        if events:
+            events[2].record(stream)
+        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets,
+                         workspace=ws)
+        if events:
+            events[3].record(stream)
+        fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)
+        if events:
+            events[4].record(stream)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev[i])
+    if clocks is not None:   # read while the GPU works through the enqueued steps
+        clocks.append(clock_state())
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    names = ["fam_lse", "fam_mass", "evict_select", "kv_compact"]
+    per_step = {n: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)] for j, n in enumerate(names)}
+    ms = {n: float(np.mean(v)) for n, v in per_step.items()}
+    work = algorithmic_work(wl, total)
+    t_fam = (ms["fam_lse"] + ms["fam_mass"]) * 1e-3
+    t_ec = (ms["evict_select"] + ms["kv_compact"]) * 1e-3
+    lines = {
+        "fam_lse": ("mfma", work["lse_flops"] / (ms["fam_lse"] * 1e-3), PEAK_BF16_FLOPS, "TFLOP/s"),
+        "fam_mass": ("mfma", work["mass_flops"] / (ms["fam_mass"] * 1e-3), PEAK_BF16_FLOPS, "TFLOP/s"),
+        "evict_select": ("hbm", work["select_bytes"] / (ms["evict_select"] * 1e-3), PEAK_HBM_BYTES, "GB/s"),
+        "kv_compact": ("hbm", work["compact_bytes"] / (ms["kv_compact"] * 1e-3), PEAK_HBM_BYTES, "GB/s"),
+    }
+    flushed = None
+    if flushed_reps > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        fe = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(flushed_reps)]
+        for i, e in enumerate(fe):
+            flush.fill_(i & 0x7f)
+            e[0].record(stream)
+            fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets, workspace=ws)
+            e[1].record(stream)
+            fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        sel_us = float(np.median([e[0].elapsed_time(e[1]) for e in fe])) * 1e3
+        cmp_us = float(np.median([e[1].elapsed_time(e[2]) for e in fe])) * 1e3
+        nbytes = work["select_bytes"] + work["compact_bytes"]
+        flushed = {"reps": flushed_reps, "caches": "512 MiB fill before every rep (untimed)",
+                   "select_us": round(sel_us, 1), "compact_us": round(cmp_us, 1), "bytes": nbytes,
+                   "GBps": round(nbytes / ((sel_us + cmp_us) * 1e-6) / 1e9, 1),
+                   "hbm_frac": round(nbytes / ((sel_us + cmp_us) * 1e-6) / PEAK_HBM_BYTES, 4)}
+        del flush
+    return {"names": names, "ms": ms, "per_step": per_step, "lines": lines, "work": work,
+            "budgets": budgets, "total": total, "mass": mass, "lse": lse, "idx": idx, "offsets": offsets,
+            "ms_step": wall * 1e3 / steps, "t_fam": t_fam, "t_ec": t_ec, "flushed": flushed}
+
+
+def workload_row(wl, steps, warmup, stream):
+    """One more workload's step, timed on its own inputs (for the lines of
+    the other score workloads beside the headline one)."""
+    dev = torch.device("cuda:0")
+    t = wl.tensors()
+    q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
+    del t
+    run = time_step(wl, q, k, v, steps, warmup, stream)
+    ms, work = run["ms"], run["work"]
+    out = {"workload": wl.name, "steps": steps,
+           "config": {"q_heads": wl.Hq, "kv_heads": wl.Hkv, "seq_len": wl.S, "head_dim": wl.d, "window": wl.W,
+                      "sinks": wl.sinks, "kept_total": run["total"]},
+           "pairs_per_s": work["causal_pairs"] / (run["ms_step"] * 1e-3),
+           "fam_mfma_frac": round((work["lse_flops"] + work["mass_flops"]) / run["t_fam"] / PEAK_BF16_FLOPS, 4),
+           "evict_compact_gbps": round((work["select_bytes"] + work["compact_bytes"]) / run["t_ec"] / 1e9, 2),
+           "evict_compact_hbm_frac": round((work["select_bytes"] + work["compact_bytes"]) / run["t_ec"]
+                                           / PEAK_HBM_BYTES, 4),
+           "kernel_ms": {n: round(ms[n], 4) for n in run["names"]}}
+    del q, k, v, run
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -396,6 +600,10 @@ def main():
                     help="timed runs per cell of the decode-time eviction sweep; 0 skips it")
     ap.add_argument("--chunked-only", action="store_true",
                     help="run only the chunked prefill-compress row (for a kernel trace of it alone)")
+    ap.add_argument("--other-workloads", type=int, default=5,
+                    help="timed steps of the 8k and 32k score workloads beside the 128k line; 0 skips them")
+    ap.add_argument("--flushed-reps", type=int, default=5,
+                    help="select + compact reps after a cache-evicting fill (headline workload); 0 skips them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -423,65 +631,13 @@ def main():
         print(json.dumps({"chunked_prefill": chunked_row(max(1, args.chunked_runs), q, k, v, wl, stream)}),
               flush=True)
         return
-    bi = wl.budget_inputs()
-    budgets = (fam.fam_budgets_from_ratios(bi["ratios"], bi["t"]).tolist() if "ratios" in bi
-               else [bi["uniform"]] * wl.Hkv)
-    kept, offsets_host = fam.evict_plan(budgets, wl.S, wl.sinks, wl.recent)
-    total = int(offsets_host[-1])
-    B, Hq, Hkv, S, d = 1, wl.Hq, wl.Hkv, wl.S, wl.d
-    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev)
-    mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
-    idx = torch.empty(total, dtype=torch.int32, device=dev)
-    offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=dev)
-    ws = torch.empty(max(16, fam.evict_select_workspace_size(Hkv, S, wl.sinks, wl.recent)),
-                     dtype=torch.uint8, device=dev)
-    k_new = torch.empty((total, d), dtype=k.dtype, device=dev)
-    v_new = torch.empty((total, d), dtype=v.dtype, device=dev)
-
-    knorm = torch.empty((B, Hkv, fam.fam_key_norm_parts(S)), dtype=torch.float32, device=dev)
-    mass_ws = torch.empty(fam.fam_mass_workspace_size(B, Hq, Hkv, S), dtype=torch.uint8, device=dev)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-
-    def step(events=None):
-        if events:
-            events[0].record(stream)
-        fam.fam_key_norms(k, knorm=knorm)
-        fam.fam_lse(q, k, lse=lse, knorm=knorm)
-        if events:
-            events[1].record(stream)
-        fam.fam_mass(q, k, lse, wl.W, mass=mass, workspace=mass_ws)
-        if events:
-            events[2].record(stream)
-        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets,
-                         workspace=ws)
-        if events:
-            events[3].record(stream)
-        fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)
-        if events:
-            events[4].record(stream)
-
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev[i])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-
-    names = ["fam_lse", "fam_mass", "evict_select", "kv_compact"]
-    per_step = {n: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)] for j, n in enumerate(names)}
-    ms = {n: float(np.mean(v)) for n, v in per_step.items()}
-    work = algorithmic_work(wl, total)
-    ms_step = wall * 1e3 / args.steps
-    t_fam = (ms["fam_lse"] + ms["fam_mass"]) * 1e-3
-    t_ec = (ms["evict_select"] + ms["kv_compact"]) * 1e-3
-    lines = {
-        "fam_lse": ("mfma", work["lse_flops"] / (ms["fam_lse"] * 1e-3), PEAK_BF16_FLOPS, "TFLOP/s"),
-        "fam_mass": ("mfma", work["mass_flops"] / (ms["fam_mass"] * 1e-3), PEAK_BF16_FLOPS, "TFLOP/s"),
-        "evict_select": ("hbm", work["select_bytes"] / (ms["evict_select"] * 1e-3), PEAK_HBM_BYTES, "GB/s"),
-        "kv_compact": ("hbm", work["compact_bytes"] / (ms["kv_compact"] * 1e-3), PEAK_HBM_BYTES, "GB/s"),
-    }
+    clocks = []
+    run = time_step(wl, q, k, v, args.steps, args.warmup, stream, flushed_reps=args.flushed_reps, clocks=clocks)
+    names, ms, per_step, lines, work = run["names"], run["ms"], run["per_step"], run["lines"], run["work"]
+    budgets, total, mass, lse = run["budgets"], run["total"], run["mass"], run["lse"]
+    B, Hq, Hkv, S = 1, wl.Hq, wl.Hkv, wl.S
+    ms_step = run["ms_step"]
+    t_fam, t_ec = run["t_fam"], run["t_ec"]
     traffic = measured_traffic(args.workload)
     roof = {}
     for n, (bound, ach, peak, unit) in lines.items():
@@ -504,7 +660,7 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": wl.name, "batch": 1, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
-                   "head_dim": d, "window": wl.W, "sinks": wl.sinks, "recent": wl.recent,
+                   "head_dim": wl.d, "window": wl.W, "sinks": wl.sinks, "recent": wl.recent,
                    "kept_total": total, "budgets": [int(b) for b in budgets]},
         "fam_mfma_frac": round((work["lse_flops"] + work["mass_flops"]) / t_fam / PEAK_BF16_FLOPS, 4),
         "fam_pairs_per_s": work["causal_pairs"] / t_fam,
@@ -515,6 +671,8 @@ def main():
         "kernel_ms_min": {n: round(float(np.min(per_step[n])), 4) for n in names},
         "roofline": dict(roof[dominant], kernel=dominant),
         "roofline_all": roof,
+        "evict_compact_flushed": run["flushed"],
+        "clock_state_during_steps": clocks[0] if clocks else None,
     }
     if args.target_steps > 0:
         out["kvpop_target"] = kvpop_target_row(args.target_steps, q, k, lse, wl, work, stream)
@@ -526,8 +684,19 @@ def main():
         out["chunked_prefill"] = chunked_row(args.chunked_runs, q, k, v, wl, stream)
     if args.decode_runs > 0:
         out["decode_sweep"] = decode_row(args.decode_runs, stream)
+    host = None
+    if not args.no_cpu_baseline:   # host copies for the oracle's select + compact, taken before freeing
+        host = {"mass": mass[0].cpu().numpy(), "k": k[0].cpu().view(torch.int16).numpy(),
+                "v": v[0].cpu().view(torch.int16).numpy(), "budgets": budgets}
+    del q, k, v, mass, lse, run
+    torch.cuda.empty_cache()
+    if args.other_workloads > 0 and args.workload == "llama-128k":
+        out["other_workloads"] = [workload_row(WORKLOADS[n](), args.other_workloads, 1, stream)
+                                  for n in ("qwen3-4b-8k", "long-trace-32k")]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
+        out["cpu_baseline"]["cpu_model"] = cpu_model()
+        out["cpu_baseline"]["select_compact"] = oracle_select_compact(wl, host, args.decode_runs > 0)
     print(json.dumps(out), flush=True)
 
 

@@ -205,7 +205,8 @@ struct OverlapArgs {
   int64_t* common;  // [H]
   int H, S;
 };
-constexpr int kOverlapMaxS = 1 << 18;  // bitmap of the positions in 32 KiB of LDS
+constexpr int kOverlapWindow = 1 << 18;  // positions per LDS bitmap (32 KiB)
+constexpr int kOverlapMaxS = 1 << 28;    // longer heads take several windows
 hipError_t launch_overlap(const OverlapArgs& a, hipStream_t s);
 
 // Running top-k cut-off over static ranks.

@@ -29,7 +29,8 @@
 // partials in block order, so the result is deterministic.
 //
 // overlap_kernel: common[h] = |set(a_h) & set(b_h)| for two kept-index lists
-// per head, with a bitmap of the head's positions in LDS.
+// per head, with a bitmap of the head's positions in LDS (per window of
+// 262144 positions).
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -309,43 +310,51 @@ __global__ __launch_bounds__(kOverlapThreads) void overlap_kernel(OverlapArgs p)
   extern __shared__ uint32_t bits[];
   __shared__ int64_t part[kOverlapThreads / 64];
   const int h = blockIdx.x;
-  const int words = (p.S + 31) / 32;
-  for (int w = threadIdx.x; w < words; w += kOverlapThreads) bits[w] = 0u;
-  __syncthreads();
-  // batches of kOverlapBatch entries per thread, all loads in flight (clamped
-  // indices; entries past the list are dropped after the loads)
   const int64_t a0 = p.off_a[h], a1 = p.off_a[h + 1];
-  for (int64_t i0 = a0 + threadIdx.x; i0 < a1; i0 += (int64_t)kOverlapThreads * kOverlapBatch) {
-    int x[kOverlapBatch];
-#pragma unroll
-    for (int u = 0; u < kOverlapBatch; ++u) {
-      const int64_t i = i0 + (int64_t)u * kOverlapThreads;
-      x[u] = p.idx_a[i < a1 ? i : a1 - 1];
-    }
-#pragma unroll
-    for (int u = 0; u < kOverlapBatch; ++u)
-      if (i0 + (int64_t)u * kOverlapThreads < a1 && x[u] >= 0 && x[u] < p.S)
-        atomicOr(&bits[x[u] >> 5], 1u << (x[u] & 31));
-  }
-  __syncthreads();
-  int64_t cnt = 0;
   const int64_t b0 = p.off_b[h], b1 = p.off_b[h + 1];
-  for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)kOverlapThreads * kOverlapBatch) {
-    int x[kOverlapBatch];
+  int64_t cnt = 0;
+  // windows of kOverlapWindow positions, one bitmap in LDS each (one window
+  // up to 262144 positions; longer heads re-read both lists per window)
+  for (int w0 = 0; w0 < p.S; w0 += kOverlapWindow) {
+    const int wn = p.S - w0 < kOverlapWindow ? p.S - w0 : kOverlapWindow;
+    const int words = (wn + 31) / 32;
+    for (int w = threadIdx.x; w < words; w += kOverlapThreads) bits[w] = 0u;
+    __syncthreads();
+    // batches of kOverlapBatch entries per thread, all loads in flight
+    // (clamped indices; entries past the list are dropped after the loads)
+    for (int64_t i0 = a0 + threadIdx.x; i0 < a1; i0 += (int64_t)kOverlapThreads * kOverlapBatch) {
+      int x[kOverlapBatch];
 #pragma unroll
-    for (int u = 0; u < kOverlapBatch; ++u) {
-      const int64_t i = i0 + (int64_t)u * kOverlapThreads;
-      x[u] = p.idx_b[i < b1 ? i : b1 - 1];
-    }
+      for (int u = 0; u < kOverlapBatch; ++u) {
+        const int64_t i = i0 + (int64_t)u * kOverlapThreads;
+        x[u] = p.idx_a[i < a1 ? i : a1 - 1];
+      }
 #pragma unroll
-    for (int u = 0; u < kOverlapBatch; ++u) {
-      const int y = x[u];
-      if (i0 + (int64_t)u * kOverlapThreads < b1 && y >= 0 && y < p.S && ((bits[y >> 5] >> (y & 31)) & 1u)) {
-        // count each position of b once: clear it after the first hit
-        const uint32_t old = atomicAnd(&bits[y >> 5], ~(1u << (y & 31)));
-        if ((old >> (y & 31)) & 1u) ++cnt;
+      for (int u = 0; u < kOverlapBatch; ++u) {
+        const int y = x[u] - w0;
+        if (i0 + (int64_t)u * kOverlapThreads < a1 && x[u] >= w0 && y < wn)
+          atomicOr(&bits[y >> 5], 1u << (y & 31));
       }
     }
+    __syncthreads();
+    for (int64_t i0 = b0 + threadIdx.x; i0 < b1; i0 += (int64_t)kOverlapThreads * kOverlapBatch) {
+      int x[kOverlapBatch];
+#pragma unroll
+      for (int u = 0; u < kOverlapBatch; ++u) {
+        const int64_t i = i0 + (int64_t)u * kOverlapThreads;
+        x[u] = p.idx_b[i < b1 ? i : b1 - 1];
+      }
+#pragma unroll
+      for (int u = 0; u < kOverlapBatch; ++u) {
+        const int y = x[u] - w0;
+        if (i0 + (int64_t)u * kOverlapThreads < b1 && x[u] >= w0 && y < wn && ((bits[y >> 5] >> (y & 31)) & 1u)) {
+          // count each position of b once: clear it after the first hit
+          const uint32_t old = atomicAnd(&bits[y >> 5], ~(1u << (y & 31)));
+          if ((old >> (y & 31)) & 1u) ++cnt;
+        }
+      }
+    }
+    __syncthreads();
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o);
@@ -403,7 +412,8 @@ hipError_t launch_cost_ratio(const RankArgs& rank_scores, const RankArgs& rank_i
 
 hipError_t launch_overlap(const OverlapArgs& a, hipStream_t s) {
   if (a.H == 0) return hipSuccess;
-  const size_t lds = (size_t)((a.S + 31) / 32) * sizeof(uint32_t);
+  const int window = a.S < kOverlapWindow ? a.S : kOverlapWindow;
+  const size_t lds = (size_t)((window + 31) / 32) * sizeof(uint32_t);
   hipLaunchKernelGGL(overlap_kernel, dim3((unsigned)a.H), dim3(kOverlapThreads), lds, s, a);
   return hipGetLastError();
 }

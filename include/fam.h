@@ -631,7 +631,8 @@ size_t fam_eviction_cost_ratio_workspace_size(int H, int n);
  *   idx_a, idx_b          device int32 kept positions (e.g. evict_select's)
  *   offsets_a, offsets_b  device [H + 1] int64, non-decreasing
  *   common                device out, [H] int64
- * Requirements: S <= 262144 (a bitmap of the positions in LDS).
+ * Requirements: S <= 2^28 (a bitmap of 262144 positions in LDS per pass;
+ * longer heads take one pass per 262144 positions).
  * Errors: FAM_ERR_INVALID_ARG, FAM_ERR_UNSUPPORTED, FAM_ERR_HIP.
  * ---------------------------------------------------------------------- */
 fam_status fam_retention_overlap(const int32_t* idx_a, const int64_t* offsets_a,

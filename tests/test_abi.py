@@ -332,7 +332,7 @@ def test_ranking_validation():
     assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE, FAKE, cws - 1, None) == WORKSPACE
     assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE, None, cws, None) == WORKSPACE
     assert lib.fam_eviction_cost(FAKE, 100, FAKE, 2, 100, FAKE, FAKE + 4, cws, None) == INVALID   # workspace alignment
-    assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 2, 300000, FAKE, None) == UNSUPPORTED
+    assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 2, (1 << 28) + 1, FAKE, None) == UNSUPPORTED
     assert lib.fam_retention_overlap(FAKE, FAKE, None, FAKE, 2, 100, FAKE, None) == INVALID
     assert lib.fam_retention_overlap(FAKE, FAKE, FAKE, FAKE, 0, 100, None, None) == 0
 

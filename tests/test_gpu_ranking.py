@@ -119,6 +119,33 @@ def test_retention_overlap_on_selections():
         assert got[h] / len(a) == rk.retention_recall(a, b)
 
 
+def test_retention_overlap_at_300000_positions_eight_heads():
+    """Beyond one 262144-position bitmap: the selections of two scorers over
+    8 heads of 300000 positions (the round-based select path), counted in
+    two windows, against set arithmetic; lists with positions on both sides
+    of the window edge and duplicates."""
+    say("fam_retention_overlap S=300000 H=8")
+    H, S = 8, 300000
+    rng = np.random.default_rng(17)
+    a_scores = rng.exponential(size=(H, S)).astype(np.float32)
+    b_scores = (a_scores + 0.5 * rng.random((H, S))).astype(np.float32)
+    budgets = [int(x) for x in rng.integers(1000, S, H)]
+    ia, oa = fam.evict_select(torch.from_numpy(a_scores).to(DEV), budgets, 4, 512)
+    ib, ob = fam.evict_select(torch.from_numpy(b_scores).to(DEV), budgets, 4, 512)
+    got = fam.fam_retention_overlap(ia, oa, ib, ob, S).cpu().numpy()
+    ia_h, oa_h, ib_h, ob_h = ia.cpu().numpy(), oa.cpu().numpy(), ib.cpu().numpy(), ob.cpu().numpy()
+    for h in range(H):
+        a = ia_h[oa_h[h]:oa_h[h + 1]]
+        b = ib_h[ob_h[h]:ob_h[h + 1]]
+        assert got[h] == len(set(a.tolist()) & set(b.tolist())), h
+    edge = 1 << 18
+    a = torch.tensor([edge - 1, edge, edge, S - 1, 5, -3], dtype=torch.int32, device=DEV)
+    b = torch.tensor([edge, edge - 1, S - 1, S - 1, S, 5, edge + 1], dtype=torch.int32, device=DEV)
+    oa1 = torch.tensor([0, 6], dtype=torch.int64, device=DEV)
+    ob1 = torch.tensor([0, 7], dtype=torch.int64, device=DEV)
+    assert fam.fam_retention_overlap(a, oa1, b, ob1, S).cpu().tolist() == [4]
+
+
 def test_retention_overlap_duplicates_and_out_of_range():
     say("fam_retention_overlap hand cases")
     a = torch.tensor([1, 2, 3, 3, 9, 0, 5], dtype=torch.int32, device=DEV)
