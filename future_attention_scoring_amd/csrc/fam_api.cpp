@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -58,6 +59,16 @@ fam_status launched(hipError_t e, hipStream_t s, const char* what) {
   return ok();
 }
 
+// The bits of an enum argument as an int: a C caller may pass any value, and
+// loading an out-of-range value as the C++ enum type would be undefined.
+template <typename E>
+int enum_bits(const E* e) {
+  static_assert(sizeof(E) == sizeof(int), "enums of the ABI are int-sized");
+  int v;
+  std::memcpy(&v, e, sizeof v);
+  return v;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 constexpr int kMaxSeq = 1 << 28;
@@ -71,10 +82,10 @@ struct ScoreShape {
   int rows() const { return Sq > 0 ? Sq : S; }
 };
 
-fam_status check_scores(const void* q, const void* k, fam_dtype dtype, const ScoreShape& s) {
+fam_status check_scores(const void* q, const void* k, int dtype, const ScoreShape& s) {
   if (!q || !k) return fail(FAM_ERR_INVALID_ARG, "q and k must be non-null");
   if (dtype != FAM_BF16 && dtype != FAM_FP16)
-    return fail(FAM_ERR_UNSUPPORTED, "dtype %d is not bf16 or fp16", (int)dtype);
+    return fail(FAM_ERR_UNSUPPORTED, "dtype %d is not bf16 or fp16", dtype);
   if (s.B < 1 || s.Hq < 1 || s.Hkv < 1 || s.S < 1)
     return fail(FAM_ERR_INVALID_ARG, "B, Hq, Hkv and S must be >= 1 (got %d, %d, %d, %d)",
                 s.B, s.Hq, s.Hkv, s.S);
@@ -170,7 +181,7 @@ size_t lse_split_bytes(const ScoreShape& s, int nks) {
   return nks > 1 ? (size_t)(nks + 1) * s.B * s.Hq * s.rows() * sizeof(float) : 0;
 }
 
-fam::Elem elem_of(fam_dtype dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
+fam::Elem elem_of(int dt) { return dt == FAM_BF16 ? fam::Elem::kBf16 : fam::Elem::kFp16; }
 
 // Partial slices of the group-sum mass pass. From kMassRangeMinS keys on
 // (while at most kMassMaxRanges ranges cover the query rows and the grid of
@@ -206,7 +217,7 @@ size_t per_head_split_bytes(const ScoreShape& s, int nsplit) {
 
 // Group-sum mass pass on a validated shape: as many splits as wanted and as
 // the workspace holds (none without one).
-fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype dtype,
+fam_status mass_group(const void* q, const void* k, const float* lse, int dtype,
                       const ScoreShape& s, int W, float scale, float* mass, void* workspace,
                       size_t workspace_bytes, hipStream_t stream, const char* what) {
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
@@ -235,7 +246,7 @@ fam_status mass_group(const void* q, const void* k, const float* lse, fam_dtype 
 // Key norms, the bounded first pass and the group-sum mass pass. The
 // key-norm partial maxima ([B * Hkv][P] floats, P <= S) occupy the start of
 // `mass` until the mass pass overwrites it.
-fam_status compute_all(const void* q, const void* k, fam_dtype dtype, const ScoreShape& s, int W,
+fam_status compute_all(const void* q, const void* k, int dtype, const ScoreShape& s, int W,
                        float scale, float* lse, float* mass, void* workspace,
                        size_t workspace_bytes, hipStream_t hs, const char* who) {
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
@@ -280,7 +291,7 @@ Plan plan_of(int S, int sinks, int recent) {
 extern "C" {
 
 const char* fam_status_string(fam_status st) {
-  switch (st) {
+  switch (enum_bits(&st)) {
     case FAM_OK: return "FAM_OK";
     case FAM_ERR_INVALID_ARG: return "FAM_ERR_INVALID_ARG";
     case FAM_ERR_UNSUPPORTED: return "FAM_ERR_UNSUPPORTED";
@@ -295,8 +306,9 @@ const char* fam_last_error(void) { return g_error.c_str(); }
 
 int fam_key_norm_parts(int S) { return S < 1 ? 0 : (S < fam::kNormParts ? S : fam::kNormParts); }
 
-fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, int d,
+fam_status fam_key_norms(const void* k, fam_dtype dtype_arg, int B, int Hkv, int S, int d,
                          int64_t k_sb, int64_t k_sh, int64_t k_ss, float* knorm, void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
   const ScoreShape s{B, Hkv, Hkv, S, d, k_sb, k_sh, k_ss, k_sb, k_sh, k_ss, 0};
   fam_status st = check_scores(k, k, dtype, s);
   if (st != FAM_OK) return st;
@@ -306,9 +318,10 @@ fam_status fam_key_norms(const void* k, fam_dtype dtype, int B, int Hkv, int S, 
                     "fam_key_norms launch");
 }
 
-fam_status fam_lse(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
+fam_status fam_lse(const void* q, const void* k, fam_dtype dtype_arg, int B, int Hq, int Hkv, int S,
                    int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
                    int64_t k_ss, float scale, const float* knorm, float* lse, void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
@@ -332,10 +345,11 @@ size_t fam_compute_workspace_size(int B, int Hq, int Hkv, int Sq, int Sk) {
   return lse_bytes > mass_bytes ? lse_bytes : mass_bytes;
 }
 
-fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype, int B, int Hq,
+fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype_arg, int B, int Hq,
                     int Hkv, int S, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb,
                     int64_t k_sh, int64_t k_ss, int W, float scale, float* mass, void* workspace,
                     size_t workspace_bytes, void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
@@ -343,11 +357,12 @@ fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dt
                     static_cast<hipStream_t>(stream), "fam_mass launch");
 }
 
-fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype, int B,
+fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam_dtype dtype_arg, int B,
                              int Hq, int Hkv, int S, int d, int64_t q_sb, int64_t q_sh,
                              int64_t q_ss, int64_t k_sb, int64_t k_sh, int64_t k_ss, int W,
                              float scale, float* mass_q, void* workspace, size_t workspace_bytes,
                              void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
@@ -377,7 +392,8 @@ size_t fam_mass_per_head_workspace_size(int B, int Hq, int Hkv, int S) {
 }
 
 fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, int W, float eps,
-                            fam_aggregate aggregate, float* target, void* stream) {
+                            fam_aggregate aggregate_arg, float* target, void* stream) {
+  const int aggregate = enum_bits(&aggregate_arg);
   if (!mass_q || !target) return fail(FAM_ERR_INVALID_ARG, "mass_q and target must be non-null");
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1)
     return fail(FAM_ERR_INVALID_ARG, "B, Hq, Hkv and S must be >= 1 (got %d, %d, %d, %d)", B, Hq, Hkv, S);
@@ -385,17 +401,18 @@ fam_status fam_kvpop_target(const float* mass_q, int B, int Hq, int Hkv, int S, 
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(FAM_ERR_INVALID_ARG, "eps must be finite and >= 0");
   if (aggregate != FAM_AGG_MAX && aggregate != FAM_AGG_MEAN)
-    return fail(FAM_ERR_INVALID_ARG, "aggregate %d is not FAM_AGG_MAX or FAM_AGG_MEAN", (int)aggregate);
+    return fail(FAM_ERR_INVALID_ARG, "aggregate %d is not FAM_AGG_MAX or FAM_AGG_MEAN", aggregate);
   if ((reinterpret_cast<uintptr_t>(mass_q) | reinterpret_cast<uintptr_t>(target)) & 3u)
     return fail(FAM_ERR_INVALID_ARG, "mass_q and target must be 4-byte aligned");
   const fam::TargetArgs a{mass_q, target, B, Hq, Hkv, S, W, eps, aggregate == FAM_AGG_MEAN ? 1 : 0};
   return launched(fam::launch_target(a, static_cast<hipStream_t>(stream)), static_cast<hipStream_t>(stream), "fam_kvpop_target launch");
 }
 
-fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv, int S,
+fam_status fam_compute(const void* q, const void* k, fam_dtype dtype_arg, int B, int Hq, int Hkv, int S,
                        int d, int64_t q_sb, int64_t q_sh, int64_t q_ss, int64_t k_sb, int64_t k_sh,
                        int64_t k_ss, int W, float scale, float* lse, float* mass,
                        void* workspace, size_t workspace_bytes, void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
   const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
   fam_status st = check_scores(q, k, dtype, s);
   if (st != FAM_OK) return st;
@@ -403,11 +420,12 @@ fam_status fam_compute(const void* q, const void* k, fam_dtype dtype, int B, int
                      static_cast<hipStream_t>(stream), "fam_compute");
 }
 
-fam_status fam_compute_chunk(const void* q, const void* k, fam_dtype dtype, int B, int Hq, int Hkv,
+fam_status fam_compute_chunk(const void* q, const void* k, fam_dtype dtype_arg, int B, int Hq, int Hkv,
                              int Sq, int Sk, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss,
                              int64_t k_sb, int64_t k_sh, int64_t k_ss, int W, float scale,
                              float* lse, float* mass, void* workspace, size_t workspace_bytes,
                              void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
   if (Sq < 1 || Sq > Sk)
     return fail(FAM_ERR_INVALID_ARG, "query rows Sq = %d must be in [1, Sk = %d]", Sq, Sk);
   const ScoreShape s{B, Hq, Hkv, Sk, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, Sq};
