@@ -424,8 +424,19 @@ def decode_row(runs, stream):
                           "unit": "GB/s", "frac": round(tot_bytes / (tot_us * 1e-6) / PEAK_HBM_BYTES, 4)}}
 
 
+def under_profiler():
+    """True inside a rocprofv3 run. Its preloaded library starts the GPU runtime
+    in every child process, so a child that replaces itself with another
+    program (the SMI tools are scripts started through /usr/bin/env) must not
+    be spawned there."""
+    return any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", "")
+
+
 def clock_state():
-    """The GPU's current clocks as the SMI tools report them (None if neither runs)."""
+    """The GPU's current clocks as the SMI tools report them (None if neither
+    runs; not queried under a profiler)."""
+    if under_profiler():
+        return {"skipped": "not queried under a profiler"}
     for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
         try:
             res = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
