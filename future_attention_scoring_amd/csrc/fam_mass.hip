@@ -158,10 +158,12 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const int ntw = r_hi - r_lo;
     const int nfull_h = PER_HEAD ? max(0, r_hi - max(t_full, r_lo))   // per query head
                                  : max(0, t1 - max(t_full, t0));
-    // step u -> (tile, query head of the group); the latest tiles come first
-    auto tile_of = [&](int u) { return PER_HEAD ? r_hi - 1 - u % ntw : t1 - 1 - u / g; };
-    auto head_of = [&](int u) { return PER_HEAD ? u / ntw : u % g; };
-    auto is_full = [&](int u) { return PER_HEAD ? u % ntw < nfull_h : u < nfull_h * g; };
+    // step u = sq * D + sr with D = ntw (PER_HEAD: sq the query head, sr the
+    // tile counted from the latest) or D = g (sq the tile counted from the
+    // latest, sr the query head); the loop keeps the pair (sq, sr) and steps
+    // it instead of dividing every step
+    auto tile_at = [&](int sq_, int sr_) { return PER_HEAD ? r_hi - 1 - sr_ : t1 - 1 - sq_; };
+    auto head_at = [&](int sq_, int sr_) { return PER_HEAD ? sq_ : sr_; };
 
     // staging offsets (elements) inside a tile: chunk c of this thread is
     // off0 + c * pass_stride (the host guarantees kQTile * q_ss < 2^31)
@@ -171,9 +173,9 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.Sq;
     u32x4_t st[CHUNKS];
     float lst = 0.f;
-    auto load_step = [&](int u) {
-      const int t = tile_of(u);
-      const int gi = head_of(u);
+    auto load_step = [&](int sq_, int sr_) {
+      const int t = tile_at(sq_, sr_);
+      const int gi = head_at(sq_, sr_);
       const int r0 = t * kQTile;
       const uint16_t* tile = qgroup + gi * p.q_sh + (int64_t)r0 * p.q_ss;   // uniform
       if (r0 + kQTile <= p.Sq) {
@@ -214,17 +216,26 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       u_begin = r_lo < r_hi ? (t1 - r_hi) * g : 0;
       u_end = r_lo < r_hi ? (t1 - r_lo) * g : 0;
     }
-    if (u_begin < u_end) {
-      load_step(u_begin);
+    const int nsr = PER_HEAD ? ntw : g;   // D above
+    int cq = 0, cr = 0;   // (sq, sr) of step u
+    if (u_begin < u_end) {   // then nsr >= 1
+      cq = u_begin / nsr;
+      cr = u_begin - cq * nsr;
+      load_step(cq, cr);
       store_step(u_begin & 1);
       __syncthreads();
     }
     for (int u = u_begin; u < u_end; ++u) {
       const bool more = u + 1 < u_end;
-      if (more) load_step(u + 1);
+      int nq = cq, nr = cr + 1;   // (sq, sr) of step u + 1
+      if (nr == nsr) {
+        nr = 0;
+        ++nq;
+      }
+      if (more) load_step(nq, nr);
       const int buf = u & 1;
-      const int i0t = tile_of(u) * kQTile;
-      const bool full = is_full(u);
+      const int i0t = tile_at(cq, cr) * kQTile;
+      const bool full = PER_HEAD ? cr < nfull_h : u < nfull_h * g;
 #pragma unroll
       for (int rb = 0; rb < kQTile / 32; ++rb) {
         const int i0 = i0t + 32 * rb;
@@ -260,12 +271,14 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         mid[0] = 0.f;
         mid[1] = 0.f;
       }
-      if (PER_HEAD && u % ntw == ntw - 1) {  // this query head is complete
-        write_cols(head_dst(head_of(u)));
+      if (PER_HEAD && cr == ntw - 1) {  // this query head is complete
+        write_cols(head_dst(cq));
         top[0] = top[1] = mid[0] = mid[1] = 0.f;
       }
       if (more) store_step((u + 1) & 1);
       __syncthreads();
+      cq = nq;
+      cr = nr;
     }
   }
 
