@@ -432,22 +432,35 @@ def under_profiler():
     return any(k.startswith("ROCPROF") for k in os.environ) or "rocprof" in os.environ.get("LD_PRELOAD", "")
 
 
-def clock_state():
+def clock_state(keep_busy=None):
     """The GPU's current clocks as the SMI tools report them (None if neither
-    runs; not queried under a profiler)."""
+    runs; not queried under a profiler). `keep_busy`, if given, is called
+    (and must wait for its own work) over and over while the query runs, so
+    that the tool samples the clocks under that load and not after it."""
     if under_profiler():
         return {"skipped": "not queried under a profiler"}
     for cmd in (["amd-smi", "metric", "--clock", "--json"], ["rocm-smi", "--showclocks", "--json"]):
         try:
-            res = subprocess.run(cmd, capture_output=True, text=True, timeout=30)
-        except (OSError, subprocess.TimeoutExpired):
+            proc = subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True)
+        except OSError:
             continue
-        if res.returncode == 0 and res.stdout.strip():
+        t_end = time.perf_counter() + 30.0
+        busy_calls = 0
+        while keep_busy is not None and proc.poll() is None and time.perf_counter() < t_end:
+            keep_busy()
+            busy_calls += 1
+        try:
+            out, _ = proc.communicate(timeout=max(1.0, t_end - time.perf_counter()))
+        except subprocess.TimeoutExpired:
+            proc.kill()
+            proc.communicate()
+            continue
+        if proc.returncode == 0 and out.strip():
             try:
-                rep = json.loads(res.stdout)
+                rep = json.loads(out)
             except ValueError:
-                return {"tool": cmd[0], "report": res.stdout.strip()[:2000]}
-            return {"tool": cmd[0], "clocks_mhz": _clock_values(rep)}
+                return {"tool": cmd[0], "report": out.strip()[:2000]}
+            return {"tool": cmd[0], "clocks_mhz": _clock_values(rep), "steps_run_during_query": busy_calls}
     return None
 
 
@@ -529,10 +542,13 @@ def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
     t0 = time.perf_counter()
     for i in range(steps):
         step(ev[i])
-    if clocks is not None:   # read while the GPU works through the enqueued steps
-        clocks.append(clock_state())
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    if clocks is not None:   # after the timed steps, under more of the same steps (untimed)
+        def busy():
+            step()
+            torch.cuda.synchronize()
+        clocks.append(clock_state(busy))
 
     names = ["fam_lse", "fam_mass", "evict_select", "kv_compact"]
     per_step = {n: [ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(steps)] for j, n in enumerate(names)}
