@@ -141,7 +141,9 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
   const int split = (blockIdx.x / nbh) % nks;
   const int slot = (blockIdx.x / nbh) / nks;
   const int b = bh / p.Hkv, h = bh % p.Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform over the wave: kept in a scalar register, so that
+  // the per-wave window and causal tests below are scalar work
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
   const int unit = slot * kWaves + wave;

@@ -102,7 +102,9 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   const int split = rtiles > 0 ? p.nsplit - 1 - rest / nkb_all : (PER_HEAD ? 0 : rest % p.nsplit);
   const int kbi = rtiles > 0 ? rest % nkb_all : (PER_HEAD ? rest : rest / p.nsplit);
   const int b = bh / p.Hkv, h = bh % p.Hkv;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  // the wave index is uniform over the wave: kept in a scalar register, so that
+  // the per-wave window and causal tests below are scalar work
+  const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int half = lane >> 5, col = lane & 31;
 
   const int j0 = kbi * kKeysPerWG;
