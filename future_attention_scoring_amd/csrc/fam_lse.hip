@@ -54,6 +54,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 64;
 constexpr int kKeyTile = 64;
 constexpr float kMinBoundSum = 0x1p-80f;
+constexpr int kReadAhead = 4;   // bounded pass: A-fragment reads ahead of their MFMAs (KS >= 4)
 
 // Causal and ragged-tile mask of a 32x32 block (keys on rows, queries on columns).
 __device__ __forceinline__ void mask_block(f32x16_t& acc, int kb, int qblock, int S, int lane) {
@@ -254,13 +255,30 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
           // the wave's MFMA block at raised priority: its matrix work issues
           // while the other waves of the SIMD are in their exp/sum phase
           __builtin_amdgcn_s_setprio(1);
+          // the A fragments are read kReadAhead k-steps ahead of their MFMAs:
+          // the first kReadAhead reads, then per k-step two MFMAs and the
+          // read kReadAhead steps ahead, then the last MFMAs (without the
+          // scheduling groups the compiler waits for each read just before
+          // its MFMAs)
+          u32x4_t af[KS];
+#pragma unroll
+          for (int ks = 0; ks < kReadAhead; ++ks)
+            af[ks] = *reinterpret_cast<const u32x4_t*>(&buf[(32 * kk2 + col) * PITCH + ks * 16 + half * 8]);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(
-                &buf[(32 * kk2 + col) * PITCH + ks * 16 + half * 8]);
-            acc0 = Mma<T>::run(a, qf[0][ks], acc0);
-            acc1 = Mma<T>::run(a, qf[1][ks], acc1);
+            if (ks + kReadAhead < KS)
+              af[ks + kReadAhead] = *reinterpret_cast<const u32x4_t*>(
+                  &buf[(32 * kk2 + col) * PITCH + (ks + kReadAhead) * 16 + half * 8]);
+            acc0 = Mma<T>::run(af[ks], qf[0][ks], acc0);
+            acc1 = Mma<T>::run(af[ks], qf[1][ks], acc1);
           }
+          __builtin_amdgcn_sched_group_barrier(0x100, kReadAhead, 0);   // DS reads
+#pragma unroll
+          for (int ks = 0; ks < KS - kReadAhead; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kReadAhead, 0);
           __builtin_amdgcn_s_setprio(0);
           bound_update(acc0, kb, qp0, p.S, lane, p.c, M[0], l[0]);
           bound_update(acc1, kb, qp0 + 32, p.S, lane, p.c, M[1], l[1]);
