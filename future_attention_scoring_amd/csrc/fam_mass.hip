@@ -41,8 +41,6 @@
 //     caches would not hold them; within a range they share a few MB of Q.
 //     The per-query-head mode splits the same way, one partial slice per
 //     query head.
-#include <algorithm>
-
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -295,23 +293,13 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
 }
 
 // mass = sum over the splits of the partial column sums, in split order.
-// The output is `rows` rows of S floats ([B*Hkv] or [B*Hq]); row r is written
-// by workgroups whose ids are r mod 8, i.e. (ids going round-robin over the
-// chip's 8 XCDs) from XCD r % 8. evict_select places head r on that same
-// XCD, so when it reads the masses next they are in its L2.
-constexpr int kXcds = 8;
-__global__ __launch_bounds__(kThreads) void mass_reduce_kernel(const float* part, float* mass, int rows,
-                                                               int S, int nsplit, int per_row) {
-  const int x = blockIdx.x % kXcds, j = blockIdx.x / kXcds;
-  const int row = x + kXcds * (j / per_row);   // per_row workgroups per row
-  if (row >= rows) return;
-  const int64_t n = (int64_t)rows * S;
-  const int64_t base = (int64_t)row * S;
-  const int stride = per_row * kThreads;
-  for (int e = (j % per_row) * kThreads + threadIdx.x; e < S; e += stride) {
-    float acc = part[base + e];
-    for (int k = 1; k < nsplit; ++k) acc += part[(int64_t)k * n + base + e];
-    mass[base + e] = acc;
+__global__ __launch_bounds__(kThreads) void mass_reduce_kernel(const float* part, float* mass,
+                                                               int64_t n, int nsplit) {
+  const int64_t stride = (int64_t)gridDim.x * kThreads;
+  for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
+    float acc = part[e];
+    for (int k = 1; k < nsplit; ++k) acc += part[(int64_t)k * n + e];
+    mass[e] = acc;
   }
 }
 
@@ -328,13 +316,10 @@ hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
   else
     hipLaunchKernelGGL((mass_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   if (nsplit > 1) {
-    const int rows = a.B * (per_head ? a.Hq : a.Hkv);
-    // about four elements per thread, at most 512 workgroups per row
-    const int per_row = std::max(1, std::min(512, (a.S + 4 * kThreads - 1) / (4 * kThreads)));
-    const int64_t blocks = (int64_t)kXcds * per_row * ((rows + kXcds - 1) / kXcds);
-    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(mass_reduce_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, s, a.part,
-                       per_head ? a.mass_q : a.mass, rows, a.S, nsplit, per_row);
+    const int64_t n = (int64_t)a.B * (per_head ? a.Hq : a.Hkv) * a.S;
+    const int64_t blocks = (n + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(mass_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
+                       dim3(kThreads), 0, s, a.part, per_head ? a.mass_q : a.mass, n, nsplit);
   }
   return hipGetLastError();
 }
