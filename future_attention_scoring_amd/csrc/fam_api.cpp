@@ -116,6 +116,18 @@ float resolve_scale(float scale, int d) {
 // Arguments of the first pass and of the key-norm pass; with `knorm` non-null
 // the row shift is the Cauchy-Schwarz bound built from the key-norm partial
 // maxima stored there ([B * Hkv][nkn] floats).
+// The mass pass starts its accumulators at -L/c (c = scale * log2 e); below
+// c = 2^-100 that quotient could overflow. Such a scale is refused by every
+// entry point that runs the mass pass.
+fam_status check_mass_scale(float scale, int d) {
+  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  const float c = resolve_scale(scale, d);
+  if (!(c >= 0x1p-100f))
+    return fail(FAM_ERR_UNSUPPORTED, "scale %g is below what the mass pass supports (scale * log2(e) >= 2^-100)",
+                (double)scale);
+  return FAM_OK;
+}
+
 fam::LseArgs lse_args(const void* q, const void* k, const ScoreShape& s, float scale, float* lse,
                       float* knorm) {
   fam::LseArgs a{};
@@ -222,7 +234,7 @@ fam_status mass_group(const void* q, const void* k, const float* lse, int dtype,
                       size_t workspace_bytes, hipStream_t stream, const char* what) {
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
-  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  if (const fam_status sc = check_mass_scale(scale, s.d); sc != FAM_OK) return sc;
   if (workspace && !aligned16(workspace))
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   const size_t per_split = (size_t)s.B * s.Hkv * s.S * sizeof(float);
@@ -251,7 +263,7 @@ fam_status compute_all(const void* q, const void* k, int dtype, const ScoreShape
                        size_t workspace_bytes, hipStream_t hs, const char* who) {
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
-  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  if (const fam_status sc = check_mass_scale(scale, s.d); sc != FAM_OK) return sc;
   if (workspace && !aligned16(workspace))
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   fam::LseArgs a = lse_args(q, k, s, scale, lse, mass);
@@ -368,7 +380,7 @@ fam_status fam_mass_per_head(const void* q, const void* k, const float* lse, fam
   if (st != FAM_OK) return st;
   if (!lse || !mass_q) return fail(FAM_ERR_INVALID_ARG, "lse and mass_q must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
-  if (!std::isfinite(scale)) return fail(FAM_ERR_INVALID_ARG, "scale must be finite");
+  if (const fam_status sc = check_mass_scale(scale, s.d); sc != FAM_OK) return sc;
   if (workspace && !aligned16(workspace))
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   fam::MassArgs a = mass_args(q, k, lse, s, W, scale, nullptr, mass_q, nullptr, 1);

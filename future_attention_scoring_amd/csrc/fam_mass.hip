@@ -18,10 +18,11 @@
 //     half-waves hold disjoint query rows and are added once at the end).
 //   * The workgroup walks the 64-row query tiles i >= j0 + W of every query
 //     head of the group, latest tile first. Each (tile, head) step stages 64
-//     query rows and their normalisers (in base-2 units) through
-//     double-buffered LDS; the tile base is a uniform pointer and a thread's
-//     chunks sit at one 32-bit offset plus multiples of a uniform stride (no
-//     per-chunk registers).
+//     query rows and, per row, -L/c (the normaliser in base-2 units over the
+//     scale c, where the row's accumulators start) through double-buffered
+//     LDS; the tile base is a uniform pointer and a thread's chunks sit at one
+//     32-bit offset plus multiples of a uniform stride (no per-chunk
+//     registers).
 //   * Only band steps (those that contain some i < j + W) evaluate the window
 //     predicate. Keys that no query can reach (j > S - 1 - W) get exactly 0.
 //   * Per-step partial sums are added into a mid-level accumulator that is
@@ -55,27 +56,35 @@ static_assert(kKeysPerWG == kMassKeysPerWG, "host and kernel key-block size");
 constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
 static_assert(kQTile == kMassQTile, "host and kernel query-tile size");
 
-// Sum of exp2(c*s - L) over one 32x32 block, no window predicate.
-__device__ __forceinline__ float block_sum_full(const f32x16_t& acc, const float (&lv)[16], float c) {
+// The accumulator of a block starts at -L_i / c for its query row i, so that
+// after the MFMAs it holds s - L_i / c and each term is exp2(c * acc): one
+// multiply per element, and the normalisers need no registers beside the
+// accumulators once the MFMAs have started. (The rounding of -L_i / c and of
+// the accumulation is scaled back down by c: about |L_i| * 2^-21 in the
+// exponent, i.e. a relative error near 1e-5 at most per term.)
+//
+// Sum of exp2(c * acc) over one 32x32 block, no window predicate.
+__device__ __forceinline__ float block_sum_full(const f32x16_t& acc, float c) {
   float e[16];
 #pragma unroll
-  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(acc[v], c, -lv[v]));
+  for (int v = 0; v < 16; ++v) e[v] = fast_exp2(acc[v] * c);
   return sum16(e);
 }
 
 // Same with the window predicate i >= j + W.
-__device__ __forceinline__ float block_sum_band(const f32x16_t& acc, const float (&lv)[16], int i0,
-                                                int jk, int W, int lane, float c) {
+__device__ __forceinline__ float block_sum_band(const f32x16_t& acc, int i0, int jk, int W, int lane,
+                                                float c) {
   if (i0 + 31 < jk + W) return 0.f;
   float e[16];
   const int j = jk + (lane & 31);
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
-    const float x = fast_exp2(fmaf(acc[v], c, -lv[v]));
+    const float x = fast_exp2(acc[v] * c);
     e[v] = i0 + acc_row(v, lane) < j + W ? 0.f : x;
   }
   return sum16(e);
 }
+
 
 // PER_HEAD: the steps run head-major (all tiles of one query head, then the
 // next) and each query head's column sums go to mass_q [B, Hq, S] when its
@@ -206,7 +215,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         // copy, so that it is not hoisted out of the loop into a spilled register)
         int t = tid;
         asm volatile("" : "+v"(t));
-        sl[buf][t] = lst * kLog2e;
+        sl[buf][t] = -lst * kLog2e / p.c;   // the accumulators' start (+inf rows: -inf)
       }
     };
 
@@ -251,7 +260,10 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
             lv[4 * r4 + 2] = x[2];
             lv[4 * r4 + 3] = x[3];
           }
-          f32x16_t acc0 = {}, acc1 = {};
+          f32x16_t acc0, acc1;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) acc0[v] = lv[v];
+          acc1 = acc0;
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
             const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&sq[buf][(32 * rb + col) * PITCH + ks * 16 + half * 8]);
@@ -259,11 +271,11 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
             acc1 = Mma<T>::run(a, kf[1][ks], acc1);
           }
           if (full) {
-            mid[0] += block_sum_full(acc0, lv, p.c);
-            mid[1] += block_sum_full(acc1, lv, p.c);
+            mid[0] += block_sum_full(acc0, p.c);
+            mid[1] += block_sum_full(acc1, p.c);
           } else {
-            mid[0] += block_sum_band(acc0, lv, i0, jw, Wr, lane, p.c);
-            mid[1] += block_sum_band(acc1, lv, i0, jw + 32, Wr, lane, p.c);
+            mid[0] += block_sum_band(acc0, i0, jw, Wr, lane, p.c);
+            mid[1] += block_sum_band(acc1, i0, jw + 32, Wr, lane, p.c);
           }
         }
       }

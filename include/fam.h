@@ -155,7 +155,10 @@ fam_status fam_lse(const void* q, const void* k, fam_dtype dtype,
  *          bytes the long-sequence ranges give way to the short-sequence
  *          splits, as many as fit; NULL: no splits. Calls sharing a
  *          workspace must be ordered on one stream.
- *   other arguments and requirements as for fam_lse.
+ *   other arguments and requirements as for fam_lse, except that a positive
+ *   scale with scale * log2(e) < 2^-100 returns FAM_ERR_UNSUPPORTED (the
+ *   pass starts each row's accumulators at -lse / scale in base-2 units;
+ *   the same holds for fam_mass_per_head, fam_compute and fam_compute_chunk).
  * ---------------------------------------------------------------------- */
 fam_status fam_mass(const void* q, const void* k, const float* lse, fam_dtype dtype,
                     int B, int Hq, int Hkv, int S, int d,

@@ -128,6 +128,30 @@ def test_mass_per_head_validation():
     assert lib.fam_mass_per_head(*bad) == INVALID
 
 
+def test_mass_pass_refuses_a_scale_below_its_range():
+    """The mass pass starts each row's accumulators at -lse / c (c = scale *
+    log2 e): a positive scale with c < 2^-100 is refused before any launch by
+    every entry point that runs the pass. (Accepted scales are exercised by
+    the GPU tests; these calls all fail validation, so nothing launches.)"""
+    lib = fam.load()
+    tiny = float(np.float32(2.0 ** -101))
+    mass = [FAKE, FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, tiny, FAKE, None, 0, None]
+    assert lib.fam_mass(*mass) == UNSUPPORTED
+    assert lib.fam_mass_per_head(*mass) == UNSUPPORTED
+    st = lib.fam_compute(FAKE, FAKE, 0, 1, 4, 2, 64, 128, 0, 8192, 128, 0, 8192, 128, 4, tiny, FAKE, FAKE,
+                         None, 0, None)
+    assert st == UNSUPPORTED
+    st = lib.fam_compute_chunk(FAKE, FAKE, 0, 1, 4, 2, 32, 64, 128, 0, 4096, 128, 0, 8192, 128, 4, tiny, FAKE,
+                               FAKE, None, 0, None)
+    assert st == UNSUPPORTED
+    # a negative W is still reported first as an invalid argument
+    bad = list(mass); bad[15] = -1
+    assert lib.fam_mass(*bad) == INVALID
+    # non-finite scales are invalid, as before
+    bad = list(mass); bad[16] = float("nan")
+    assert lib.fam_mass(*bad) == INVALID
+
+
 def test_mass_per_head_workspace_size():
     """One [B, Hq, S] fp32 slice per range of 64 query tiles of 64 rows from
     65536 keys on (at most 128 ranges); no split below."""
