@@ -103,6 +103,28 @@ def test_explicit_scale_and_strided_views():
     check_mass(mass.cpu().numpy(), mass_ref, S, 16)
 
 
+@pytest.mark.parametrize("scale", [1e-30, 1e-12, 0.5, 1.0])
+def test_scales_from_the_smallest_accepted_to_sharp(scale):
+    """The mass pass starts each row's accumulators at -lse / c (c = scale *
+    log2 e) and forms exp2(c * acc); at tiny scales -lse / c reaches ~1e31
+    and swamps every dot product, at 1.0 (11x the default at d = 128) the
+    normalisers reach 87 and the masses span 23 decades (sharper scales put
+    masses below what fp32 represents, which would test the number format
+    rather than the kernels). Both passes against the oracle at the parity
+    bar, and the per-query-head mass summed over each group against the
+    group mass."""
+    say(f"scale {scale}")
+    q, k = rand_inputs(31, 1, 4, 2, 300, 128, torch.bfloat16, spread=1.3)
+    lse, mass = fam.fam_compute(q.to(DEV), k.to(DEV), 5, scale=scale)
+    mass_q = fam.fam_mass_per_head(q.to(DEV), k.to(DEV), lse, 5, scale=scale)
+    torch.cuda.synchronize()
+    lse_ref, mass_ref = fo.fam(to64(q), to64(k), 5, scale=scale)
+    check_lse(lse.cpu().numpy(), lse_ref)
+    check_mass(mass.cpu().numpy(), mass_ref, 300, 5)
+    grp = mass_q.view(1, 2, 2, 300).sum(dim=2).cpu().numpy()
+    np.testing.assert_allclose(grp, mass.cpu().numpy(), rtol=1e-5, atol=0)
+
+
 def test_tiny_workload_full_oracle():
     wl = workloads.tiny()
     say(wl.name)
