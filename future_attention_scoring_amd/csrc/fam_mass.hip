@@ -144,6 +144,11 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     for (int ks = 0; ks < KS; ++ks)
       kf[blk][ks] = ok ? load16(kbase + (int64_t)key * p.k_ss + ks * 16 + half * 8) : zero16();
   }
+  // wait for the K fragments here, once: otherwise the compiler's wait
+  // analysis keeps them pending across the loop's back edge and waits for
+  // every load in flight (the next step's Q tile included) before each step's
+  // first MFMA
+  __builtin_amdgcn_s_waitcnt(0);
 
   float top[2] = {0.f, 0.f}, mid[2] = {0.f, 0.f};
   // this wave's column sums (the two half-waves added) into dst[key]
@@ -184,6 +189,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.Sq;
     u32x4_t st[CHUNKS];
     float lst = 0.f;
+    bool lrow_ok = true;
     auto load_step = [&](int sq_, int sr_) {
       const int t = tile_at(sq_, sr_);
       const int gi = head_at(sq_, sr_);
@@ -202,8 +208,10 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       }
       if (tid < kQTile) {
         const int row = r0 + tid;
-        const float x = lgroup[(int64_t)gi * p.Sq + min(row, p.Sq - 1)];
-        lst = row < p.Sq ? x : kInf;
+        // the loaded value is not used until the store, so that this wave
+        // does not wait for the step's loads here
+        lst = lgroup[(int64_t)gi * p.Sq + min(row, p.Sq - 1)];
+        lrow_ok = row < p.Sq;
       }
     };
     const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
@@ -215,7 +223,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         // copy, so that it is not hoisted out of the loop into a spilled register)
         int t = tid;
         asm volatile("" : "+v"(t));
-        sl[buf][t] = -lst * kLog2e / p.c;   // the accumulators' start (+inf rows: -inf)
+        sl[buf][t] = lrow_ok ? -lst * kLog2e / p.c : -kInf;   // the accumulators' start (rows past Sq: -inf)
       }
     };
 
