@@ -188,9 +188,12 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     const uint16_t* qgroup = p.q + b * p.q_sb + (int64_t)(h * g) * p.q_sh;
     const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.Sq;
     u32x4_t st[CHUNKS];
+    // the step's 64 normalisers are loaded and staged by one wave, lw, which
+    // rotates with the step so that no SIMD carries that work every step
     float lst = 0.f;
     bool lrow_ok = true;
-    auto load_step = [&](int sq_, int sr_) {
+    const float nlc = -kLog2e / p.c;   // accumulator start = lse * nlc
+    auto load_step = [&](int sq_, int sr_, int lw) {
       const int t = tile_at(sq_, sr_);
       const int gi = head_at(sq_, sr_);
       const int r0 = t * kQTile;
@@ -206,8 +209,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
           st[c] = load16(qgroup + gi * p.q_sh + (int64_t)row * p.q_ss + (id % CPR) * 8);
         }
       }
-      if (tid < kQTile) {
-        const int row = r0 + tid;
+      if (wave == lw) {
+        const int row = r0 + lane;
         // the loaded value is not used until the store, so that this wave
         // does not wait for the step's loads here
         lst = lgroup[(int64_t)gi * p.Sq + min(row, p.Sq - 1)];
@@ -215,15 +218,15 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       }
     };
     const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
-    auto store_step = [&](int buf) {
+    auto store_step = [&](int buf, int lw) {
 #pragma unroll
       for (int c = 0; c < CHUNKS; ++c) store16(&sq[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
-      if (tid < kQTile) {
-        // the slot's address is formed here from the thread index (an opaque
+      if (wave == lw) {
+        // the slot's address is formed here from the lane index (an opaque
         // copy, so that it is not hoisted out of the loop into a spilled register)
-        int t = tid;
+        int t = lane;
         asm volatile("" : "+v"(t));
-        sl[buf][t] = lrow_ok ? -lst * kLog2e / p.c : -kInf;   // the accumulators' start (rows past Sq: -inf)
+        sl[buf][t] = lrow_ok ? lst * nlc : -kInf;   // the accumulators' start (rows past Sq: -inf)
       }
     };
 
@@ -240,8 +243,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     if (u_begin < u_end) {   // then nsr >= 1
       cq = u_begin / nsr;
       cr = u_begin - cq * nsr;
-      load_step(cq, cr);
-      store_step(u_begin & 1);
+      load_step(cq, cr, u_begin & 3);
+      store_step(u_begin & 1, u_begin & 3);
       __syncthreads();
     }
     for (int u = u_begin; u < u_end; ++u) {
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         nr = 0;
         ++nq;
       }
-      if (more) load_step(nq, nr);
+      if (more) load_step(nq, nr, (u + 1) & 3);
       const int buf = u & 1;
       const int i0t = tile_at(cq, cr) * kQTile;
       const bool full = PER_HEAD ? cr < nfull_h : u < nfull_h * g;
@@ -297,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         write_cols(head_dst(cq));
         top[0] = top[1] = mid[0] = mid[1] = 0.f;
       }
-      if (more) store_step((u + 1) & 1);
+      if (more) store_step((u + 1) & 1, (u + 1) & 3);
       __syncthreads();
       cq = nq;
       cr = nr;
