@@ -54,6 +54,7 @@ constexpr int kKeysPerWave = 64;
 constexpr int kKeysPerWG = kKeysPerWave * kWaves;
 static_assert(kKeysPerWG == kMassKeysPerWG, "host and kernel key-block size");
 constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
+constexpr int kReadAhead = 2;   // A-fragment reads issued this many k-steps ahead
 static_assert(kQTile == kMassQTile, "host and kernel query-tile size");
 
 // The accumulator of a block starts at -L_i / c for its query row i, so that
@@ -275,12 +276,30 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
 #pragma unroll
           for (int v = 0; v < 16; ++v) acc0[v] = lv[v];
           acc1 = acc0;
+          // the A fragments are read kReadAhead k-steps ahead of their MFMAs:
+          // the normaliser reads and the first kReadAhead fragment reads,
+          // then per k-step two MFMAs and the read kReadAhead steps ahead,
+          // then the last MFMAs (left to itself the compiler reads one step
+          // ahead)
+          u32x4_t af[KS];
+#pragma unroll
+          for (int ks = 0; ks < kReadAhead; ++ks)
+            af[ks] = *reinterpret_cast<const u32x4_t*>(&sq[buf][(32 * rb + col) * PITCH + ks * 16 + half * 8]);
 #pragma unroll
           for (int ks = 0; ks < KS; ++ks) {
-            const u32x4_t a = *reinterpret_cast<const u32x4_t*>(&sq[buf][(32 * rb + col) * PITCH + ks * 16 + half * 8]);
-            acc0 = Mma<T>::run(a, kf[0][ks], acc0);
-            acc1 = Mma<T>::run(a, kf[1][ks], acc1);
+            if (ks + kReadAhead < KS)
+              af[ks + kReadAhead] = *reinterpret_cast<const u32x4_t*>(
+                  &sq[buf][(32 * rb + col) * PITCH + (ks + kReadAhead) * 16 + half * 8]);
+            acc0 = Mma<T>::run(af[ks], kf[0][ks], acc0);
+            acc1 = Mma<T>::run(af[ks], kf[1][ks], acc1);
           }
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 + kReadAhead, 0);   // DS reads
+#pragma unroll
+          for (int ks = 0; ks < KS - kReadAhead; ++ks) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kReadAhead, 0);
           if (full) {
             mid[0] += block_sum_full(acc0, p.c);
             mid[1] += block_sum_full(acc1, p.c);
