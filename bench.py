@@ -581,7 +581,27 @@ def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
                    "select_us": round(sel_us, 1), "compact_us": round(cmp_us, 1), "bytes": nbytes,
                    "GBps": round(nbytes / ((sel_us + cmp_us) * 1e-6) / 1e9, 1),
                    "hbm_frac": round(nbytes / ((sel_us + cmp_us) * 1e-6) / PEAK_HBM_BYTES, 4)}
-        del flush
+        # what a plain device copy of the compaction's bytes (the kept K and V
+        # rows read once and written once) reaches on this machine, warm and
+        # after the same fill: the practical ceiling of the HBM-bound kernels
+        half = work["compact_bytes"] // 2
+        src = torch.empty(half, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        ref = {}
+        for mode in ("warm", "flushed"):
+            ce = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(flushed_reps)]
+            dst.copy_(src)
+            for i, e in enumerate(ce):
+                if mode == "flushed":
+                    flush.fill_(i & 0x7f)
+                e[0].record(stream)
+                dst.copy_(src)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            us = float(np.median([e[0].elapsed_time(e[1]) for e in ce])) * 1e3
+            ref[mode] = {"us": round(us, 1), "GBps": round(2 * half / (us * 1e-6) / 1e9, 1)}
+        flushed["copy_reference"] = dict(ref, bytes=2 * half, kernel="torch copy_ (device to device)")
+        del flush, src, dst
     return {"names": names, "ms": ms, "per_step": per_step, "lines": lines, "work": work,
             "budgets": budgets, "total": total, "mass": mass, "lse": lse, "idx": idx, "offsets": offsets,
             "ms_step": wall * 1e3 / steps, "t_fam": t_fam, "t_ec": t_ec, "flushed": flushed}
