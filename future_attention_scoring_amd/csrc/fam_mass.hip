@@ -19,10 +19,10 @@
 //   * The workgroup walks the 64-row query tiles i >= j0 + W of every query
 //     head of the group, latest tile first. Each (tile, head) step stages 64
 //     query rows and, per row, -L/c (the normaliser in base-2 units over the
-//     scale c, where the row's accumulators start) through double-buffered
-//     LDS; the tile base is a uniform pointer and a thread's chunks sit at one
-//     32-bit offset plus multiples of a uniform stride (no per-chunk
-//     registers).
+//     scale c, where the row's accumulators start) in double-buffered LDS;
+//     the rows go from global memory straight into LDS (a uniform tile base
+//     plus one 32-bit offset per chunk and lane), the next step's while the
+//     current one computes.
 //   * Only band steps (those that contain some i < j + W) evaluate the window
 //     predicate. Keys that no query can reach (j > S - 1 - W) get exactly 0.
 //   * Per-step partial sums are added into a mid-level accumulator that is
@@ -55,6 +55,31 @@ constexpr int kKeysPerWG = kKeysPerWave * kWaves;
 static_assert(kKeysPerWG == kMassKeysPerWG, "host and kernel key-block size");
 constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
 constexpr int kReadAhead = 2;   // A-fragment reads issued this many k-steps ahead
+// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+constexpr int kWaitVm0 = 0x0F70;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16 bytes per lane from global memory (uniform base + per-lane byte
+// offset) into LDS at lds + 16 * lane (gfx950 global_load_lds_dwordx4;
+// M0 holds the LDS address). Written as assembly so that the compiler's
+// wait analysis does not take it for a store that may alias every LDS read
+// (it would wait for it before each read of the other buffer); the caller
+// waits for it (vmcnt) before the barrier that publishes the tile.
+// M0 is named as clobbered (nothing else in these kernels keeps a value in
+// it; the compiler warns that it reserves M0, hence the local pragma).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(off), "s"(base), "s"(lds)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
 static_assert(kQTile == kMassQTile, "host and kernel query-tile size");
 
 // The accumulator of a block starts at -L_i / c for its query row i, so that
@@ -95,8 +120,6 @@ template <int D, typename T, bool PER_HEAD>
 __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
   constexpr int PITCH = D + 8;
   constexpr int KS = D / 16;
-  constexpr int CPR = D / 8;
-  constexpr int CHUNKS = kQTile * CPR / kThreads;
   __shared__ __attribute__((aligned(16))) uint16_t sq[2][kQTile * PITCH];
   __shared__ __attribute__((aligned(16))) float sl[2][kQTile];
 
@@ -182,32 +205,54 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     auto tile_at = [&](int sq_, int sr_) { return PER_HEAD ? r_hi - 1 - sr_ : t1 - 1 - sq_; };
     auto head_at = [&](int sq_, int sr_) { return PER_HEAD ? sq_ : sr_; };
 
-    // staging offsets (elements) inside a tile: chunk c of this thread is
-    // off0 + c * pass_stride (the host guarantees kQTile * q_ss < 2^31)
-    const int off0 = (tid / CPR) * (int)p.q_ss + (tid % CPR) * 8;
-    const int pass_stride = (kThreads / CPR) * (int)p.q_ss;   // uniform
     const uint16_t* qgroup = p.q + b * p.q_sb + (int64_t)(h * g) * p.q_sh;
     const float* lgroup = p.lse + ((int64_t)b * p.Hq + h * g) * p.Sq;
-    u32x4_t st[CHUNKS];
+    // The Q tile goes from global memory straight into LDS (gfx950's
+    // global_load_lds_dwordx4: lane l of a wave instruction fills the 16
+    // bytes at the LDS base + 16 l), so it holds no registers while in
+    // flight. The padded tile is NCH chunks of 64 such slots; slot s is row
+    // s / SPR, 16-byte column s % SPR, and the pad column re-reads the row's
+    // last 16 bytes. Wave w loads chunks w, w + 4, ...; the last chunk goes to
+    // a wave that changes with the step. Offsets are elements inside a tile
+    // (the host guarantees kQTile * q_ss < 2^31).
+    constexpr int SPR = PITCH / 8;
+    constexpr int NCH = kQTile * SPR / 64;
+    constexpr int NPW = NCH / 4;
+    static_assert(kQTile * SPR % 64 == 0 && NCH % 4 == 1, "chunks of the padded tile");
+    uint32_t qoff[NPW + 1];   // bytes
+#pragma unroll
+    for (int j = 0; j <= NPW; ++j) {
+      const int s = (j < NPW ? wave + 4 * j : NCH - 1) * 64 + lane;
+      qoff[j] = (uint32_t)((s / SPR) * (int)p.q_ss + min(s % SPR, SPR - 2) * 8) * 2u;
+    }
+    const uint32_t sq_lds = (uint32_t)(uintptr_t)(lds_void*)&sq[0][0];
+    auto dma = [&](const uint16_t* tile, uint32_t off, int buf, int chunk) {
+      dma16(tile, off, sq_lds + (uint32_t)(buf * kQTile * PITCH * 2 + chunk * 1024));
+    };
     // the step's 64 normalisers are loaded and staged by one wave, lw, which
     // rotates with the step so that no SIMD carries that work every step
     float lst = 0.f;
     bool lrow_ok = true;
     const float nlc = -kLog2e / p.c;   // accumulator start = lse * nlc
-    auto load_step = [&](int sq_, int sr_, int lw) {
+    auto load_step = [&](int sq_, int sr_, int lw, int buf) {
       const int t = tile_at(sq_, sr_);
       const int gi = head_at(sq_, sr_);
       const int r0 = t * kQTile;
+      const int xw = (lw + 2) & 3;   // the wave that loads the last chunk
       const uint16_t* tile = qgroup + gi * p.q_sh + (int64_t)r0 * p.q_ss;   // uniform
       if (r0 + kQTile <= p.Sq) {
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off0 + c * pass_stride);
-      } else {  // ragged last tile: clamp rows (their normaliser is +inf)
+        for (int j = 0; j < NPW; ++j) dma(tile, qoff[j], buf, wave + 4 * j);
+        if (wave == xw) dma(tile, qoff[NPW], buf, NCH - 1);
+      } else {  // ragged last tile: rows past Sq re-read row Sq - 1 (their normaliser is -inf)
 #pragma unroll
-        for (int c = 0; c < CHUNKS; ++c) {
-          const int id = tid + c * kThreads;
-          const int row = min(r0 + id / CPR, p.Sq - 1);
-          st[c] = load16(qgroup + gi * p.q_sh + (int64_t)row * p.q_ss + (id % CPR) * 8);
+        for (int j = 0; j <= NPW; ++j) {
+          if (j < NPW || wave == xw) {
+            const int ch = j < NPW ? wave + 4 * j : NCH - 1;
+            const int s = ch * 64 + lane;
+            const int row = min(s / SPR, p.Sq - 1 - r0);   // >= 0: r0 < Sq
+            dma(tile, (uint32_t)(row * (int)p.q_ss + min(s % SPR, SPR - 2) * 8) * 2u, buf, ch);
+          }
         }
       }
       if (wave == lw) {
@@ -218,10 +263,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         lrow_ok = row < p.Sq;
       }
     };
-    const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
     auto store_step = [&](int buf, int lw) {
-#pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) store16(&sq[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
       if (wave == lw) {
         // the slot's address is formed here from the lane index (an opaque
         // copy, so that it is not hoisted out of the loop into a spilled register)
@@ -229,6 +271,8 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         asm volatile("" : "+v"(t));
         sl[buf][t] = lrow_ok ? lst * nlc : -kInf;   // the accumulators' start (rows past Sq: -inf)
       }
+      // the tile's direct loads have landed in LDS before the barrier that follows
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
     };
 
     // this workgroup's share of the key block's steps: its range's tiles, or
@@ -244,7 +288,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     if (u_begin < u_end) {   // then nsr >= 1
       cq = u_begin / nsr;
       cr = u_begin - cq * nsr;
-      load_step(cq, cr, u_begin & 3);
+      load_step(cq, cr, u_begin & 3, u_begin & 1);
       store_step(u_begin & 1, u_begin & 3);
       __syncthreads();
     }
@@ -255,7 +299,7 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
         nr = 0;
         ++nq;
       }
-      if (more) load_step(nq, nr, (u + 1) & 3);
+      if (more) load_step(nq, nr, (u + 1) & 3, (u + 1) & 1);
       const int buf = u & 1;
       const int i0t = tile_at(cq, cr) * kQTile;
       const bool full = PER_HEAD ? cr < nfull_h : u < nfull_h * g;
