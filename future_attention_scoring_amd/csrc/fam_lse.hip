@@ -132,8 +132,6 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
   static_assert(BOUND || !SPLIT, "only the bounded form splits the key range");
   constexpr int PITCH = D + 8;                 // LDS row pitch in elements
   constexpr int KS = D / 16;                   // MFMA k-steps per 32x32 block
-  constexpr int CPR = D / 8;                   // 16-byte chunks per row
-  constexpr int CHUNKS = kKeyTile * CPR / kThreads;
   __shared__ __attribute__((aligned(16))) uint16_t sk[2][kKeyTile * PITCH];
 
   const int nbh = p.B * p.Hkv;
@@ -193,31 +191,51 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
       qf[blk][ks] = ok ? load16(qbase + (int64_t)row * p.q_ss + ks * 16 + half * 8) : zero16();
   }
 
-  // staging: a uniform tile pointer plus fixed per-thread 32-bit offsets; the
-  // ragged last tile clamps its rows (keys >= S are masked in the update)
-  const int off0 = (tid / CPR) * (int)p.k_ss + (tid % CPR) * 8;
-  const int pass_stride = (kThreads / CPR) * (int)p.k_ss;   // uniform: chunk c at off0 + c * pass_stride
-  u32x4_t st[CHUNKS];
-  auto load_tile = [&](int t) {
-    const int r0 = t * kKeyTile;
-    if (r0 + kKeyTile <= p.S) {
-      const uint16_t* tile = kbase + (int64_t)r0 * p.k_ss;
+  // K tiles go from global memory straight into LDS (gfx950's
+  // global_load_lds_dwordx4: lane l of a wave instruction fills the 16 bytes
+  // at the LDS base + 16 l), so they hold no registers while in flight. The
+  // padded tile is NCH chunks of 64 such slots; slot s is key s / SPR, 16-byte
+  // column s % SPR, and the pad column re-reads the row's last 16 bytes.
+  // Wave w loads chunks w, w + 4, ...; the last chunk goes to a wave that
+  // changes with the tile. Offsets are bytes inside a tile (the host
+  // guarantees kKeyTile * k_ss < 2^31 elements); the ragged last tile clamps
+  // its keys (keys >= S are masked in the update).
+  constexpr int SPR = PITCH / 8;
+  constexpr int NCH = kKeyTile * SPR / 64;
+  constexpr int NPW = NCH / 4;
+  static_assert(kKeyTile * SPR % 64 == 0 && NCH % 4 == 1, "chunks of the padded tile");
+  uint32_t koff[NPW + 1];
 #pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) st[c] = load16(tile + off0 + c * pass_stride);
+  for (int j = 0; j <= NPW; ++j) {
+    const int s = (j < NPW ? wave + 4 * j : NCH - 1) * 64 + lane;
+    koff[j] = (uint32_t)((s / SPR) * (int)p.k_ss + min(s % SPR, SPR - 2) * 8) * 2u;
+  }
+  const uint32_t sk_lds = (uint32_t)(uintptr_t)(lds_void*)&sk[0][0];
+  auto load_tile = [&](int t, int buf) {
+    const int r0 = t * kKeyTile;
+    const int xw = t & 3;   // the wave that loads the last chunk
+    const uint16_t* tile = kbase + (int64_t)r0 * p.k_ss;   // uniform
+    const uint32_t lb = sk_lds + (uint32_t)(buf * kKeyTile * PITCH * 2);
+    if (r0 + kKeyTile <= p.S) {
+#pragma unroll
+      for (int j = 0; j < NPW; ++j) dma16(tile, koff[j], lb + (uint32_t)((wave + 4 * j) * 1024));
+      if (wave == xw) dma16(tile, koff[NPW], lb + (uint32_t)((NCH - 1) * 1024));
     } else {
 #pragma unroll
-      for (int c = 0; c < CHUNKS; ++c) {
-        const int id = tid + c * kThreads;
-        const int key = min(r0 + id / CPR, p.S - 1);
-        st[c] = load16(kbase + (int64_t)key * p.k_ss + (id % CPR) * 8);
+      for (int j = 0; j <= NPW; ++j) {
+        if (j < NPW || wave == xw) {
+          const int ch = j < NPW ? wave + 4 * j : NCH - 1;
+          const int s = ch * 64 + lane;
+          const int key = min(s / SPR, p.S - 1 - r0);   // >= 0: r0 < S
+          dma16(tile, (uint32_t)(key * (int)p.k_ss + min(s % SPR, SPR - 2) * 8) * 2u,
+                lb + (uint32_t)(ch * 1024));
+        }
       }
     }
   };
-  const int lds0 = (tid / CPR) * PITCH + (tid % CPR) * 8;   // chunk c at lds0 + c * (kThreads / CPR) * PITCH
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < CHUNKS; ++c) store16(&sk[buf][lds0 + c * (kThreads / CPR) * PITCH], st[c]);
-  };
+  // the tile's direct loads have landed in LDS (before the barrier that
+  // publishes it)
+  auto wait_tile = [&]() { __builtin_amdgcn_s_waitcnt(kWaitVm0); };
 
   float* lse_row = p.lse + row0;
   bool done = false;
@@ -239,13 +257,13 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
     // this workgroup's share of the key tiles
     const int t0 = (int)((int64_t)ntiles * split / nks), t1 = (int)((int64_t)ntiles * (split + 1) / nks);
     if (t0 < t1) {
-      load_tile(t0);
-      store_tile(0);
+      load_tile(t0, 0);
+      wait_tile();
     }
     __syncthreads();
     for (int t = t0; t < t1; ++t) {
       const bool more = t + 1 < t1;
-      if (more) load_tile(t + 1);
+      if (more) load_tile(t + 1, (t + 1 - t0) & 1);
       const uint16_t* buf = sk[(t - t0) & 1];
 #pragma unroll
       for (int kk2 = 0; kk2 < kKeyTile / 32; ++kk2) {
@@ -284,7 +302,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
           bound_update(acc1, kb, qp0 + 32, p.S, lane, p.c, M[1], l[1]);
         }
       }
-      if (more) store_tile((t + 1 - t0) & 1);
+      if (more) wait_tile();
       __syncthreads();
     }
     if constexpr (SPLIT) {   // partial sums and the shift; the second launch finishes
@@ -321,12 +339,12 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
 
   // running maximum: the plain form, or the repeat of a loose bound
   float m[2] = {-kInf, -kInf}, l[2] = {0.f, 0.f};
-  load_tile(0);
-  store_tile(0);
+  load_tile(0, 0);
+  wait_tile();
   __syncthreads();
   for (int t = 0; t < ntiles; ++t) {
     const bool more = t + 1 < ntiles;
-    if (more) load_tile(t + 1);
+    if (more) load_tile(t + 1, (t + 1) & 1);
     const uint16_t* buf = sk[t & 1];
 #pragma unroll
     for (int kk = 0; kk < kKeyTile / 32; ++kk) {
@@ -344,7 +362,7 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
         online_update(acc1, kb, qp0 + 32, p.S, lane, p.c, m[1], l[1]);
       }
     }
-    if (more) store_tile((t + 1) & 1);
+    if (more) wait_tile();
     __syncthreads();
   }
 

@@ -55,31 +55,6 @@ constexpr int kKeysPerWG = kKeysPerWave * kWaves;
 static_assert(kKeysPerWG == kMassKeysPerWG, "host and kernel key-block size");
 constexpr int kQTile = 64;   // query rows per staged step (two 32-row MFMA blocks)
 constexpr int kReadAhead = 2;   // A-fragment reads issued this many k-steps ahead
-// s_waitcnt vmcnt(0) with the other counters left alone (gfx9 encoding:
-// vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-constexpr int kWaitVm0 = 0x0F70;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// 16 bytes per lane from global memory (uniform base + per-lane byte
-// offset) into LDS at lds + 16 * lane (gfx950 global_load_lds_dwordx4;
-// M0 holds the LDS address). Written as assembly so that the compiler's
-// wait analysis does not take it for a store that may alias every LDS read
-// (it would wait for it before each read of the other buffer); the caller
-// waits for it (vmcnt) before the barrier that publishes the tile.
-// M0 is named as clobbered (nothing else in these kernels keeps a value in
-// it; the compiler warns that it reserves M0, hence the local pragma).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* base, uint32_t off, uint32_t lds) {
-  asm volatile(
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %0, %1"
-      :
-      : "v"(off), "s"(base), "s"(lds)
-      : "memory", "m0");
-}
-#pragma clang diagnostic pop
 static_assert(kQTile == kMassQTile, "host and kernel query-tile size");
 
 // The accumulator of a block starts at -L_i / c for its query row i, so that
