@@ -54,7 +54,7 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerWave = 64;
 constexpr int kKeyTile = 64;
 constexpr float kMinBoundSum = 0x1p-80f;
-constexpr int kReadAhead = 4;   // bounded pass: A-fragment reads ahead of their MFMAs (KS >= 4)
+constexpr int kReadAhead = 2;   // bounded pass: A-fragment reads ahead of their MFMAs (KS >= 4)
 
 // Causal and ragged-tile mask of a 32x32 block (keys on rows, queries on columns).
 __device__ __forceinline__ void mask_block(f32x16_t& acc, int kb, int qblock, int S, int lane) {
