@@ -42,6 +42,8 @@
 //     caches would not hold them; within a range they share a few MB of Q.
 //     The per-query-head mode splits the same way, one partial slice per
 //     query head.
+#include <type_traits>
+
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -278,56 +280,66 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
       const int buf = u & 1;
       const int i0t = tile_at(cq, cr) * kQTile;
       const bool full = PER_HEAD ? cr < nfull_h : u < nfull_h * g;
+      // the step's two 32-row blocks, instantiated for full steps (no
+      // window tests at all) and for band steps; one uniform branch a step
+      auto blocks = [&](auto full_tag) {
+        constexpr bool FULL = decltype(full_tag)::value;
 #pragma unroll
-      for (int rb = 0; rb < kQTile / 32; ++rb) {
-        const int i0 = i0t + 32 * rb;
-        if (full || i0 + 31 >= jw + Wr) {
-          float lv[16];
+        for (int rb = 0; rb < kQTile / 32; ++rb) {
+          const int i0 = i0t + 32 * rb;
+          if (FULL || i0 + 31 >= jw + Wr) {
+            float lv[16];
 #pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sl[buf][32 * rb + 8 * r4 + 4 * half]);
-            lv[4 * r4 + 0] = x[0];
-            lv[4 * r4 + 1] = x[1];
-            lv[4 * r4 + 2] = x[2];
-            lv[4 * r4 + 3] = x[3];
-          }
-          f32x16_t acc0, acc1;
+            for (int r4 = 0; r4 < 4; ++r4) {
+              const f32x4_t x = *reinterpret_cast<const f32x4_t*>(&sl[buf][32 * rb + 8 * r4 + 4 * half]);
+              lv[4 * r4 + 0] = x[0];
+              lv[4 * r4 + 1] = x[1];
+              lv[4 * r4 + 2] = x[2];
+              lv[4 * r4 + 3] = x[3];
+            }
+            f32x16_t acc0, acc1;
 #pragma unroll
-          for (int v = 0; v < 16; ++v) acc0[v] = lv[v];
-          acc1 = acc0;
-          // the A fragments are read kReadAhead k-steps ahead of their MFMAs:
-          // the normaliser reads and the first kReadAhead fragment reads,
-          // then per k-step two MFMAs and the read kReadAhead steps ahead,
-          // then the last MFMAs (left to itself the compiler reads one step
-          // ahead)
-          u32x4_t af[KS];
+            for (int v = 0; v < 16; ++v) acc0[v] = lv[v];
+            acc1 = acc0;
+            // the A fragments are read kReadAhead k-steps ahead of their MFMAs:
+            // the normaliser reads and the first kReadAhead fragment reads,
+            // then per k-step two MFMAs and the read kReadAhead steps ahead,
+            // then the last MFMAs (left to itself the compiler reads one step
+            // ahead)
+            u32x4_t af[KS];
 #pragma unroll
-          for (int ks = 0; ks < kReadAhead; ++ks)
-            af[ks] = *reinterpret_cast<const u32x4_t*>(&sq[buf][(32 * rb + col) * PITCH + ks * 16 + half * 8]);
+            for (int ks = 0; ks < kReadAhead; ++ks)
+              af[ks] = *reinterpret_cast<const u32x4_t*>(&sq[buf][(32 * rb + col) * PITCH + ks * 16 + half * 8]);
 #pragma unroll
-          for (int ks = 0; ks < KS; ++ks) {
-            if (ks + kReadAhead < KS)
-              af[ks + kReadAhead] = *reinterpret_cast<const u32x4_t*>(
-                  &sq[buf][(32 * rb + col) * PITCH + (ks + kReadAhead) * 16 + half * 8]);
-            acc0 = Mma<T>::run(af[ks], kf[0][ks], acc0);
-            acc1 = Mma<T>::run(af[ks], kf[1][ks], acc1);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x100, 4 + kReadAhead, 0);   // DS reads
+            for (int ks = 0; ks < KS; ++ks) {
+              if (ks + kReadAhead < KS)
+                af[ks + kReadAhead] = *reinterpret_cast<const u32x4_t*>(
+                    &sq[buf][(32 * rb + col) * PITCH + (ks + kReadAhead) * 16 + half * 8]);
+              acc0 = Mma<T>::run(af[ks], kf[0][ks], acc0);
+              acc1 = Mma<T>::run(af[ks], kf[1][ks], acc1);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 + kReadAhead, 0);   // DS reads
 #pragma unroll
-          for (int ks = 0; ks < KS - kReadAhead; ++ks) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, 2 * kReadAhead, 0);
-          if (full) {
-            mid[0] += block_sum_full(acc0, p.c);
-            mid[1] += block_sum_full(acc1, p.c);
-          } else {
-            mid[0] += block_sum_band(acc0, i0, jw, Wr, lane, p.c);
-            mid[1] += block_sum_band(acc1, i0, jw + 32, Wr, lane, p.c);
+            for (int ks = 0; ks < KS - kReadAhead; ++ks) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);   // MFMAs
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * kReadAhead, 0);
+            if constexpr (FULL) {
+              mid[0] += block_sum_full(acc0, p.c);
+              mid[1] += block_sum_full(acc1, p.c);
+              // keep the next block's reads and MFMAs from being scheduled
+              // into this block's exps (that raises the register peak)
+              __builtin_amdgcn_sched_barrier(0);
+            } else {
+              mid[0] += block_sum_band(acc0, i0, jw, Wr, lane, p.c);
+              mid[1] += block_sum_band(acc1, i0, jw + 32, Wr, lane, p.c);
+            }
           }
         }
-      }
+      };
+      if (full) blocks(std::true_type{});
+      else blocks(std::false_type{});
       if ((u & 7) == 7) {
         top[0] += mid[0];
         top[1] += mid[1];
