@@ -366,12 +366,23 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
 }
 
 // mass = sum over the splits of the partial column sums, in split order.
+// The slices' loads go out kBatch at a time and are added in split order,
+// so a thread waits for a few round trips instead of one per slice.
 __global__ __launch_bounds__(kThreads) void mass_reduce_kernel(const float* part, float* mass,
                                                                int64_t n, int nsplit) {
+  constexpr int kBatch = 8;
   const int64_t stride = (int64_t)gridDim.x * kThreads;
   for (int64_t e = (int64_t)blockIdx.x * kThreads + threadIdx.x; e < n; e += stride) {
-    float acc = part[e];
-    for (int k = 1; k < nsplit; ++k) acc += part[(int64_t)k * n + e];
+    float acc = 0.f;
+    for (int k0 = 0; k0 < nsplit; k0 += kBatch) {
+      float v[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        v[j] = part[(int64_t)min(k0 + j, nsplit - 1) * n + e];   // in bounds, used only if k0 + j < nsplit
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (k0 + j < nsplit) acc = k0 + j == 0 ? v[j] : acc + v[j];
+    }
     mass[e] = acc;
   }
 }
