@@ -197,9 +197,9 @@ __global__ __launch_bounds__(kThreads, 3) void lse_kernel(LseArgs p, int npb) {
   // padded tile is NCH chunks of 64 such slots; slot s is key s / SPR, 16-byte
   // column s % SPR, and the pad column re-reads the row's last 16 bytes.
   // Wave w loads chunks w, w + 4, ...; the last chunk goes to a wave that
-  // changes with the tile. Offsets are bytes inside a tile (the host
-  // guarantees kKeyTile * k_ss < 2^31 elements); the ragged last tile clamps
-  // its keys (keys >= S are masked in the update).
+  // changes with the tile. Offsets are bytes inside a tile (the host refuses
+  // row strides above 2^24 elements, so 64 rows span less than 2^31 bytes);
+  // the ragged last tile clamps its keys (keys >= S are masked in the update).
   constexpr int SPR = PITCH / 8;
   constexpr int NCH = kKeyTile * SPR / 64;
   constexpr int NPW = NCH / 4;

@@ -190,8 +190,9 @@ __global__ __launch_bounds__(kThreads, 3) void mass_kernel(MassArgs p) {
     // flight. The padded tile is NCH chunks of 64 such slots; slot s is row
     // s / SPR, 16-byte column s % SPR, and the pad column re-reads the row's
     // last 16 bytes. Wave w loads chunks w, w + 4, ...; the last chunk goes to
-    // a wave that changes with the step. Offsets are elements inside a tile
-    // (the host guarantees kQTile * q_ss < 2^31).
+    // a wave that changes with the step. Offsets are bytes inside a tile: the
+    // host refuses row strides above 2^24 elements, so 64 rows span less than
+    // 2^31 bytes.
     constexpr int SPR = PITCH / 8;
     constexpr int NCH = kQTile * SPR / 64;
     constexpr int NPW = NCH / 4;
