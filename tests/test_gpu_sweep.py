@@ -17,6 +17,13 @@ Each case runs fam_compute and the per-query-head mass (each query head's
 mass against the oracle's, and their group sums against the group mass to
 fp32 rounding), then the chunk mode on the same inputs: the last Sq rows as
 the chunk's queries over all S keys, against the oracle's chunk functions.
+
+A second sweep draws eviction cases (head counts, lengths around the
+4096-candidate chunks, sinks, windows, budgets from 0 past S, and scores that
+are normal, heavy-tailed like masses, from a few distinct values, or mixed
+with NaN, +-inf and +-0) and compares select bit for bit with the oracle's
+sort-based selection, and compact (on cases up to 300000 rows) bit for bit
+with its fancy-index gather.
 """
 import numpy as np
 import pytest
@@ -25,6 +32,7 @@ import torch
 from future_attention_scoring_amd import fam
 from oracle import chunked as ch
 from oracle import fam_oracle as fo
+from oracle import select_oracle as so
 
 pytestmark = pytest.mark.gpu
 
@@ -117,3 +125,54 @@ def test_random_shape_against_oracle(c):
         check_mass(to64(mass_c[b]), mass_cref)
     grp = mass_q.view(B, Hkv, Hq // Hkv, S).double().sum(2)
     np.testing.assert_allclose(grp.cpu().numpy(), to64(mass), rtol=1e-5, atol=0)
+
+
+def draw_select_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        S = int(rng.choice([int(rng.integers(1, 600)), int(rng.integers(3000, 9000)),
+                            int(rng.integers(9000, 40000))]))
+        cases.append(dict(seed=2000 + i, H=int(rng.integers(1, 70)), S=S,
+                          sinks=int(rng.choice([0, 1, 4, int(rng.integers(0, 50))])),
+                          recent=int(rng.choice([0, 16, 512, int(rng.integers(0, 300))])),
+                          kind=str(rng.choice(["normal", "heavy", "few", "special"]))))
+    return cases
+
+
+SELECT_CASES = draw_select_cases(40, 20261203)
+
+
+def select_scores(rng, kind, H, S):
+    if kind == "normal":
+        return rng.standard_normal((H, S)).astype(np.float32)
+    if kind == "heavy":                       # positive, spanning many octaves, like masses
+        return np.exp(rng.standard_normal((H, S)) * 4.0).astype(np.float32)
+    if kind == "few":                         # many equal keys: ties go to the lower position
+        return rng.choice(np.array([0.5, 1.0, 2.0], np.float32), size=(H, S))
+    pool = np.array([0.0, -0.0, 1.0, -1.0, np.inf, -np.inf, np.nan, 2.5, 1e-38], np.float32)
+    s = rng.choice(pool, size=(H, S)).astype(np.float32)
+    mix = rng.random((H, S)) < 0.5
+    s[mix] = rng.standard_normal(mix.sum()).astype(np.float32)
+    return s
+
+
+@pytest.mark.parametrize("c", SELECT_CASES, ids=lambda c: f"s{c['seed']}")
+def test_random_select_and_compact_against_oracle(c):
+    H, S, sinks, recent = c["H"], c["S"], c["sinks"], c["recent"]
+    say(f"select sweep seed={c['seed']} H={H} S={S} sinks={sinks} recent={recent} {c['kind']}")
+    rng = np.random.default_rng(c["seed"])
+    scores = select_scores(rng, c["kind"], H, S)
+    budgets = [int(x) for x in rng.integers(0, S + 8, H)]
+    idx, off = fam.evict_select(torch.from_numpy(scores).to(DEV), budgets, sinks, recent)
+    torch.cuda.synchronize()
+    idx_ref, off_ref = so.select(scores, budgets, sinks, recent)
+    assert off.cpu().numpy().tolist() == off_ref.tolist()
+    assert np.array_equal(idx.cpu().numpy(), idx_ref), "index lists differ"
+    if H * S <= 300000:   # the gather too (K/V of d = 64 as raw 16-bit patterns)
+        kv = torch.from_numpy(rng.integers(-30000, 30000, size=(2, H, S, 64), dtype=np.int16))
+        k_new, v_new = fam.kv_compact(kv[0].view(torch.bfloat16).to(DEV), kv[1].view(torch.bfloat16).to(DEV),
+                                      idx, off)
+        torch.cuda.synchronize()
+        assert np.array_equal(k_new.cpu().view(torch.int16).numpy(), so.compact(kv[0].numpy(), idx_ref, off_ref))
+        assert np.array_equal(v_new.cpu().view(torch.int16).numpy(), so.compact(kv[1].numpy(), idx_ref, off_ref))
