@@ -24,6 +24,12 @@ are normal, heavy-tailed like masses, from a few distinct values, or mixed
 with NaN, +-inf and +-0) and compares select bit for bit with the oracle's
 sort-based selection, and compact (on cases up to 300000 rows) bit for bit
 with its fancy-index gather.
+
+A third draws ranking-quality cases (rows with ties and special values, head
+counts and lengths around the 4096-entry tiles, budgets (s, w, k) of the
+running cut-off from 0 past S): the rank order and the running cut-offs
+exactly, the eviction cost to 1e-12 relative, against oracle/ranking.py and
+oracle/topk_cutoff.py.
 """
 import numpy as np
 import pytest
@@ -32,7 +38,9 @@ import torch
 from future_attention_scoring_amd import fam
 from oracle import chunked as ch
 from oracle import fam_oracle as fo
+from oracle import ranking as rk
 from oracle import select_oracle as so
+from oracle import topk_cutoff as tc
 
 pytestmark = pytest.mark.gpu
 
@@ -176,3 +184,44 @@ def test_random_select_and_compact_against_oracle(c):
         torch.cuda.synchronize()
         assert np.array_equal(k_new.cpu().view(torch.int16).numpy(), so.compact(kv[0].numpy(), idx_ref, off_ref))
         assert np.array_equal(v_new.cpu().view(torch.int16).numpy(), so.compact(kv[1].numpy(), idx_ref, off_ref))
+
+
+def draw_ranking_cases(n, seed):
+    rng = np.random.default_rng(seed)
+    cases = []
+    for i in range(n):
+        S = int(rng.choice([int(rng.integers(1, 300)), int(rng.integers(1000, 9000)),
+                            int(rng.integers(9000, 20000))]))
+        cases.append(dict(seed=3000 + i, H=int(rng.integers(1, 12)), S=S,
+                          s=int(rng.choice([0, 1, 4, int(rng.integers(0, S + 4))])),
+                          w=int(rng.choice([0, 3, 512, int(rng.integers(0, S + 4))])),
+                          k=int(rng.choice([0, 1, int(rng.integers(0, S + 4))]))))
+    return cases
+
+
+RANKING_CASES = draw_ranking_cases(32, 20261204)
+
+
+@pytest.mark.parametrize("c", RANKING_CASES, ids=lambda c: f"s{c['seed']}")
+def test_random_ranking_and_cutoffs_against_oracle(c):
+    H, S, s, w, k = c["H"], c["S"], c["s"], c["w"], c["k"]
+    say(f"ranking sweep seed={c['seed']} H={H} S={S} s={s} w={w} k={k}")
+    rng = np.random.default_rng(c["seed"])
+    scores = rng.standard_normal((H, S)).astype(np.float32)
+    scores[rng.random((H, S)) < 0.1] = 0.5                  # ties
+    scores[rng.random((H, S)) < 0.02] = np.nan
+    scores[rng.random((H, S)) < 0.02] = -0.0
+    imp = (rng.random((H, S)) ** 3).astype(np.float32)
+    sd, impd = torch.from_numpy(scores).to(DEV), torch.from_numpy(imp).to(DEV)
+    order = fam.fam_rank_order(sd)
+    cost = fam.fam_eviction_cost(impd, order)
+    cut = fam.fam_topk_cutoff(order, s, w, k)
+    torch.cuda.synchronize()
+    order_ref = rk.rank_order(scores)
+    np.testing.assert_array_equal(order.cpu().numpy(), order_ref)
+    np.testing.assert_allclose(cost.cpu().numpy(), rk.eviction_cost(imp.astype(np.float64), order_ref),
+                               rtol=1e-12, atol=0)
+    got = cut.cpu().numpy()
+    for h in range(H):
+        ranks = tc.ranks_from_scores(scores[h].astype(np.float64))
+        np.testing.assert_array_equal(got[h], tc.cutoffs(ranks, s, w, k))
