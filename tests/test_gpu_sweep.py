@@ -15,8 +15,11 @@ the boundaries of the kernels fall at many offsets at once:
 
 Each case runs fam_compute and the per-query-head mass (each query head's
 mass against the oracle's, and their group sums against the group mass to
-fp32 rounding), then the chunk mode on the same inputs: the last Sq rows as
-the chunk's queries over all S keys, against the oracle's chunk functions.
+fp32 rounding), the KVpop target epilogue on that mass (eps 0 or 1e-6, max
+or mean over the group, against oracle.kvpop_target: 2.5e-3 absolute on the
+log, -inf where the oracle has it), then the chunk mode on the same inputs:
+the last Sq rows as the chunk's queries over all S keys, against the
+oracle's chunk functions.
 
 A second sweep draws eviction cases (head counts, lengths around the
 4096-candidate chunks, sinks, windows, budgets from 0 past S, and scores that
@@ -38,6 +41,7 @@ import torch
 from future_attention_scoring_amd import fam
 from oracle import chunked as ch
 from oracle import fam_oracle as fo
+from oracle import kvpop_target as kt
 from oracle import ranking as rk
 from oracle import select_oracle as so
 from oracle import topk_cutoff as tc
@@ -47,6 +51,7 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 LSE_TOL = 1e-3
 MASS_RTOL = 2e-3
+TARGET_ATOL = 2.5e-3
 
 
 def say(msg):
@@ -69,6 +74,15 @@ def check_mass(got, ref):
     if pos.any():
         rel = np.abs(got[pos] - ref[pos]) / np.maximum(ref[pos], np.finfo(np.float32).tiny)
         assert rel.max() <= MASS_RTOL, f"mass max rel err {rel.max()}"
+
+
+def check_target(got, ref):
+    got = np.asarray(got, np.float64)
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), "-inf positions differ"
+    fin = np.isfinite(ref)
+    if fin.any():
+        err = np.abs(got[fin] - ref[fin]).max()
+        assert err <= TARGET_ATOL, f"target max abs err {err}"
 
 
 def draw_cases(n, seed):
@@ -117,6 +131,9 @@ def test_random_shape_against_oracle(c):
     q, k = inputs(c)
     lse, mass = fam.fam_compute(q, k, W)
     mass_q = fam.fam_mass_per_head(q, k, lse, W)
+    eps = (0.0, 1e-6)[c["seed"] % 2]
+    agg = ("max", "mean")[(c["seed"] // 2) % 2]
+    tgt = fam.fam_kvpop_target(mass_q, Hkv, W, eps=eps, aggregate=agg)
     lse_c, mass_c = fam.fam_compute_chunk(q[:, :, S - Sq:], k, W)
     torch.cuda.synchronize()
     qn, kn = to64(q), to64(k)
@@ -127,6 +144,9 @@ def test_random_shape_against_oracle(c):
         check_lse(to64(lse[b]), lse_ref)
         check_mass(to64(mass[b]), mass_ref)
         check_mass(to64(mass_q[b]), per_q_ref)
+        g = Hq // Hkv
+        for h in range(Hkv):
+            check_target(to64(tgt[b, h]), kt.target(per_q_ref[h * g:(h + 1) * g], W, eps=eps, aggregate=agg))
         lse_cref = ch.chunk_lse(qn[b, :, S - Sq:], kn[b], pos, S - Sq)
         mass_cref = ch.chunk_mass(qn[b, :, S - Sq:], kn[b], pos, lse_cref, S - Sq, W)
         check_lse(to64(lse_c[b]), lse_cref)
