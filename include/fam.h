@@ -8,8 +8,11 @@
  * Conventions shared by every entry point
  *   - Strides are in elements. The last (head-dim) axis is contiguous.
  *   - The library never allocates or frees device memory and keeps no state
- *     between calls, apart from loaded code objects and a thread-local error
- *     string. The caller owns every buffer.
+ *     between calls, apart from loaded code objects, a thread-local error
+ *     string and two per-device values read once (the address of
+ *     evict_select_noalloc's static scratch array, which the code object
+ *     holds on every GPU it is loaded on, and the long select path's count
+ *     of resident workgroups). The caller owns every other buffer.
  *   - Device entry points only enqueue work on `stream` and return; they do
  *     not synchronise (except under the FAM_SYNC_CHECK debug switch below,
  *     and kv_compact_inplace_status, which exists to wait). Outputs are valid
