@@ -44,7 +44,8 @@ constexpr int kBins = 1024;                          // per histogram level (10 
 constexpr int kBinsPerThread = kBins / kThreads;     // 4 bins = one 8-byte u16 group
 constexpr int kRadixBins = 2048;                     // exact pick: 11 bits per pass
 constexpr int kMaxChunks = (kSelectMaxCandidates + 3) / kSelectChunk + 1;
-constexpr int kLdsList = 4096;  // (b1, b2) entries held in LDS
+constexpr int kLdsList = 1024;  // (b1, b2) entries held in LDS (more are read from the lists in L2);
+                                 // 8 KB keeps the scatter launch at four workgroups per CU
 constexpr int kRankMax = 128;   // up to this many, rank them by direct comparison
 
 
