@@ -607,6 +607,49 @@ def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
             "ms_step": wall * 1e3 / steps, "t_fam": t_fam, "t_ec": t_ec, "flushed": flushed}
 
 
+def mass_select_row(reps, q, k, wl, run, stream):
+    """fam_mass_select against fam_mass followed by evict_select on the same
+    workload (HIP events on the launch stream, the two forms alternating in
+    every rep). Both forms spend about 57 ms in the mass pass at 128k, whose
+    run-to-run spread is far larger than the launches the combined form
+    saves, so only the totals are reported; the saving itself is read from a
+    kernel trace (end of the mass pass to the end of the last select launch)."""
+    dev = q.device
+    B, Hq, Hkv, S = 1, wl.Hq, wl.Hkv, wl.S
+    lse, budgets, total = run["lse"], run["budgets"], run["total"]
+    mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
+    idx = torch.empty(total, dtype=torch.int32, device=dev)
+    offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=dev)
+    mws = torch.empty(max(16, fam.fam_mass_workspace_size(B, Hq, Hkv, S)), dtype=torch.uint8, device=dev)
+    sws = torch.empty(max(16, fam.evict_select_workspace_size(Hkv, S, wl.sinks, wl.recent)),
+                      dtype=torch.uint8, device=dev)
+
+    def fused():
+        fam.fam_mass_select(q, k, lse, wl.W, budgets, wl.sinks, wl.recent, mass=mass, idx=idx,
+                            offsets=offsets, mass_workspace=mws, select_workspace=sws)
+
+    def apart():
+        fam.fam_mass(q, k, lse, wl.W, mass=mass, workspace=mws)
+        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets, workspace=sws)
+
+    fused()
+    apart()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    for e in ev:
+        e[0].record(stream)
+        fused()
+        e[1].record(stream)
+        apart()
+        e[2].record(stream)
+    torch.cuda.synchronize()
+    f = [e[0].elapsed_time(e[1]) for e in ev]
+    a = [e[1].elapsed_time(e[2]) for e in ev]
+    return {"reps": reps, "ms_median": {"fam_mass_select": round(float(np.median(f)), 4),
+                                        "fam_mass + evict_select": round(float(np.median(a)), 4)},
+            "ms_spread": {"fam_mass_select": round(max(f) - min(f), 4),
+                          "fam_mass + evict_select": round(max(a) - min(a), 4)}}
+
+
 def workload_row(wl, steps, warmup, stream):
     """One more workload's step, timed on its own inputs (for the lines of
     the other score workloads beside the headline one)."""
@@ -651,6 +694,8 @@ def main():
                     help="timed steps of the 8k and 32k score workloads beside the 128k line; 0 skips them")
     ap.add_argument("--flushed-reps", type=int, default=5,
                     help="select + compact reps after a cache-evicting fill (headline workload); 0 skips them")
+    ap.add_argument("--mass-select-reps", type=int, default=5,
+                    help="reps of fam_mass_select against fam_mass + evict_select (headline workload); 0 skips them")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (to scale HBM byte counters)")
     args = ap.parse_args()
@@ -721,6 +766,8 @@ def main():
         "evict_compact_flushed": run["flushed"],
         "clock_state_during_steps": clocks[0] if clocks else None,
     }
+    if args.mass_select_reps > 0:
+        out["mass_select"] = mass_select_row(args.mass_select_reps, q, k, wl, run, stream)
     if args.target_steps > 0:
         out["kvpop_target"] = kvpop_target_row(args.target_steps, q, k, lse, wl, work, stream)
         for n in ("fam_mass_per_head", "fam_kvpop_target"):

@@ -32,6 +32,9 @@
 //               also writes the sinks, the window and the offsets.
 // A bin that is taken whole needs no further level.
 // Output per head: sinks, then the chosen candidates, then the window.
+// When the scores are masses whose split parts the mass pass has just
+// written, launch 1 is sel_hist_reduce instead: it adds the parts (the mass
+// pass's own reduction) and builds the histograms from the sums in registers.
 #include "fam_device.hpp"
 #include "fam_kernels.hpp"
 
@@ -137,7 +140,9 @@ __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row
     k[i] = (first + i >= p.c0 && first + i < p.c1) ? order_key(f[i]) : 0u;
 }
 
-// Inclusive prefix sum over the 256 threads; `total` receives the sum.
+// Inclusive prefix sum over the NT threads of the workgroup; `total`
+// receives the sum. `sh` holds NT / 64 ints.
+template <int NT = kThreads>
 __device__ int block_scan(int v, int* sh, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -149,7 +154,7 @@ __device__ int block_scan(int v, int* sh, int& total) {
   __syncthreads();
   int before = 0, tot = 0;
 #pragma unroll
-  for (int w = 0; w < kThreads / 64; ++w) {
+  for (int w = 0; w < NT / 64; ++w) {
     const int s = sh[w];
     before += w < wave ? s : 0;
     tot += s;
@@ -177,22 +182,24 @@ __device__ __forceinline__ void wave0_exclusive_scan(int n, F val, int* out) {
   }
 }
 
-// This thread's 4 bins of an LDS histogram as descending inclusive
-// cumulative counts: cum[j] = # elements in bins >= 4*tid + j.
+// This thread's kBins / NT bins of an LDS histogram as descending inclusive
+// cumulative counts: cum[j] = # elements in bins >= (kBins / NT) * tid + j.
+template <int NT = kThreads>
 __device__ __forceinline__ void descending_cum(const uint32_t* hist, int* sh,
-                                               uint32_t (&cum)[kBinsPerThread]) {
-  uint32_t h[kBinsPerThread];
+                                               uint32_t (&cum)[kBins / NT]) {
+  constexpr int kB = kBins / NT;
+  uint32_t h[kB];
   int local = 0;
 #pragma unroll
-  for (int j = 0; j < kBinsPerThread; ++j) {
-    h[j] = hist[kBinsPerThread * threadIdx.x + j];
+  for (int j = 0; j < kB; ++j) {
+    h[j] = hist[kB * threadIdx.x + j];
     local += (int)h[j];
   }
   int total;
-  const int incl = block_scan(local, sh, total);
+  const int incl = block_scan<NT>(local, sh, total);
   uint32_t run = (uint32_t)(total - incl);
 #pragma unroll
-  for (int j = kBinsPerThread - 1; j >= 0; --j) {
+  for (int j = kB - 1; j >= 0; --j) {
     run += h[j];
     cum[j] = run;
   }
@@ -575,6 +582,123 @@ __device__ __forceinline__ void scatter_phase(const SelectArgs& p) {
   }
 }
 
+// ---------------------------------------------------------------- launch 1, fed by the mass pass
+// When the scores are the key masses whose partial sums the mass pass left
+// in `part` ([nsplit][H * S], the slices of a [H, S] output), this launch
+// replaces the mass pass's reduction and the first select launch: each chunk
+// adds its positions' slices in split order (the order, and so the bits, of
+// the plain reduction), writes the masses, and builds its level-1 histogram
+// from the sums still in registers. Workgroups past the select grid reduce
+// the positions no chunk covers (before the first chunk, after the last).
+constexpr int kReduceBatch = 8;     // slices in flight per thread
+constexpr int kReduceThreads = 256; // threads per chunk (16 consecutive positions each)
+
+__device__ __forceinline__ float reduce_one(const float* part, int64_t n, int nsplit, int64_t e) {
+  float acc = 0.f;
+  for (int k0 = 0; k0 < nsplit; k0 += kReduceBatch) {
+    float v[kReduceBatch];
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j) v[j] = part[(int64_t)min(k0 + j, nsplit - 1) * n + e];
+#pragma unroll
+    for (int j = 0; j < kReduceBatch; ++j)
+      if (k0 + j < nsplit) acc = k0 + j == 0 ? v[j] : acc + v[j];
+  }
+  return acc;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void sel_hist_reduce(SelectArgs p, const float* part, float* mass,
+                                                      int nsplit, int ngrid) {
+  constexpr int PT = kSelectChunk / NT;   // consecutive positions per thread
+  constexpr int BPT = kBins / NT;         // histogram bins per thread
+  __shared__ uint32_t hist[kBins];
+  __shared__ int sh[NT / 64];
+  const int S = p.S;
+  const int64_t n = (int64_t)p.H * S;
+  const int a0 = p.c0 & ~3;
+  if ((int)blockIdx.x >= ngrid) {
+    const int64_t after = (int64_t)a0 + (int64_t)p.nchunk * kSelectChunk;
+    const int64_t per_head = a0 + (S > after ? S - after : 0);
+    const int64_t nout = (int64_t)p.H * per_head;
+    const int64_t stride = (int64_t)(gridDim.x - ngrid) * NT;
+    for (int64_t e = (int64_t)(blockIdx.x - ngrid) * NT + threadIdx.x; e < nout; e += stride) {
+      const int64_t h = e / per_head, j = e - h * per_head;
+      const int64_t at = h * S + (j < a0 ? j : after + (j - a0));
+      mass[at] = reduce_one(part, n, nsplit, at);
+    }
+    return;
+  }
+  int w, hl;
+  if (!wg_coords(p, w, hl)) return;
+  const int first = a0 + w * kSelectChunk + PT * (int)threadIdx.x;
+  const int64_t row = (int64_t)hl * S;
+  float acc[PT];
+  const bool vec_ok = ((reinterpret_cast<uintptr_t>(part) | reinterpret_cast<uintptr_t>(mass)) & 15u) == 0 &&
+                      (S & 3) == 0;
+  if (vec_ok && first + PT <= S) {
+    for (int k0 = 0; k0 < nsplit; k0 += kReduceBatch) {
+      f32x4_t v[kReduceBatch][PT / 4];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) {
+        const float* src = part + (int64_t)min(k0 + j, nsplit - 1) * n + row + first;
+#pragma unroll
+        for (int q = 0; q < PT / 4; ++q) v[j][q] = *reinterpret_cast<const f32x4_t*>(src + 4 * q);
+      }
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j)
+        if (k0 + j < nsplit) {
+#pragma unroll
+          for (int q = 0; q < PT / 4; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              acc[4 * q + c] = k0 + j == 0 ? v[j][q][c] : acc[4 * q + c] + v[j][q][c];
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < PT / 4; ++q)
+      *reinterpret_cast<f32x4_t*>(mass + row + first + 4 * q) =
+          f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+  } else {
+    // the row's end or unaligned rows: positions clamped into the row, stores masked
+#pragma unroll
+    for (int i = 0; i < PT; ++i) acc[i] = 0.f;
+    for (int k0 = 0; k0 < nsplit; k0 += kReduceBatch) {
+      float v[kReduceBatch][PT];
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j) {
+        const float* src = part + (int64_t)min(k0 + j, nsplit - 1) * n + row;
+#pragma unroll
+        for (int i = 0; i < PT; ++i) v[j][i] = src[min(first + i, S - 1)];
+      }
+#pragma unroll
+      for (int j = 0; j < kReduceBatch; ++j)
+        if (k0 + j < nsplit) {
+#pragma unroll
+          for (int i = 0; i < PT; ++i) acc[i] = k0 + j == 0 ? v[j][i] : acc[i] + v[j][i];
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < PT; ++i)
+      if (first + i < S) mass[row + first + i] = acc[i];
+  }
+  if (trivial_head(p, p.n_choose[hl])) return;
+  for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < PT; ++i)
+    if (first + i >= p.c0 && first + i < p.c1) atomicAdd(&hist[key_top(order_key(acc[i]))], 1u);
+  __syncthreads();
+  uint32_t cum[BPT];
+  descending_cum<NT>(hist, sh, cum);
+  // this thread's BPT counts (each <= kSelectChunk) as packed u16
+  uint16_t* dst = ws_of(p).cum1 + ((size_t)hl * p.nchunk + w) * kBins + BPT * threadIdx.x;
+  uint32_t r[BPT / 2];
+#pragma unroll
+  for (int q = 0; q < BPT / 2; ++q) r[q] = (cum[2 * q] & 0xffffu) | (cum[2 * q + 1] << 16);
+  if constexpr (BPT == 4) *reinterpret_cast<u32x2_t*>(dst) = u32x2_t{r[0], r[1]};
+  else *reinterpret_cast<uint32_t*>(dst) = r[0];
+}
+
 __global__ __launch_bounds__(kThreads) void sel_hist(SelectArgs p) { hist_phase(p); }
 __global__ __launch_bounds__(kThreads) void sel_collect(SelectArgs p) { collect_phase(p); }
 __global__ __launch_bounds__(kThreads) void sel_scatter(SelectArgs p) { scatter_phase(p); }
@@ -611,6 +735,22 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(sel_collect, grid, dim3(kThreads), 0, s, a);
     hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_select_from_parts(const SelectArgs& a, const float* part, int nsplit,
+                                    hipStream_t s) {
+  const int groups = (a.nheads + kXcds - 1) / kXcds;
+  const int ngrid = kXcds * a.nchunk * groups;
+  const int a0 = a.c0 & ~3;
+  const int64_t after = (int64_t)a0 + (int64_t)a.nchunk * kSelectChunk;
+  const int64_t nout = (int64_t)a.H * (a0 + (a.S > after ? a.S - after : 0));
+  const int64_t blocks = (nout + kReduceThreads - 1) / kReduceThreads;
+  const int64_t extra = blocks < 1024 ? blocks : 1024;
+  hipLaunchKernelGGL(sel_hist_reduce<kReduceThreads>, dim3((unsigned)(ngrid + extra)), dim3(kReduceThreads), 0, s,
+                     a, part, const_cast<float*>(a.scores), nsplit, ngrid);
+  hipLaunchKernelGGL(sel_collect, dim3(ngrid), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(sel_scatter, dim3(ngrid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -228,10 +228,11 @@ size_t per_head_split_bytes(const ScoreShape& s, int nsplit) {
 }
 
 // Group-sum mass pass on a validated shape: as many splits as wanted and as
-// the workspace holds (none without one).
-fam_status mass_group(const void* q, const void* k, const float* lse, int dtype,
-                      const ScoreShape& s, int W, float scale, float* mass, void* workspace,
-                      size_t workspace_bytes, hipStream_t stream, const char* what) {
+// the workspace holds (none without one). mass_prepare checks the arguments
+// and fills the launch's arguments; mass_group also launches.
+fam_status mass_prepare(const void* q, const void* k, const float* lse, const ScoreShape& s, int W,
+                        float scale, float* mass, void* workspace, size_t workspace_bytes,
+                        fam::MassArgs& a) {
   if (!lse || !mass) return fail(FAM_ERR_INVALID_ARG, "lse and mass must be non-null");
   if (W < 0) return fail(FAM_ERR_INVALID_ARG, "window W must be >= 0 (got %d)", W);
   if (const fam_status sc = check_mass_scale(scale, s.d); sc != FAM_OK) return sc;
@@ -240,18 +241,27 @@ fam_status mass_group(const void* q, const void* k, const float* lse, int dtype,
   const size_t per_split = (size_t)s.B * s.Hkv * s.S * sizeof(float);
   const MassPlan plan = mass_plan(s);
   if (workspace && plan.range_tiles > 0 && mass_split_bytes(s, plan.nsplit) <= workspace_bytes) {
-    fam::MassArgs a = mass_args(q, k, lse, s, W, scale, mass, nullptr, static_cast<float*>(workspace),
-                                plan.nsplit);
+    a = mass_args(q, k, lse, s, W, scale, mass, nullptr, static_cast<float*>(workspace), plan.nsplit);
     a.range_tiles = plan.range_tiles;
-    return launched(fam::launch_mass(a, elem_of(dtype), stream), stream, what);
+    return ok();
   }
   // even shares, as many as wanted and as the workspace holds
   int nsplit = mass_splits(s.B, s.Hkv, s.S);
   if (!workspace) nsplit = 1;
   if ((size_t)nsplit * per_split > workspace_bytes) nsplit = (int)(workspace_bytes / per_split);
   if (nsplit < 2) nsplit = 1;
-  const fam::MassArgs a = mass_args(q, k, lse, s, W, scale, mass, nullptr,
-                                    nsplit > 1 ? static_cast<float*>(workspace) : nullptr, nsplit);
+  a = mass_args(q, k, lse, s, W, scale, mass, nullptr,
+                nsplit > 1 ? static_cast<float*>(workspace) : nullptr, nsplit);
+  return ok();
+}
+
+fam_status mass_group(const void* q, const void* k, const float* lse, int dtype,
+                      const ScoreShape& s, int W, float scale, float* mass, void* workspace,
+                      size_t workspace_bytes, hipStream_t stream, const char* what) {
+  fam::MassArgs a{};
+  if (const fam_status st = mass_prepare(q, k, lse, s, W, scale, mass, workspace, workspace_bytes, a);
+      st != FAM_OK)
+    return st;
   return launched(fam::launch_mass(a, elem_of(dtype), stream), stream, what);
 }
 
@@ -497,10 +507,13 @@ size_t evict_select_workspace_size(int H, int S, int sinks, int recent) {
   return fam::select_workspace_bytes(select_slots(H), select_chunks(p));
 }
 
-fam_status evict_select(const float* scores, int64_t score_row_stride, int H, int S,
-                        const int64_t* budgets, int sinks, int recent, int32_t* idx,
-                        int64_t* offsets_dev, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+}  // extern "C"
+
+namespace {
+// Checks of evict_select's arguments (all but the scores' values).
+fam_status select_check(const float* scores, int64_t score_row_stride, int H, int S,
+                        const int64_t* budgets, int sinks, int recent, const int32_t* idx,
+                        const int64_t* offsets_dev, const void* workspace, size_t workspace_bytes) {
   if (H < 0) return fail(FAM_ERR_INVALID_ARG, "H must be >= 0 (got %d)", H);
   if (S < 1 || S > kMaxSeq) return fail(FAM_ERR_INVALID_ARG, "S = %d out of range", S);
   if (sinks < 0 || recent < 0) return fail(FAM_ERR_INVALID_ARG, "sinks and recent must be >= 0");
@@ -514,25 +527,48 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
   if (p.c1 - p.c0 > fam::kSelectLongMaxCandidates)
     return fail(FAM_ERR_UNSUPPORTED, "%d candidates per head exceed %d", p.c1 - p.c0,
                 fam::kSelectLongMaxCandidates);
-  const bool long_path = p.c1 - p.c0 > fam::kSelectMaxCandidates;
   const size_t need_ws = evict_select_workspace_size(H, S, sinks, recent);
   if (!workspace || workspace_bytes < need_ws)
     return fail(FAM_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu)", need_ws,
                 workspace ? workspace_bytes : (size_t)0);
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0)
     return fail(FAM_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
+  if (p.c1 - p.c0 > fam::kSelectMaxCandidates && fam::select_long_batch_heads(select_chunks(p)) < 1)
+    return fail(FAM_ERR_UNSUPPORTED, "evict_select: the device cannot hold the %d chunk workgroups of one head",
+                select_chunks(p));
+  return ok();
+}
+
+// Whether the select of these sizes can take its scores straight from the
+// mass pass's partial slices (one batch of heads in three launches, more
+// than one chunk a head, some head neither empty nor whole).
+bool select_from_parts_ok(int H, int S, const int64_t* budgets, int sinks, int recent) {
+  const Plan p = plan_of(S, sinks, recent);
+  if (H < 1 || H > fam::kSelectBatch || p.c1 - p.c0 > fam::kSelectMaxCandidates || select_chunks(p) < 2)
+    return false;
+  for (int h = 0; h < H; ++h) {
+    int64_t kh = budgets[h] > p.forced ? budgets[h] : p.forced;
+    if (kh > S) kh = S;
+    if (kh - p.forced != 0 && kh - p.forced != p.c1 - p.c0) return true;
+  }
+  return false;
+}
+
+// The select launches for checked arguments (H >= 1). With `part` non-null
+// (select_from_parts_ok holds), `scores` is the [H, S] mass, which the first
+// launch forms from the nsplit slices at `part` before it is read.
+fam_status select_run(const float* scores, int64_t score_row_stride, int H, int S,
+                      const int64_t* budgets, int sinks, int recent, int32_t* idx,
+                      int64_t* offsets_dev, void* workspace, const float* part, int nsplit,
+                      hipStream_t stream) {
+  const Plan p = plan_of(S, sinks, recent);
+  const bool long_path = p.c1 - p.c0 > fam::kSelectMaxCandidates;
   int64_t total = 0;
   for (int h = 0; h < H; ++h) {
     int64_t kh = budgets[h] > p.forced ? budgets[h] : p.forced;
     total += kh > S ? S : kh;
   }
-  int batch = fam::kSelectBatch;
-  if (long_path) {
-    batch = fam::select_long_batch_heads(select_chunks(p));
-    if (batch < 1)
-      return fail(FAM_ERR_UNSUPPORTED, "evict_select: the device cannot hold the %d chunk workgroups of one head",
-                  select_chunks(p));
-  }
+  const int batch = long_path ? fam::select_long_batch_heads(select_chunks(p)) : fam::kSelectBatch;
   fam::SelectArgs a{};
   a.scores = scores;
   a.row_stride = score_row_stride;
@@ -558,21 +594,74 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
       a.n_choose[i] = (int32_t)(kh - p.forced);
       off += kh;
     }
-    const hipError_t e = long_path ? fam::launch_select_long(a, static_cast<hipStream_t>(stream), h0 == 0)
-                                   : fam::launch_select(a, static_cast<hipStream_t>(stream));
+    const hipError_t e = part ? fam::launch_select_from_parts(a, part, nsplit, stream)
+                         : long_path ? fam::launch_select_long(a, stream, h0 == 0)
+                                     : fam::launch_select(a, stream);
     if (e != hipSuccess) return hip_status(e, "evict_select launch");
   }
-  const fam_status rc = launched(hipSuccess, static_cast<hipStream_t>(stream), "evict_select launch");
+  const fam_status rc = launched(hipSuccess, stream, "evict_select launch");
   if (rc != FAM_OK || !long_path || !sync_check()) return rc;
   // under the sync check: the long path's error word counts waits that ran
   // out of polls
   uint32_t word = 0;
-  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, static_cast<hipStream_t>(stream));
-  if (e == hipSuccess) e = hipStreamSynchronize(static_cast<hipStream_t>(stream));
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof word, hipMemcpyDeviceToHost, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) return hip_status(e, "evict_select (sync check)");
   if (word != 0u)
     return fail(FAM_ERR_TIMEOUT, "evict_select: %u wait(s) ran out of polls; the index lists are incomplete", word);
   return ok();
+}
+}  // namespace
+
+extern "C" {
+
+fam_status evict_select(const float* scores, int64_t score_row_stride, int H, int S,
+                        const int64_t* budgets, int sinks, int recent, int32_t* idx,
+                        int64_t* offsets_dev, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  if (const fam_status st = select_check(scores, score_row_stride, H, S, budgets, sinks, recent, idx,
+                                         offsets_dev, workspace, workspace_bytes);
+      st != FAM_OK || H == 0)
+    return st;
+  return select_run(scores, score_row_stride, H, S, budgets, sinks, recent, idx, offsets_dev, workspace,
+                    nullptr, 0, static_cast<hipStream_t>(stream));
+}
+
+fam_status fam_mass_select(const void* q, const void* k, const float* lse, fam_dtype dtype_arg, int B,
+                           int Hq, int Hkv, int S, int d, int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                           int64_t k_sb, int64_t k_sh, int64_t k_ss, int W, float scale, float* mass,
+                           void* mass_workspace, size_t mass_workspace_bytes,
+                           const int64_t* budgets, int sinks, int recent, int32_t* idx,
+                           int64_t* offsets_dev, void* select_workspace,
+                           size_t select_workspace_bytes, void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
+  if (const fam_status st = check_scores(q, k, dtype, s); st != FAM_OK) return st;
+  fam::MassArgs a{};
+  if (const fam_status st = mass_prepare(q, k, lse, s, W, scale, mass, mass_workspace,
+                                         mass_workspace_bytes, a);
+      st != FAM_OK)
+    return st;
+  const int H = B * Hkv;
+  if (const fam_status st = select_check(mass, S, H, S, budgets, sinks, recent, idx, offsets_dev,
+                                         select_workspace, select_workspace_bytes);
+      st != FAM_OK)
+    return st;
+  if (a.nsplit > 1) {
+    // the mass pass's slices are read while the select workspace is written
+    const uintptr_t m0 = reinterpret_cast<uintptr_t>(a.part);
+    const uintptr_t m1 = m0 + mass_split_bytes(s, a.nsplit);
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(select_workspace);
+    const uintptr_t s1 = s0 + select_workspace_bytes;
+    if (m0 < s1 && s0 < m1)
+      return fail(FAM_ERR_INVALID_ARG, "mass and select workspaces must not overlap");
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool fused = a.nsplit > 1 && select_from_parts_ok(H, S, budgets, sinks, recent);
+  hipError_t e = fam::launch_mass(a, elem_of(dtype), hs, !fused);
+  if (const fam_status st = launched(e, hs, "fam_mass_select (mass pass)"); st != FAM_OK) return st;
+  return select_run(mass, S, H, S, budgets, sinks, recent, idx, offsets_dev, select_workspace,
+                    fused ? a.part : nullptr, a.nsplit, hs);
 }
 
 // evict_select without a caller workspace: the workspace is a static device

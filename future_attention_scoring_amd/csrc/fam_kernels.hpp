@@ -69,7 +69,9 @@ constexpr int kMassQTile = 64;        // query rows per mass-pass step
 constexpr int kMassRangeTiles = 64;   // query tiles per range in range mode
 constexpr int kMassRangeMinS = 65536; // range mode from this many keys on
 constexpr int kMassMaxRanges = 128;   // at most this many ranges (partial slices)
-hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s);
+// With reduce == false and nsplit > 1 the partial sums stay in `part` and
+// the caller launches their reduction (the select launches that read them).
+hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s, bool reduce = true);
 
 // KVpop supervision target from per-query-head mass.
 struct TargetArgs {
@@ -109,6 +111,13 @@ struct SelectArgs {
 };
 size_t select_workspace_bytes(int slots, int nchunk);
 hipError_t launch_select(const SelectArgs& a, hipStream_t s);
+// The select launches over scores that are the mass pass's output, fed by its
+// partial sums part [nsplit][H * S]: the first launch adds the slices (the
+// reduction the mass pass would otherwise run) and builds the histograms.
+// Requires head0 == 0, nheads == H <= kSelectBatch, row_stride == S, more
+// than one chunk a head, at most kSelectMaxCandidates candidates and a head
+// that is not trivial; `a.scores` is the mass the launches write and read.
+hipError_t launch_select_from_parts(const SelectArgs& a, const float* part, int nsplit, hipStream_t s);
 size_t select_long_workspace_bytes(int slots);
 // Heads per long-path launch for heads of nchunk chunks (0: the device holds fewer).
 int select_long_batch_heads(int nchunk);

@@ -389,7 +389,7 @@ __global__ __launch_bounds__(kThreads) void mass_reduce_kernel(const float* part
 }
 
 template <int D, typename T>
-hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
+hipError_t launch_mass_t(const MassArgs& a, hipStream_t s, bool reduce) {
   const int nkb = (a.S + kKeysPerWG - 1) / kKeysPerWG;
   const bool per_head = a.mass_q != nullptr;
   // per-query-head mass splits only in range mode
@@ -400,7 +400,7 @@ hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((mass_kernel<D, T, true>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   else
     hipLaunchKernelGGL((mass_kernel<D, T, false>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
-  if (nsplit > 1) {
+  if (nsplit > 1 && reduce) {
     const int64_t n = (int64_t)a.B * (per_head ? a.Hq : a.Hkv) * a.S;
     const int64_t blocks = (n + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(mass_reduce_kernel, dim3((unsigned)(blocks < 4096 ? blocks : 4096)),
@@ -411,9 +411,10 @@ hipError_t launch_mass_t(const MassArgs& a, hipStream_t s) {
 
 }  // namespace
 
-hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s) {
-  if (a.d == 128) return e == Elem::kBf16 ? launch_mass_t<128, Bf16>(a, s) : launch_mass_t<128, Fp16>(a, s);
-  return e == Elem::kBf16 ? launch_mass_t<64, Bf16>(a, s) : launch_mass_t<64, Fp16>(a, s);
+hipError_t launch_mass(const MassArgs& a, Elem e, hipStream_t s, bool reduce) {
+  if (a.d == 128)
+    return e == Elem::kBf16 ? launch_mass_t<128, Bf16>(a, s, reduce) : launch_mass_t<128, Fp16>(a, s, reduce);
+  return e == Elem::kBf16 ? launch_mass_t<64, Bf16>(a, s, reduce) : launch_mass_t<64, Fp16>(a, s, reduce);
 }
 
 }  // namespace fam

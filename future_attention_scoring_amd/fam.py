@@ -45,6 +45,9 @@ _SIGNATURES = {
     "fam_soft_topk": (_i, [_p, _i, ctypes.c_double, ctypes.c_double, _p]),
     "evict_select": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
     "evict_select_workspace_size": (ctypes.c_size_t, [_i, _i, _i, _i]),
+    "fam_mass_select": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
+                             _i, _f, _p, _p, ctypes.c_size_t, _p, _i, _i, _p, _p, _p,
+                             ctypes.c_size_t, _p]),
     "evict_select_noalloc": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p]),
     "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
     "fam_compute_chunk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
@@ -348,6 +351,50 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(scores)))
     return idx, offsets
+
+
+def fam_mass_select(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,
+                    budgets: Sequence[int], sinks: int, recent: int, scale: Optional[float] = None,
+                    mass: Optional[torch.Tensor] = None, idx: Optional[torch.Tensor] = None,
+                    offsets: Optional[torch.Tensor] = None,
+                    mass_workspace: Optional[torch.Tensor] = None,
+                    select_workspace: Optional[torch.Tensor] = None
+                    ) -> Tuple[torch.Tensor, torch.Tensor, torch.Tensor]:
+    """fam_mass and then evict_select on the [B * Hkv, S] masses, in one call:
+    returns (mass [B, Hkv, S] (or [Hkv, S]), idx, offsets)."""
+    q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
+    lse = lse.contiguous()
+    if lse.numel() != B * Hq * S or lse.dtype != torch.float32:
+        raise FamError(1, "lse must be fp32 [B, Hq, S]")
+    H = B * Hkv
+    b = _i64_array(budgets)
+    if b.size != H:
+        raise FamError(1, f"{b.size} budgets for {H} heads")
+    if mass is None:
+        mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
+    _, host_off = evict_plan(b, S, sinks, recent)
+    if idx is None:
+        idx = torch.empty(int(host_off[-1]), dtype=torch.int32, device=q4.device)
+    if offsets is None:
+        offsets = torch.empty(H + 1, dtype=torch.int64, device=q4.device)
+    # both workspaces stay referenced until the launches are queued, so that
+    # the allocator cannot hand one's memory to the other
+    if mass_workspace is None:
+        n = fam_mass_workspace_size(B, Hq, Hkv, S)
+        mass_workspace = torch.empty(n, dtype=torch.uint8, device=q4.device) if n else None
+    mws, mbytes = ((mass_workspace.data_ptr(), mass_workspace.numel() * mass_workspace.element_size())
+                   if mass_workspace is not None else (None, 0))
+    if select_workspace is None:
+        nbytes = evict_select_workspace_size(H, S, sinks, recent)
+        select_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q4.device)
+    _check(load().fam_mass_select(q4.data_ptr(), k4.data_ptr(), lse.data_ptr(), _dtype_code(q4), B,
+                                  Hq, Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
+                                  0.0 if scale is None else scale, mass.data_ptr(), mws, mbytes,
+                                  b.ctypes.data, int(sinks), int(recent), idx.data_ptr(),
+                                  offsets.data_ptr(), select_workspace.data_ptr(),
+                                  select_workspace.numel() * select_workspace.element_size(),
+                                  _stream(q4)))
+    return (mass if q.dim() == 4 else mass[0]), idx, offsets
 
 
 def evict_select_noalloc(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,

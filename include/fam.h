@@ -395,6 +395,44 @@ fam_status evict_select(const float* scores, int64_t score_row_stride, int H, in
 size_t evict_select_workspace_size(int H, int S, int sinks, int recent);
 
 /* ------------------------------------------------------------------------
+ * fam_mass_select -- fam_mass, then evict_select on its output.
+ *
+ * [KVpop] "Defining Future Attention Utility" (the mass of each key) and
+ * "The KVpop Scoring Module" / Figure 1 (sinks + window + the best-scored
+ * rest): the budgeted selection runs on the masses just computed. The
+ * results are those of
+ *
+ *   fam_mass(q, k, lse, ..., W, scale, mass, mass_workspace, ...);
+ *   evict_select(mass, S, B * Hkv, S, budgets, sinks, recent, idx,
+ *                offsets_dev, select_workspace, ...);
+ *
+ * bit for bit (mass, idx and offsets_dev), with one launch fewer when the
+ * mass pass splits (a mass_workspace of fam_mass_workspace_size bytes), the
+ * heads B * Hkv number at most 64, each head has at most 131072 candidates
+ * in more than one chunk of 4096, and some head keeps part of its
+ * candidates: the launch that adds the mass pass's partial sums then also
+ * builds the selection's first histograms, from the sums in registers.
+ * Otherwise the two calls run one after the other.
+ *
+ *   arguments as for fam_mass (q ... mass_workspace_bytes) and for
+ *   evict_select (budgets ... select_workspace_bytes), with H = B * Hkv
+ *   heads of S scores (the mass rows); mass, idx, offsets_dev and the two
+ *   workspaces must not overlap (overlapping workspaces are refused).
+ * Errors: those of fam_mass and evict_select; nothing is launched when an
+ * argument is refused.
+ * ---------------------------------------------------------------------- */
+fam_status fam_mass_select(const void* q, const void* k, const float* lse, fam_dtype dtype,
+                           int B, int Hq, int Hkv, int S, int d,
+                           int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                           int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                           int W, float scale, float* mass,
+                           void* mass_workspace, size_t mass_workspace_bytes,
+                           const int64_t* budgets, int sinks, int recent,
+                           int32_t* idx, int64_t* offsets_dev,
+                           void* select_workspace, size_t select_workspace_bytes,
+                           void* stream);
+
+/* ------------------------------------------------------------------------
  * evict_select_noalloc -- evict_select for callers that cannot allocate.
  *
  * For callers that may not allocate device memory at all (code under HIP

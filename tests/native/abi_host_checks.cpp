@@ -115,6 +115,13 @@ int main() {
            FAM_ERR_UNSUPPORTED);
     EXPECT(evict_select_noalloc(ffake, 100, 2, 100, b, -1, 4, ifake, lfake, nullptr) == FAM_ERR_INVALID_ARG);
     EXPECT(evict_select(ffake, 100, 0, 100, nullptr, 4, 4, ifake, lfake, nullptr, 0, nullptr) == FAM_OK);
+    const size_t mws = fam_mass_workspace_size(1, 4, 2, 8192), sws = evict_select_workspace_size(2, 8192, 4, 64);
+    EXPECT(fam_mass_select(fake, fake, ffake, FAM_BF16, 1, 4, 2, 8192, 128, 0, 8192 * 128, 128, 0, 8192 * 128, 128,
+                           4, 0.f, ffake, fake, mws, b, 4, 64, ifake, lfake, fake, sws, nullptr) ==
+           FAM_ERR_INVALID_ARG);                                                     // overlapping workspaces
+    EXPECT(fam_mass_select(fake, fake, ffake, FAM_BF16, 1, 4, 2, 8192, 128, 0, 8192 * 128, 128, 0, 8192 * 128, 128,
+                           4, 0.f, ffake, fake, mws, b, 4, 64, ifake, lfake, nullptr, 0, nullptr) ==
+           FAM_ERR_WORKSPACE);
   }
   EXPECT(kv_compact(fake, fake, 4, 2, 100, 128, 0, 128, 0, 128, ifake, lfake, 10, fake, fake, nullptr) ==
          FAM_ERR_UNSUPPORTED);

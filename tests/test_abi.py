@@ -178,6 +178,36 @@ def test_fam_mass_and_compute_validation():
     assert st == INVALID
 
 
+def test_fam_mass_select_validation():
+    """fam_mass_select refuses what fam_mass or evict_select refuses, and
+    overlapping workspaces, before anything is launched."""
+    lib = fam.load()
+    S, H = 8192, 2
+    mws = lib.fam_mass_workspace_size(1, 4, 2, S)
+    sws = lib.evict_select_workspace_size(H, S, 4, 64)
+    assert mws > 0 and sws > 0
+    b = np.array([1000, 2000], dtype=np.int64)
+
+    def call(lse=FAKE, W=4, mass_ws=FAKE, mass_bytes=mws, budgets=b.ctypes.data, sinks=4, recent=64,
+             sel_ws=FAKE + (1 << 30), sel_bytes=sws, d=128, idx=FAKE):
+        return lib.fam_mass_select(FAKE, FAKE, lse, 0, 1, 4, 2, S, d, 0, S * d, d, 0, S * d, d, W, 0.0,
+                                   FAKE, mass_ws, mass_bytes, budgets, sinks, recent, idx, FAKE,
+                                   sel_ws, sel_bytes, None)
+
+    assert call(lse=None) == INVALID                       # as fam_mass
+    assert call(W=-1) == INVALID
+    assert call(d=100) == UNSUPPORTED
+    assert call(mass_ws=FAKE + 4) == INVALID               # misaligned mass workspace
+    assert call(sel_bytes=sws - 1) == 3                    # FAM_ERR_WORKSPACE, as evict_select
+    assert call(sel_ws=None) == 3
+    assert call(idx=None) == INVALID
+    assert call(sinks=-1) == INVALID
+    bad = np.array([1000, -1], dtype=np.int64)
+    assert call(budgets=bad.ctypes.data) == INVALID
+    assert call(sel_ws=FAKE + 1024) == INVALID             # inside the mass workspace
+    assert call(sel_ws=FAKE + mws - 16) == INVALID         # overlapping its end
+
+
 def test_mass_workspace_size():
     lib = fam.load()
     # from 65536 keys on, one part per range of 64 query tiles of 64 rows

@@ -94,6 +94,19 @@ def test_score_entry_points_stay_inside_their_outputs(B, Hq, Hkv, S, d, W):
     fam.fam_mass(q, k, lse2.t, W, mass=mass2.t, workspace=w2.t)
     mass2.check("fam_mass")
     w2.check("fam_mass workspace")
+    # the mass pass feeding the select (the fused launch when it splits)
+    H, sinks, recent = B * Hkv, 4, W + 3
+    budgets = [S // 3 + 7 * h for h in range(H)]
+    _, off = fam.evict_plan(budgets, S, sinks, recent)
+    mass4, idx4, offs4 = Guarded((B, Hkv, S), torch.float32), Guarded((int(off[-1]),), torch.int32), \
+        Guarded((H + 1,), torch.int64)
+    w5, w6 = ws(fam.fam_mass_workspace_size(B, Hq, Hkv, S)), ws(fam.evict_select_workspace_size(H, S, sinks, recent))
+    fam.fam_mass_select(q, k, lse2.t, W, budgets, sinks, recent, mass=mass4.t, idx=idx4.t, offsets=offs4.t,
+                        mass_workspace=w5.t, select_workspace=w6.t)
+    for n, x in (("fam_mass_select mass", mass4), ("fam_mass_select idx", idx4),
+                 ("fam_mass_select offsets", offs4), ("fam_mass_select mass workspace", w5),
+                 ("fam_mass_select select workspace", w6)):
+        x.check(n)
     mq = Guarded((B, Hq, S), torch.float32)
     w3 = ws(fam.fam_mass_per_head_workspace_size(B, Hq, Hkv, S))
     fam.fam_mass_per_head(q, k, lse2.t, W, mass_q=mq.t, workspace=w3.t)
