@@ -1,8 +1,9 @@
 """The hot path captured in a HIP graph and replayed.
 
 One step of the path (key norms, first pass, mass pass, evict_select,
-kv_compact) and one compression of the chunked loop (evict_select,
-kv_compact_inplace with its fill kernel) are captured with
+kv_compact), the same step with fam_mass_select, and one compression of the
+chunked loop (evict_select, kv_compact_inplace with its fill kernel) are
+captured with
 torch.cuda.graph and replayed several times, with eager work of the same
 kernels and synchronisations between the replays. Every replay must equal
 the eager result bit for bit, also after the inputs were overwritten in
@@ -165,4 +166,70 @@ def test_inplace_compression_and_cutoff_in_a_graph():
         # eager in-place compaction on other buffers between replays
         k2, v2 = k0.clone(), v0.clone()
         fam.kv_compact_inplace(k2, v2, idx, offsets, total_rows=total)
+        torch.cuda.synchronize()
+
+
+def test_combined_mass_select_step_in_a_graph():
+    """The step with fam_mass_select (the mass pass's reduction building the
+    select histograms) captured and replayed: every replay equals the eager
+    result and the two-call form bit for bit."""
+    B, Hq, Hkv, S, d, W, sinks, recent = 1, 8, 2, 9000, 128, 64, 4, 64
+    budgets = [2500, 4100]
+    say(f"graph: fam_lse + fam_mass_select + kv_compact S={S}")
+    q, k, v = seeded(31, (B, Hq, S, d)), seeded(32, (B, Hkv, S, d)), seeded(33, (B, Hkv, S, d))
+    knorm = torch.empty(B, Hkv, fam.fam_key_norm_parts(S), device=DEV)
+    lse = torch.empty(B, Hq, S, device=DEV)
+    mass = torch.empty(B, Hkv, S, device=DEV)
+    mws = torch.empty(fam.fam_mass_workspace_size(B, Hq, Hkv, S), dtype=torch.uint8, device=DEV)
+    assert mws.numel() > 0                    # the mass pass splits: the combined launch runs
+    _, host_off = fam.evict_plan(budgets, S, sinks, recent)
+    total = int(host_off[-1])
+    idx = torch.empty(total, dtype=torch.int32, device=DEV)
+    offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=DEV)
+    sws = torch.empty(max(16, fam.evict_select_workspace_size(Hkv, S, sinks, recent)), dtype=torch.uint8,
+                      device=DEV)
+    k_new = torch.empty(total, d, dtype=k.dtype, device=DEV)
+    v_new = torch.empty_like(k_new)
+
+    def step():
+        fam.fam_key_norms(k, knorm=knorm)
+        fam.fam_lse(q, k, lse=lse, knorm=knorm)
+        fam.fam_mass_select(q, k, lse, W, budgets, sinks, recent, mass=mass, idx=idx, offsets=offsets,
+                            mass_workspace=mws, select_workspace=sws)
+        fam.kv_compact(k[0], v[0], idx, offsets, total_rows=total, k_new=k_new, v_new=v_new)
+
+    def snapshot():
+        return [t.clone() for t in (lse, mass, idx, offsets, k_new.view(torch.int16), v_new.view(torch.int16))]
+
+    step()
+    torch.cuda.synchronize()
+    want = snapshot()
+    ref_mass = fam.fam_mass(q, k, lse, W)
+    ref_idx, ref_off = fam.evict_select(ref_mass[0], budgets, sinks, recent)
+    torch.cuda.synchronize()
+    assert torch.equal(ref_mass.view(torch.int32), want[1].view(torch.int32))
+    assert torch.equal(ref_idx, want[2]) and torch.equal(ref_off, want[3])
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for t in (lse, mass, k_new, v_new):
+            t.fill_(0)
+        idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(snapshot(), want):
+            assert torch.equal(a, b), f"replay {rep}"
+        # eager work of the same kernels on other data between replays
+        q2, k2 = seeded(40 + rep, (B, Hq, S, d)), seeded(50 + rep, (B, Hkv, S, d))
+        fam.fam_mass_select(q2, k2, fam.fam_lse(q2, k2), W, budgets, sinks, recent)
         torch.cuda.synchronize()
