@@ -70,6 +70,8 @@ def check(q, k, W, budgets, sinks, recent, mass_ws_bytes=None):
     (3, 1, 4, 4, 8192, 0, 0, 0),          # no sinks, no window
     (4, 1, 8, 8, 16384, 128, 4, 128),     # eight heads, one a XCD
     (5, 1, 6, 3, 70001, 512, 4, 512),     # ranges of query rows, ragged rows
+    (6, 3, 8, 4, 8200, 32, 4, 32),        # 12 heads: a last group of 8 heads only half full
+    (7, 8, 8, 8, 8192, 16, 4, 16),        # 64 heads: one full batch
 ])
 def test_mass_select_matches_two_calls(seed, B, Hq, Hkv, S, W, sinks, recent):
     say(f"fam_mass_select seed={seed} B={B} Hq={Hq} Hkv={Hkv} S={S} W={W} sinks={sinks} recent={recent}")
