@@ -8,7 +8,8 @@ index lists must also equal the oracle's selection on the returned masses.
 Cases cover the short-sequence splits, the ranges of query rows from 65536
 keys on, rows whose length is not a multiple of 4, positions before the first
 and after the last chunk, and every fallback (no split, one chunk a head,
-trivial budgets, more heads than one batch).
+trivial budgets, more heads than one batch, more candidates than the
+three-launch select takes).
 """
 import numpy as np
 import pytest
@@ -113,6 +114,9 @@ def test_mass_select_fallbacks():
     # more heads than one select batch (72 > 64)
     q2, k2 = inputs(13, 9, 8, 8, 5000, d=64)
     check(q2, k2, 16, budgets_for(13, 72, 5000, 4, 16), 4, 16)
+    # more than 131072 candidates a head: the round-based select after the mass pass's ranges
+    q3, k3 = inputs(14, 1, 2, 1, 140000, d=64)
+    check(q3, k3, 256, [50000], 4, 256)
 
 
 def test_mass_select_fp16_and_strided_views():
