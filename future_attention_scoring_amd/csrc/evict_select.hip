@@ -115,12 +115,16 @@ __device__ __forceinline__ bool trivial_head(const SelectArgs& p, int n_choose) 
 }
 
 // Keys of positions base + 16*tid + i (0 outside the candidate range).
-// Interior chunks of 16-byte aligned rows issue four 16-byte loads.
+// Interior chunks of 16-byte aligned rows issue four 16-byte loads. So do the
+// edge chunks of such rows when they hold a multiple of 4 scores: a piece of
+// 4 positions then lies wholly inside the row or wholly past its end, and a
+// piece past it loads the row's last piece (in bounds) and is masked like
+// every position outside the candidates.
 __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row, int base,
                                            uint32_t (&k)[kPerThread]) {
   const int first = base + kPerThread * (int)threadIdx.x;
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  if (vec_ok && base >= p.c0 && base + kSelectChunk <= p.c1) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  if (aligned && base >= p.c0 && base + kSelectChunk <= p.c1) {
     f32x4_t f[kPerThread / 4];
 #pragma unroll
     for (int it = 0; it < kPerThread / 4; ++it)
@@ -131,7 +135,21 @@ __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row
       for (int c = 0; c < 4; ++c) k[4 * it + c] = order_key(f[it][c]);
     return;
   }
-  // edge chunk: every load reads a clamped in-range position, then masks
+  if (aligned && (p.S & 3) == 0) {
+    f32x4_t f[kPerThread / 4];
+#pragma unroll
+    for (int it = 0; it < kPerThread / 4; ++it)
+      f[it] = *reinterpret_cast<const f32x4_t*>(row + min(first + 4 * it, p.S - 4));
+#pragma unroll
+    for (int it = 0; it < kPerThread / 4; ++it)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int at = first + 4 * it + c;
+        k[4 * it + c] = (at >= p.c0 && at < p.c1) ? order_key(f[it][c]) : 0u;
+      }
+    return;
+  }
+  // edge chunks of other rows: every load reads a clamped in-range position, then masks
   float f[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) f[i] = row[min(max(first + i, p.c0), p.c1 - 1)];
@@ -591,7 +609,7 @@ __device__ __forceinline__ void scatter_phase(const SelectArgs& p) {
 // from the sums still in registers. Workgroups past the select grid reduce
 // the positions no chunk covers (before the first chunk, after the last).
 constexpr int kReduceBatch = 8;     // slices in flight per thread
-constexpr int kReduceThreads = 256; // threads per chunk (16 consecutive positions each)
+constexpr int kReduceThreads = 256; // threads per chunk (16 positions each)
 
 __device__ __forceinline__ float reduce_one(const float* part, int64_t n, int nsplit, int64_t e) {
   float acc = 0.f;
@@ -630,19 +648,27 @@ __global__ __launch_bounds__(NT) void sel_hist_reduce(SelectArgs p, const float*
   }
   int w, hl;
   if (!wg_coords(p, w, hl)) return;
-  const int first = a0 + w * kSelectChunk + PT * (int)threadIdx.x;
+  const int base = a0 + w * kSelectChunk;
   const int64_t row = (int64_t)hl * S;
+  // piece q of this thread holds positions piece(q) .. piece(q) + 3; the
+  // pieces of a wave's 16-byte load lie side by side (1 KB in a row), which
+  // the histogram allows (it does not care which thread holds a position)
+  auto piece = [&](int q) { return base + 4 * (int)threadIdx.x + 4 * NT * q; };
+  auto pos = [&](int i) { return piece(i >> 2) + (i & 3); };
   float acc[PT];
   const bool vec_ok = ((reinterpret_cast<uintptr_t>(part) | reinterpret_cast<uintptr_t>(mass)) & 15u) == 0 &&
                       (S & 3) == 0;
-  if (vec_ok && first + PT <= S) {
+  if (vec_ok) {
+    // rows of a multiple of 4: a piece lies wholly inside the row or wholly
+    // past its end; pieces past it load the row's last piece (in bounds) and
+    // are neither stored nor counted
     for (int k0 = 0; k0 < nsplit; k0 += kReduceBatch) {
       f32x4_t v[kReduceBatch][PT / 4];
 #pragma unroll
       for (int j = 0; j < kReduceBatch; ++j) {
-        const float* src = part + (int64_t)min(k0 + j, nsplit - 1) * n + row + first;
+        const float* src = part + (int64_t)min(k0 + j, nsplit - 1) * n + row;
 #pragma unroll
-        for (int q = 0; q < PT / 4; ++q) v[j][q] = *reinterpret_cast<const f32x4_t*>(src + 4 * q);
+        for (int q = 0; q < PT / 4; ++q) v[j][q] = *reinterpret_cast<const f32x4_t*>(src + min(piece(q), S - 4));
       }
 #pragma unroll
       for (int j = 0; j < kReduceBatch; ++j)
@@ -656,10 +682,11 @@ __global__ __launch_bounds__(NT) void sel_hist_reduce(SelectArgs p, const float*
     }
 #pragma unroll
     for (int q = 0; q < PT / 4; ++q)
-      *reinterpret_cast<f32x4_t*>(mass + row + first + 4 * q) =
-          f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
+      if (piece(q) < S)
+        *reinterpret_cast<f32x4_t*>(mass + row + piece(q)) =
+            f32x4_t{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]};
   } else {
-    // the row's end or unaligned rows: positions clamped into the row, stores masked
+    // unaligned rows: positions clamped into the row, stores masked
 #pragma unroll
     for (int i = 0; i < PT; ++i) acc[i] = 0.f;
     for (int k0 = 0; k0 < nsplit; k0 += kReduceBatch) {
@@ -668,7 +695,7 @@ __global__ __launch_bounds__(NT) void sel_hist_reduce(SelectArgs p, const float*
       for (int j = 0; j < kReduceBatch; ++j) {
         const float* src = part + (int64_t)min(k0 + j, nsplit - 1) * n + row;
 #pragma unroll
-        for (int i = 0; i < PT; ++i) v[j][i] = src[min(first + i, S - 1)];
+        for (int i = 0; i < PT; ++i) v[j][i] = src[min(pos(i), S - 1)];
       }
 #pragma unroll
       for (int j = 0; j < kReduceBatch; ++j)
@@ -679,14 +706,14 @@ __global__ __launch_bounds__(NT) void sel_hist_reduce(SelectArgs p, const float*
     }
 #pragma unroll
     for (int i = 0; i < PT; ++i)
-      if (first + i < S) mass[row + first + i] = acc[i];
+      if (pos(i) < S) mass[row + pos(i)] = acc[i];
   }
   if (trivial_head(p, p.n_choose[hl])) return;
   for (int i = threadIdx.x; i < kBins; i += NT) hist[i] = 0u;
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < PT; ++i)
-    if (first + i >= p.c0 && first + i < p.c1) atomicAdd(&hist[key_top(order_key(acc[i]))], 1u);
+    if (pos(i) >= p.c0 && pos(i) < p.c1) atomicAdd(&hist[key_top(order_key(acc[i]))], 1u);
   __syncthreads();
   uint32_t cum[BPT];
   descending_cum<NT>(hist, sh, cum);
