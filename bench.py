@@ -607,16 +607,20 @@ def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
             "ms_step": wall * 1e3 / steps, "t_fam": t_fam, "t_ec": t_ec, "flushed": flushed}
 
 
-def mass_select_row(reps, q, k, wl, run, stream):
+def mass_select_row(reps, q, k, wl, run, stream, derive=False):
     """fam_mass_select against fam_mass followed by evict_select on the same
-    workload (HIP events on the launch stream, the two forms alternating in
-    every rep). Both forms spend about 57 ms in the mass pass at 128k, whose
-    run-to-run spread is far larger than the launches the combined form
-    saves, so only the totals are reported; the saving itself is read from a
-    kernel trace (end of the mass pass to the end of the last select launch)."""
+    workload (HIP events on the launch stream, the forms alternating in every
+    rep). At 128k both forms spend about 57 ms in the mass pass, whose
+    run-to-run spread is far larger than the launch the combined form saves,
+    so only the totals are reported there and the saving is read from a kernel
+    trace (end of the mass pass to the end of the last select launch). With
+    `derive` (short workloads, whose mass pass is short enough), fam_mass and
+    evict_select are timed apart too, and the selection's share of the
+    combined call (its time minus fam_mass's, paired per rep) gives the
+    select + compact rate of the combined form."""
     dev = q.device
     B, Hq, Hkv, S = 1, wl.Hq, wl.Hkv, wl.S
-    lse, budgets, total = run["lse"], run["budgets"], run["total"]
+    lse, budgets, total, work = run["lse"], run["budgets"], run["total"], run["work"]
     mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=dev)
     idx = torch.empty(total, dtype=torch.int32, device=dev)
     offsets = torch.empty(Hkv + 1, dtype=torch.int64, device=dev)
@@ -628,29 +632,47 @@ def mass_select_row(reps, q, k, wl, run, stream):
         fam.fam_mass_select(q, k, lse, wl.W, budgets, wl.sinks, wl.recent, mass=mass, idx=idx,
                             offsets=offsets, mass_workspace=mws, select_workspace=sws)
 
-    def apart():
+    def mass_only():
         fam.fam_mass(q, k, lse, wl.W, mass=mass, workspace=mws)
+
+    def select_only():
         fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets, workspace=sws)
 
     fused()
-    apart()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    mass_only()
+    select_only()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(reps)]
     for e in ev:
         e[0].record(stream)
         fused()
         e[1].record(stream)
-        apart()
-        e[2].record(stream)
+        mass_only()
+        if derive:
+            e[2].record(stream)
+        select_only()
+        e[3].record(stream)
     torch.cuda.synchronize()
     f = [e[0].elapsed_time(e[1]) for e in ev]
-    a = [e[1].elapsed_time(e[2]) for e in ev]
-    return {"reps": reps, "ms_median": {"fam_mass_select": round(float(np.median(f)), 4),
-                                        "fam_mass + evict_select": round(float(np.median(a)), 4)},
-            "ms_spread": {"fam_mass_select": round(max(f) - min(f), 4),
-                          "fam_mass + evict_select": round(max(a) - min(a), 4)}}
+    a = [e[1].elapsed_time(e[3]) for e in ev]
+    out = {"reps": reps, "ms_median": {"fam_mass_select": round(float(np.median(f)), 4),
+                                       "fam_mass + evict_select": round(float(np.median(a)), 4)},
+           "ms_spread": {"fam_mass_select": round(max(f) - min(f), 4),
+                         "fam_mass + evict_select": round(max(a) - min(a), 4)}}
+    if derive:
+        m = [e[1].elapsed_time(e[2]) for e in ev]
+        sel = [e[2].elapsed_time(e[3]) for e in ev]
+        share = float(np.median([fi - mi for fi, mi in zip(f, m)])) * 1e3
+        nbytes = work["select_bytes"] + work["compact_bytes"]
+        rate = nbytes / ((share + run["ms"]["kv_compact"] * 1e3) * 1e-6)
+        out.update({"fam_mass_ms_median": round(float(np.median(m)), 4),
+                    "evict_select_us_median": round(float(np.median(sel)) * 1e3, 1),
+                    "select_us_in_fam_mass_select": round(share, 1),
+                    "evict_compact_gbps_combined": round(rate / 1e9, 2),
+                    "evict_compact_hbm_frac_combined": round(rate / PEAK_HBM_BYTES, 4)})
+    return out
 
 
-def workload_row(wl, steps, warmup, stream):
+def workload_row(wl, steps, warmup, stream, mass_select_reps=0):
     """One more workload's step, timed on its own inputs (for the lines of
     the other score workloads beside the headline one)."""
     dev = torch.device("cuda:0")
@@ -668,6 +690,8 @@ def workload_row(wl, steps, warmup, stream):
            "evict_compact_hbm_frac": round((work["select_bytes"] + work["compact_bytes"]) / run["t_ec"]
                                            / PEAK_HBM_BYTES, 4),
            "kernel_ms": {n: round(ms[n], 4) for n in run["names"]}}
+    if mass_select_reps > 0:
+        out["mass_select"] = mass_select_row(mass_select_reps, q, k, wl, run, stream, derive=True)
     del q, k, v, run
     torch.cuda.empty_cache()
     return out
@@ -785,7 +809,8 @@ def main():
     del q, k, v, mass, lse, run
     torch.cuda.empty_cache()
     if args.other_workloads > 0 and args.workload == "llama-128k":
-        out["other_workloads"] = [workload_row(WORKLOADS[n](), args.other_workloads, 1, stream)
+        out["other_workloads"] = [workload_row(WORKLOADS[n](), args.other_workloads, 1, stream,
+                                               4 * args.mass_select_reps)
                                   for n in ("qwen3-4b-8k", "long-trace-32k")]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)
