@@ -104,12 +104,30 @@ __host__ __device__ inline int chunks_of(const SelectArgs& p) {
 }
 
 // Keys of positions base + 16*tid + i (0 outside the candidate range).
-// Interior chunks of 16-byte aligned rows issue four 16-byte loads.
+// Interior chunks of 16-byte aligned rows issue four 16-byte loads. So do the
+// edge chunks of such rows when they hold a multiple of 4 scores: a piece of
+// 4 positions then lies wholly inside the row or wholly past its end, and a
+// piece past it loads the row's last piece (in bounds) and is masked like
+// every position outside the candidates.
 __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row, int base,
                                            uint32_t (&k)[kPerThread]) {
   const int first = base + kPerThread * (int)threadIdx.x;
-  const bool vec_ok = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
-  if (vec_ok && base >= p.c0 && base + kSelectChunk <= p.c1) {
+  const bool aligned = (reinterpret_cast<uintptr_t>(row) & 15u) == 0;
+  if (aligned && (base < p.c0 || base + kSelectChunk > p.c1) && (p.S & 3) == 0) {
+    f32x4_t f[kPerThread / 4];
+#pragma unroll
+    for (int it = 0; it < kPerThread / 4; ++it)
+      f[it] = *reinterpret_cast<const f32x4_t*>(row + min(first + 4 * it, p.S - 4));
+#pragma unroll
+    for (int it = 0; it < kPerThread / 4; ++it)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int at = first + 4 * it + c;
+        k[4 * it + c] = (at >= p.c0 && at < p.c1) ? order_key(f[it][c]) : 0u;
+      }
+    return;
+  }
+  if (aligned && base >= p.c0 && base + kSelectChunk <= p.c1) {
     f32x4_t f[kPerThread / 4];
 #pragma unroll
     for (int it = 0; it < kPerThread / 4; ++it)
@@ -120,7 +138,7 @@ __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row
       for (int c = 0; c < 4; ++c) k[4 * it + c] = order_key(f[it][c]);
     return;
   }
-  // edge chunk: every load reads a clamped in-range position, then masks
+  // edge chunks of other rows: every load reads a clamped in-range position, then masks
   float f[kPerThread];
 #pragma unroll
   for (int i = 0; i < kPerThread; ++i) f[i] = row[min(max(first + i, p.c0), p.c1 - 1)];
