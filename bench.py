@@ -525,11 +525,14 @@ def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
         fam.fam_lse(q, k, lse=lse, knorm=knorm)
         if events:
             events[1].record(stream)
-        fam.fam_mass(q, k, lse, wl.W, mass=mass, workspace=mass_ws)
+        # the mass pass's reduction also builds the selection's first
+        # histograms (budget-free), so the select that follows starts at
+        # its second launch
+        fam.fam_mass_prepare_select(q, k, lse, wl.W, wl.sinks, wl.recent, mass=mass, mass_workspace=mass_ws,
+                                    select_workspace=ws)
         if events:
             events[2].record(stream)
-        fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets,
-                         workspace=ws)
+        fam.evict_select_prepared(mass[0], budgets, wl.sinks, wl.recent, ws, idx=idx, offsets=offsets)
         if events:
             events[3].record(stream)
         fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)
@@ -569,16 +572,31 @@ def time_step(wl, q, k, v, steps, warmup, stream, flushed_reps=0, clocks=None):
         for i, e in enumerate(fe):
             flush.fill_(i & 0x7f)
             e[0].record(stream)
-            fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets, workspace=ws)
+            fam.evict_select_prepared(mass[0], budgets, wl.sinks, wl.recent, ws, idx=idx, offsets=offsets)
             e[1].record(stream)
             fam.kv_compact(k[0], v[0], idx, offsets, total, k_new=k_new, v_new=v_new)
             e[2].record(stream)
         torch.cuda.synchronize()
         sel_us = float(np.median([e[0].elapsed_time(e[1]) for e in fe])) * 1e3
+        # the whole evict_select (its own histogram launch included), warm and
+        # after the fill, for comparison with the prepared form of the step
+        full = {}
+        for mode in ("warm", "flushed"):
+            xe = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(flushed_reps)]
+            for i, e in enumerate(xe):
+                if mode == "flushed":
+                    flush.fill_(i & 0x7f)
+                e[0].record(stream)
+                fam.evict_select(mass[0], budgets, wl.sinks, wl.recent, idx=idx, offsets=offsets, workspace=ws)
+                e[1].record(stream)
+            torch.cuda.synchronize()
+            full[mode] = round(float(np.median([e[0].elapsed_time(e[1]) for e in xe])) * 1e3, 1)
+        # the full call rewrote the workspace for the same scores: still prepared
         cmp_us = float(np.median([e[1].elapsed_time(e[2]) for e in fe])) * 1e3
         nbytes = work["select_bytes"] + work["compact_bytes"]
         flushed = {"reps": flushed_reps, "caches": "512 MiB fill before every rep (untimed)",
                    "select_us": round(sel_us, 1), "compact_us": round(cmp_us, 1), "bytes": nbytes,
+                   "evict_select_whole_us": full,
                    "GBps": round(nbytes / ((sel_us + cmp_us) * 1e-6) / 1e9, 1),
                    "hbm_frac": round(nbytes / ((sel_us + cmp_us) * 1e-6) / PEAK_HBM_BYTES, 4)}
         # what a plain device copy of the compaction's bytes (the kept K and V
@@ -672,9 +690,11 @@ def mass_select_row(reps, q, k, wl, run, stream, derive=False):
     return out
 
 
-def workload_row(wl, steps, warmup, stream, mass_select_reps=0):
+def workload_row(wl, steps, warmup, stream, mass_select_reps=0, oracle_select=False):
     """One more workload's step, timed on its own inputs (for the lines of
-    the other score workloads beside the headline one)."""
+    the other score workloads beside the headline one); with `oracle_select`,
+    the oracle's select + compact on the same masses and K/V, timed on the
+    host."""
     dev = torch.device("cuda:0")
     t = wl.tensors()
     q, k, v = (t[n].to(dev) for n in ("q", "k", "v"))
@@ -692,6 +712,10 @@ def workload_row(wl, steps, warmup, stream, mass_select_reps=0):
            "kernel_ms": {n: round(ms[n], 4) for n in run["names"]}}
     if mass_select_reps > 0:
         out["mass_select"] = mass_select_row(mass_select_reps, q, k, wl, run, stream, derive=True)
+    if oracle_select:
+        host = {"mass": run["mass"][0].cpu().numpy(), "k": k[0].cpu().view(torch.int16).numpy(),
+                "v": v[0].cpu().view(torch.int16).numpy(), "budgets": run["budgets"]}
+        out["cpu_oracle_select_compact"] = oracle_select_compact(wl, host, False)[wl.name]
     del q, k, v, run
     torch.cuda.empty_cache()
     return out
@@ -778,6 +802,8 @@ def main():
         "config": {"workload": wl.name, "batch": 1, "q_heads": Hq, "kv_heads": Hkv, "seq_len": S,
                    "head_dim": wl.d, "window": wl.W, "sinks": wl.sinks, "recent": wl.recent,
                    "kept_total": total, "budgets": [int(b) for b in budgets]},
+        "step_calls": ["fam_key_norms", "fam_lse", "fam_mass_prepare_select", "evict_select_prepared",
+                       "kv_compact"],
         "fam_mfma_frac": round((work["lse_flops"] + work["mass_flops"]) / t_fam / PEAK_BF16_FLOPS, 4),
         "fam_pairs_per_s": work["causal_pairs"] / t_fam,
         "evict_compact_gbps": round((work["select_bytes"] + work["compact_bytes"]) / t_ec / 1e9, 2),
@@ -810,7 +836,7 @@ def main():
     torch.cuda.empty_cache()
     if args.other_workloads > 0 and args.workload == "llama-128k":
         out["other_workloads"] = [workload_row(WORKLOADS[n](), args.other_workloads, 1, stream,
-                                               4 * args.mass_select_reps)
+                                               4 * args.mass_select_reps, not args.no_cpu_baseline)
                                   for n in ("qwen3-4b-8k", "long-trace-32k")]
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl)

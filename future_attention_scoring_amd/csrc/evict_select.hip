@@ -765,8 +765,13 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_select_from_parts(const SelectArgs& a, const float* part, int nsplit,
-                                    hipStream_t s) {
+hipError_t launch_select_hist(const SelectArgs& a, hipStream_t s) {
+  const int groups = (a.nheads + kXcds - 1) / kXcds;
+  hipLaunchKernelGGL(sel_hist, dim3(kXcds * a.nchunk * groups), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_hist_reduce(const SelectArgs& a, const float* part, int nsplit, hipStream_t s) {
   const int groups = (a.nheads + kXcds - 1) / kXcds;
   const int ngrid = kXcds * a.nchunk * groups;
   const int a0 = a.c0 & ~3;
@@ -776,9 +781,24 @@ hipError_t launch_select_from_parts(const SelectArgs& a, const float* part, int 
   const int64_t extra = blocks < 1024 ? blocks : 1024;
   hipLaunchKernelGGL(sel_hist_reduce<kReduceThreads>, dim3((unsigned)(ngrid + extra)), dim3(kReduceThreads), 0, s,
                      a, part, const_cast<float*>(a.scores), nsplit, ngrid);
-  hipLaunchKernelGGL(sel_collect, dim3(ngrid), dim3(kThreads), 0, s, a);
-  hipLaunchKernelGGL(sel_scatter, dim3(ngrid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
+}
+
+hipError_t launch_select_prepared(const SelectArgs& a, hipStream_t s) {
+  const int groups = (a.nheads + kXcds - 1) / kXcds;
+  const dim3 grid(kXcds * a.nchunk * groups);
+  bool all_trivial = true;
+  for (int i = 0; i < a.nheads; ++i)
+    if (a.n_choose[i] != 0 && a.n_choose[i] != a.c1 - a.c0) all_trivial = false;
+  if (!all_trivial) hipLaunchKernelGGL(sel_collect, grid, dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(sel_scatter, grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_select_from_parts(const SelectArgs& a, const float* part, int nsplit,
+                                    hipStream_t s) {
+  const hipError_t e = launch_select_hist_reduce(a, part, nsplit, s);
+  return e != hipSuccess ? e : launch_select_prepared(a, s);
 }
 
 }  // namespace fam

@@ -510,19 +510,16 @@ size_t evict_select_workspace_size(int H, int S, int sinks, int recent) {
 }  // extern "C"
 
 namespace {
-// Checks of evict_select's arguments (all but the scores' values).
-fam_status select_check(const float* scores, int64_t score_row_stride, int H, int S,
-                        const int64_t* budgets, int sinks, int recent, const int32_t* idx,
-                        const int64_t* offsets_dev, const void* workspace, size_t workspace_bytes) {
+// Checks of the sizes, the scores and the workspace (evict_select_prepare's
+// arguments).
+fam_status select_ws_check(const float* scores, int64_t score_row_stride, int H, int S, int sinks,
+                           int recent, const void* workspace, size_t workspace_bytes) {
   if (H < 0) return fail(FAM_ERR_INVALID_ARG, "H must be >= 0 (got %d)", H);
   if (S < 1 || S > kMaxSeq) return fail(FAM_ERR_INVALID_ARG, "S = %d out of range", S);
   if (sinks < 0 || recent < 0) return fail(FAM_ERR_INVALID_ARG, "sinks and recent must be >= 0");
   if (H == 0) return ok();
-  if (!scores || !idx || !offsets_dev || !budgets)
-    return fail(FAM_ERR_INVALID_ARG, "scores, budgets, idx and offsets_dev must be non-null");
+  if (!scores) return fail(FAM_ERR_INVALID_ARG, "scores must be non-null");
   if (H > 1 && score_row_stride < S) return fail(FAM_ERR_INVALID_ARG, "score row stride must be >= S");
-  for (int h = 0; h < H; ++h)
-    if (budgets[h] < 0) return fail(FAM_ERR_INVALID_ARG, "budget of head %d is negative", h);
   const Plan p = plan_of(S, sinks, recent);
   if (p.c1 - p.c0 > fam::kSelectLongMaxCandidates)
     return fail(FAM_ERR_UNSUPPORTED, "%d candidates per head exceed %d", p.c1 - p.c0,
@@ -539,6 +536,22 @@ fam_status select_check(const float* scores, int64_t score_row_stride, int H, in
   return ok();
 }
 
+// Checks of evict_select's arguments (all but the scores' values).
+fam_status select_check(const float* scores, int64_t score_row_stride, int H, int S,
+                        const int64_t* budgets, int sinks, int recent, const int32_t* idx,
+                        const int64_t* offsets_dev, const void* workspace, size_t workspace_bytes) {
+  if (H < 0) return fail(FAM_ERR_INVALID_ARG, "H must be >= 0 (got %d)", H);
+  if (S < 1 || S > kMaxSeq) return fail(FAM_ERR_INVALID_ARG, "S = %d out of range", S);
+  if (sinks < 0 || recent < 0) return fail(FAM_ERR_INVALID_ARG, "sinks and recent must be >= 0");
+  if (H == 0) return ok();
+  if (!scores || !idx || !offsets_dev || !budgets)
+    return fail(FAM_ERR_INVALID_ARG, "scores, budgets, idx and offsets_dev must be non-null");
+  if (H > 1 && score_row_stride < S) return fail(FAM_ERR_INVALID_ARG, "score row stride must be >= S");
+  for (int h = 0; h < H; ++h)
+    if (budgets[h] < 0) return fail(FAM_ERR_INVALID_ARG, "budget of head %d is negative", h);
+  return select_ws_check(scores, score_row_stride, H, S, sinks, recent, workspace, workspace_bytes);
+}
+
 // Whether the select of these sizes can take its scores straight from the
 // mass pass's partial slices (one batch of heads in three launches, more
 // than one chunk a head, some head neither empty nor whole).
@@ -552,6 +565,46 @@ bool select_from_parts_ok(int H, int S, const int64_t* budgets, int sinks, int r
     if (kh - p.forced != 0 && kh - p.forced != p.c1 - p.c0) return true;
   }
   return false;
+}
+
+// Whether evict_select of these sizes can be split at its first launch (the
+// budget-free histograms): one batch of heads in three launches.
+bool select_prepared_ok(int H, int S, int sinks, int recent) {
+  const Plan p = plan_of(S, sinks, recent);
+  return H >= 1 && H <= fam::kSelectBatch && p.c1 - p.c0 <= fam::kSelectMaxCandidates && select_chunks(p) >= 2;
+}
+
+// The launch arguments of one batch holding all H heads (select_prepared_ok
+// holds). Without budgets every head is given one choice, so that no head
+// skips the histogram launch.
+fam::SelectArgs prepared_args(const float* scores, int64_t score_row_stride, int H, int S, int sinks,
+                              int recent, const int64_t* budgets, int32_t* idx, int64_t* offsets_dev,
+                              void* workspace) {
+  const Plan p = plan_of(S, sinks, recent);
+  fam::SelectArgs a{};
+  a.scores = scores;
+  a.row_stride = score_row_stride;
+  a.idx = idx;
+  a.offsets_dev = offsets_dev;
+  a.ws = workspace;
+  a.S = S;
+  a.H = H;
+  a.c0 = p.c0;
+  a.c1 = p.c1;
+  a.slots = select_slots(H);
+  a.nchunk = select_chunks(p);
+  a.head0 = 0;
+  a.nheads = H;
+  int64_t off = 0;
+  for (int h = 0; h < H; ++h) {
+    int64_t kh = budgets ? (budgets[h] > p.forced ? budgets[h] : p.forced) : p.forced + 1;
+    if (kh > S) kh = S;
+    a.out_off[h] = off;
+    a.n_choose[h] = (int32_t)(kh - p.forced);
+    off += kh;
+  }
+  a.total = off;
+  return a;
 }
 
 // The select launches for checked arguments (H >= 1). With `part` non-null
@@ -662,6 +715,75 @@ fam_status fam_mass_select(const void* q, const void* k, const float* lse, fam_d
   if (const fam_status st = launched(e, hs, "fam_mass_select (mass pass)"); st != FAM_OK) return st;
   return select_run(mass, S, H, S, budgets, sinks, recent, idx, offsets_dev, select_workspace,
                     fused ? a.part : nullptr, a.nsplit, hs);
+}
+
+fam_status evict_select_prepare(const float* scores, int64_t score_row_stride, int H, int S, int sinks,
+                                int recent, void* workspace, size_t workspace_bytes, void* stream) {
+  if (const fam_status st = select_ws_check(scores, score_row_stride, H, S, sinks, recent, workspace,
+                                            workspace_bytes);
+      st != FAM_OK || !select_prepared_ok(H, S, sinks, recent))
+    return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const fam::SelectArgs a = prepared_args(scores, score_row_stride, H, S, sinks, recent, nullptr, nullptr,
+                                          nullptr, workspace);
+  return launched(fam::launch_select_hist(a, hs), hs, "evict_select_prepare launch");
+}
+
+fam_status evict_select_prepared(const float* scores, int64_t score_row_stride, int H, int S,
+                                 const int64_t* budgets, int sinks, int recent, int32_t* idx,
+                                 int64_t* offsets_dev, void* workspace, size_t workspace_bytes,
+                                 void* stream) {
+  if (const fam_status st = select_check(scores, score_row_stride, H, S, budgets, sinks, recent, idx,
+                                         offsets_dev, workspace, workspace_bytes);
+      st != FAM_OK || H == 0)
+    return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (!select_prepared_ok(H, S, sinks, recent))
+    return select_run(scores, score_row_stride, H, S, budgets, sinks, recent, idx, offsets_dev, workspace,
+                      nullptr, 0, hs);
+  const fam::SelectArgs a = prepared_args(scores, score_row_stride, H, S, sinks, recent, budgets, idx,
+                                          offsets_dev, workspace);
+  return launched(fam::launch_select_prepared(a, hs), hs, "evict_select_prepared launch");
+}
+
+fam_status fam_mass_prepare_select(const void* q, const void* k, const float* lse, fam_dtype dtype_arg,
+                                   int B, int Hq, int Hkv, int S, int d, int64_t q_sb, int64_t q_sh,
+                                   int64_t q_ss, int64_t k_sb, int64_t k_sh, int64_t k_ss, int W,
+                                   float scale, float* mass, void* mass_workspace,
+                                   size_t mass_workspace_bytes, int sinks, int recent,
+                                   void* select_workspace, size_t select_workspace_bytes, void* stream) {
+  const int dtype = enum_bits(&dtype_arg);
+  const ScoreShape s{B, Hq, Hkv, S, d, q_sb, q_sh, q_ss, k_sb, k_sh, k_ss, 0};   // Sq = 0: every row is a query
+  if (const fam_status st = check_scores(q, k, dtype, s); st != FAM_OK) return st;
+  fam::MassArgs a{};
+  if (const fam_status st = mass_prepare(q, k, lse, s, W, scale, mass, mass_workspace,
+                                         mass_workspace_bytes, a);
+      st != FAM_OK)
+    return st;
+  const int H = B * Hkv;
+  if (const fam_status st = select_ws_check(mass, S, H, S, sinks, recent, select_workspace,
+                                            select_workspace_bytes);
+      st != FAM_OK)
+    return st;
+  const bool prepared = select_prepared_ok(H, S, sinks, recent);
+  if (prepared && a.nsplit > 1) {
+    // the mass pass's slices are read while the select workspace is written
+    const uintptr_t m0 = reinterpret_cast<uintptr_t>(a.part);
+    const uintptr_t m1 = m0 + mass_split_bytes(s, a.nsplit);
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(select_workspace);
+    const uintptr_t s1 = s0 + select_workspace_bytes;
+    if (m0 < s1 && s0 < m1)
+      return fail(FAM_ERR_INVALID_ARG, "mass and select workspaces must not overlap");
+  }
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  const bool fused = prepared && a.nsplit > 1;
+  hipError_t e = fam::launch_mass(a, elem_of(dtype), hs, !fused);
+  if (const fam_status st = launched(e, hs, "fam_mass_prepare_select (mass pass)"); st != FAM_OK || !prepared)
+    return st;
+  const fam::SelectArgs sa = prepared_args(mass, S, H, S, sinks, recent, nullptr, nullptr, nullptr,
+                                           select_workspace);
+  e = fused ? fam::launch_select_hist_reduce(sa, a.part, a.nsplit, hs) : fam::launch_select_hist(sa, hs);
+  return launched(e, hs, "fam_mass_prepare_select (histograms)");
 }
 
 // evict_select without a caller workspace: the workspace is a static device

@@ -118,6 +118,16 @@ hipError_t launch_select(const SelectArgs& a, hipStream_t s);
 // than one chunk a head, at most kSelectMaxCandidates candidates and a head
 // that is not trivial; `a.scores` is the mass the launches write and read.
 hipError_t launch_select_from_parts(const SelectArgs& a, const float* part, int nsplit, hipStream_t s);
+// The select split in two for callers that build the first histograms
+// ahead of the budgets: launch_select_hist is the first launch alone (every
+// head with n_choose set so that none is skipped), launch_select_hist_reduce
+// the first launch of launch_select_from_parts alone, and
+// launch_select_prepared the launches after it (the last alone when every
+// head is empty or whole). The same conditions as launch_select_from_parts
+// apply, except that every head may be trivial.
+hipError_t launch_select_hist(const SelectArgs& a, hipStream_t s);
+hipError_t launch_select_hist_reduce(const SelectArgs& a, const float* part, int nsplit, hipStream_t s);
+hipError_t launch_select_prepared(const SelectArgs& a, hipStream_t s);
 size_t select_long_workspace_bytes(int slots);
 // Heads per long-path launch for heads of nchunk chunks (0: the device holds fewer).
 int select_long_batch_heads(int nchunk);

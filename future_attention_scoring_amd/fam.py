@@ -48,6 +48,11 @@ _SIGNATURES = {
     "fam_mass_select": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64, _i64,
                              _i, _f, _p, _p, ctypes.c_size_t, _p, _i, _i, _p, _p, _p,
                              ctypes.c_size_t, _p]),
+    "evict_select_prepare": (_i, [_p, _i64, _i, _i, _i, _i, _p, ctypes.c_size_t, _p]),
+    "evict_select_prepared": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p, ctypes.c_size_t, _p]),
+    "fam_mass_prepare_select": (_i, [_p, _p, _p, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64,
+                                     _i64, _i64, _i, _f, _p, _p, ctypes.c_size_t, _i, _i, _p,
+                                     ctypes.c_size_t, _p]),
     "evict_select_noalloc": (_i, [_p, _i64, _i, _i, _p, _i, _i, _p, _p, _p]),
     "kv_compact": (_i, [_p, _p, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _p, _p, _i64, _p, _p, _p]),
     "fam_compute_chunk": (_i, [_p, _p, _i, _i, _i, _i, _i, _i, _i, _i64, _i64, _i64, _i64, _i64,
@@ -326,9 +331,7 @@ def evict_select_workspace_size(H: int, S: int, sinks: int, recent: int) -> int:
     return int(load().evict_select_workspace_size(int(H), int(S), int(sinks), int(recent)))
 
 
-def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,
-                 idx: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
-                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+def _select_outputs(scores, budgets, sinks, recent, idx, offsets):
     if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
         raise FamError(1, "scores must be a device fp32 [H, S] tensor")
     if scores.shape[1] > 1 and scores.stride(1) != 1:
@@ -338,11 +341,17 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
     if b.size != H:
         raise FamError(1, f"{b.size} budgets for {H} heads")
     _, host_off = evict_plan(b, S, sinks, recent)
-    total = int(host_off[-1])
     if idx is None:
-        idx = torch.empty(total, dtype=torch.int32, device=scores.device)
+        idx = torch.empty(int(host_off[-1]), dtype=torch.int32, device=scores.device)
     if offsets is None:
         offsets = torch.empty(H + 1, dtype=torch.int64, device=scores.device)
+    return H, S, b, idx, offsets
+
+
+def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,
+                 idx: Optional[torch.Tensor] = None, offsets: Optional[torch.Tensor] = None,
+                 workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    H, S, b, idx, offsets = _select_outputs(scores, budgets, sinks, recent, idx, offsets)
     if workspace is None:
         nbytes = evict_select_workspace_size(H, S, sinks, recent)
         workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=scores.device)
@@ -351,6 +360,70 @@ def evict_select(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recen
                                workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                _stream(scores)))
     return idx, offsets
+
+
+def evict_select_prepare(scores: torch.Tensor, sinks: int, recent: int,
+                         workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The budget-free first part of evict_select on [H, S] scores, into
+    `workspace` (allocated when not given); returns the workspace, which
+    evict_select_prepared then takes with any budgets."""
+    if scores.dim() != 2 or scores.dtype != torch.float32 or not scores.is_cuda:
+        raise FamError(1, "scores must be a device fp32 [H, S] tensor")
+    if scores.shape[1] > 1 and scores.stride(1) != 1:
+        raise FamError(1, "scores rows must be contiguous")
+    H, S = scores.shape
+    if workspace is None:
+        nbytes = evict_select_workspace_size(H, S, sinks, recent)
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=scores.device)
+    _check(load().evict_select_prepare(scores.data_ptr(), _row_stride(scores), H, S, int(sinks),
+                                       int(recent), workspace.data_ptr(),
+                                       workspace.numel() * workspace.element_size(), _stream(scores)))
+    return workspace
+
+
+def evict_select_prepared(scores: torch.Tensor, budgets: Sequence[int], sinks: int, recent: int,
+                          workspace: torch.Tensor, idx: Optional[torch.Tensor] = None,
+                          offsets: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """evict_select on scores whose workspace evict_select_prepare or
+    fam_mass_prepare_select prepared: returns (idx, offsets)."""
+    H, S, b, idx, offsets = _select_outputs(scores, budgets, sinks, recent, idx, offsets)
+    _check(load().evict_select_prepared(scores.data_ptr(), _row_stride(scores), H, S, b.ctypes.data,
+                                        int(sinks), int(recent), idx.data_ptr(), offsets.data_ptr(),
+                                        workspace.data_ptr(),
+                                        workspace.numel() * workspace.element_size(), _stream(scores)))
+    return idx, offsets
+
+
+def fam_mass_prepare_select(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int, sinks: int,
+                            recent: int, scale: Optional[float] = None,
+                            mass: Optional[torch.Tensor] = None,
+                            mass_workspace: Optional[torch.Tensor] = None,
+                            select_workspace: Optional[torch.Tensor] = None
+                            ) -> Tuple[torch.Tensor, torch.Tensor]:
+    """fam_mass that also prepares evict_select's workspace for its [B * Hkv, S]
+    output: returns (mass [B, Hkv, S] (or [Hkv, S]), select_workspace)."""
+    q4, k4, B, Hq, Hkv, S, d = _score_args(q, k)
+    lse = lse.contiguous()
+    if lse.numel() != B * Hq * S or lse.dtype != torch.float32:
+        raise FamError(1, "lse must be fp32 [B, Hq, S]")
+    H = B * Hkv
+    if mass is None:
+        mass = torch.empty((B, Hkv, S), dtype=torch.float32, device=q4.device)
+    if mass_workspace is None:
+        n = fam_mass_workspace_size(B, Hq, Hkv, S)
+        mass_workspace = torch.empty(n, dtype=torch.uint8, device=q4.device) if n else None
+    mws, mbytes = ((mass_workspace.data_ptr(), mass_workspace.numel() * mass_workspace.element_size())
+                   if mass_workspace is not None else (None, 0))
+    if select_workspace is None:
+        nbytes = evict_select_workspace_size(H, S, sinks, recent)
+        select_workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q4.device)
+    _check(load().fam_mass_prepare_select(q4.data_ptr(), k4.data_ptr(), lse.data_ptr(), _dtype_code(q4),
+                                          B, Hq, Hkv, S, d, *q4.stride()[:3], *k4.stride()[:3], int(W),
+                                          0.0 if scale is None else scale, mass.data_ptr(), mws, mbytes,
+                                          int(sinks), int(recent), select_workspace.data_ptr(),
+                                          select_workspace.numel() * select_workspace.element_size(),
+                                          _stream(q4)))
+    return (mass if q.dim() == 4 else mass[0]), select_workspace
 
 
 def fam_mass_select(q: torch.Tensor, k: torch.Tensor, lse: torch.Tensor, W: int,

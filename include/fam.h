@@ -433,6 +433,62 @@ fam_status fam_mass_select(const void* q, const void* k, const float* lse, fam_d
                            void* stream);
 
 /* ------------------------------------------------------------------------
+ * evict_select_prepare / evict_select_prepared / fam_mass_prepare_select --
+ * evict_select split at the part that does not depend on the budgets.
+ *
+ * [KVP] section 3 (the cache holds the top b of one ranking, for every
+ * budget b) and [Blog] "What we did" (one score set evicted at several cache
+ * budgets): the selection's first histograms depend only on the scores, so
+ * they can be built once, ahead of the budgets, and serve every later
+ * selection on the same scores.
+ *
+ *   evict_select_prepare(scores, row_stride, H, S, sinks, recent,
+ *                        workspace, ...)
+ *       builds those histograms in `workspace` (evict_select's workspace of
+ *       evict_select_workspace_size(H, S, sinks, recent) bytes);
+ *   fam_mass_prepare_select(<fam_mass's arguments>, sinks, recent,
+ *                           select_workspace, ...)
+ *       is fam_mass (same mass, bit for bit) that also builds them for its
+ *       own output, in the launch that adds the mass pass's partial sums
+ *       when the pass splits (a mass_workspace of fam_mass_workspace_size
+ *       bytes), so without a launch of their own;
+ *   evict_select_prepared(<evict_select's arguments>)
+ *       is evict_select (same idx and offsets_dev, bit for bit) without the
+ *       histogram launch, on a workspace that one of the two calls above
+ *       prepared for these scores, H, S, sinks and recent, and that nothing
+ *       has written since; it may be called any number of times, with any
+ *       budgets.
+ * The split applies when the H <= 64 heads have more than 4096 and at most
+ * 131072 candidates each; for other sizes the preparing calls build nothing
+ * (fam_mass_prepare_select is then fam_mass) and evict_select_prepared is
+ * evict_select. A workspace not prepared for these scores gives an
+ * unspecified selection.
+ *
+ * Arguments: as for evict_select, fam_mass and fam_mass_select; the select
+ *   workspace must not overlap the mass workspace (refused).
+ * Errors: those of evict_select and fam_mass; nothing is launched when an
+ *   argument is refused.
+ * ---------------------------------------------------------------------- */
+fam_status evict_select_prepare(const float* scores, int64_t score_row_stride, int H, int S,
+                                int sinks, int recent, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+fam_status evict_select_prepared(const float* scores, int64_t score_row_stride, int H, int S,
+                                 const int64_t* budgets, int sinks, int recent,
+                                 int32_t* idx, int64_t* offsets_dev,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+fam_status fam_mass_prepare_select(const void* q, const void* k, const float* lse, fam_dtype dtype,
+                                   int B, int Hq, int Hkv, int S, int d,
+                                   int64_t q_sb, int64_t q_sh, int64_t q_ss,
+                                   int64_t k_sb, int64_t k_sh, int64_t k_ss,
+                                   int W, float scale, float* mass,
+                                   void* mass_workspace, size_t mass_workspace_bytes,
+                                   int sinks, int recent,
+                                   void* select_workspace, size_t select_workspace_bytes,
+                                   void* stream);
+
+/* ------------------------------------------------------------------------
  * evict_select_noalloc -- evict_select for callers that cannot allocate.
  *
  * For callers that may not allocate device memory at all (code under HIP

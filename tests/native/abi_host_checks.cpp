@@ -122,6 +122,14 @@ int main() {
     EXPECT(fam_mass_select(fake, fake, ffake, FAM_BF16, 1, 4, 2, 8192, 128, 0, 8192 * 128, 128, 0, 8192 * 128, 128,
                            4, 0.f, ffake, fake, mws, b, 4, 64, ifake, lfake, nullptr, 0, nullptr) ==
            FAM_ERR_WORKSPACE);
+    EXPECT(evict_select_prepare(ffake, 8192, 2, 8192, 4, 64, fake, sws - 1, nullptr) == FAM_ERR_WORKSPACE);
+    EXPECT(evict_select_prepare(nullptr, 8192, 2, 8192, 4, 64, fake, sws, nullptr) == FAM_ERR_INVALID_ARG);
+    EXPECT(evict_select_prepare(ffake, 8192, 0, 8192, 4, 64, nullptr, 0, nullptr) == FAM_OK);
+    EXPECT(evict_select_prepared(ffake, 8192, 2, 8192, b, 4, 64, nullptr, lfake, fake, sws, nullptr) ==
+           FAM_ERR_INVALID_ARG);
+    EXPECT(fam_mass_prepare_select(fake, fake, ffake, FAM_BF16, 1, 4, 2, 8192, 128, 0, 8192 * 128, 128, 0,
+                                   8192 * 128, 128, 4, 0.f, ffake, fake, mws, 4, 64, fake, sws, nullptr) ==
+           FAM_ERR_INVALID_ARG);                                                     // overlapping workspaces
   }
   EXPECT(kv_compact(fake, fake, 4, 2, 100, 128, 0, 128, 0, 128, ifake, lfake, 10, fake, fake, nullptr) ==
          FAM_ERR_UNSUPPORTED);

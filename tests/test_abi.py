@@ -208,6 +208,36 @@ def test_fam_mass_select_validation():
     assert call(sel_ws=FAKE + mws - 16) == INVALID         # overlapping its end
 
 
+def test_select_prepare_validation():
+    """The split select refuses what evict_select and fam_mass refuse, and
+    overlapping workspaces, before anything is launched; H == 0 is a no-op."""
+    lib = fam.load()
+    S, H = 8192, 2
+    mws = lib.fam_mass_workspace_size(1, 4, 2, S)
+    sws = lib.evict_select_workspace_size(H, S, 4, 64)
+    b = np.array([1000, 2000], dtype=np.int64)
+    assert lib.evict_select_prepare(FAKE, S, H, S, 4, 64, FAKE, sws - 1, None) == WORKSPACE
+    assert lib.evict_select_prepare(FAKE, S, H, S, 4, 64, FAKE + 8, sws, None) == INVALID
+    assert lib.evict_select_prepare(None, S, H, S, 4, 64, FAKE, sws, None) == INVALID
+    assert lib.evict_select_prepare(FAKE, S - 1, H, S, 4, 64, FAKE, sws, None) == INVALID
+    assert lib.evict_select_prepare(FAKE, S, H, S, -1, 64, FAKE, sws, None) == INVALID
+    assert lib.evict_select_prepare(FAKE, S, 0, S, 4, 64, None, 0, None) == 0
+    bad = np.array([1000, -1], dtype=np.int64)
+    assert lib.evict_select_prepared(FAKE, S, H, S, bad.ctypes.data, 4, 64, FAKE, FAKE, FAKE, sws, None) == INVALID
+    assert lib.evict_select_prepared(FAKE, S, H, S, b.ctypes.data, 4, 64, None, FAKE, FAKE, sws, None) == INVALID
+    assert lib.evict_select_prepared(FAKE, S, H, S, b.ctypes.data, 4, 64, FAKE, FAKE, FAKE, sws - 1, None) == WORKSPACE
+
+    def call(lse=FAKE, W=4, sel_ws=FAKE + (1 << 30), sel_bytes=sws, d=128):
+        return lib.fam_mass_prepare_select(FAKE, FAKE, lse, 0, 1, 4, 2, S, d, 0, S * d, d, 0, S * d, d, W,
+                                           0.0, FAKE, FAKE, mws, 4, 64, sel_ws, sel_bytes, None)
+
+    assert call(lse=None) == INVALID
+    assert call(W=-1) == INVALID
+    assert call(d=100) == UNSUPPORTED
+    assert call(sel_bytes=sws - 1) == WORKSPACE
+    assert call(sel_ws=FAKE + 1024) == INVALID             # inside the mass workspace
+
+
 def test_mass_workspace_size():
     lib = fam.load()
     # from 65536 keys on, one part per range of 64 query tiles of 64 rows

@@ -217,7 +217,7 @@ def test_range_mass_matches_even_splits_and_unsplit(seed, B, Hq, Hkv, S, d, W):
         assert rel <= 1e-5, f"{name}: max rel diff {rel}"
     if W == 0:
         tot = ranged.double().sum(dim=-1).cpu().numpy()
-        np.testing.assert_allclose(tot, np.full((B, Hkv), S * (Hq // Hkv)), rtol=1e-4)
+        np.testing.assert_allclose(tot, np.full((B, Hkv), S * (Hq // Hkv)), rtol=1e-5)
 
 
 @pytest.mark.parametrize("dtype,strided", [(torch.float16, False), (torch.bfloat16, True)])
@@ -298,7 +298,7 @@ def test_range_mass_of_a_chunk(Sq, Sk, W):
     assert ((ranged - whole).abs()[pos] / whole[pos]).max().item() <= 2e-5
     if W == 0:
         tot = ranged.double().sum(dim=-1).cpu().numpy()
-        np.testing.assert_allclose(tot, np.full((B, Hkv), Sq * (Hq // Hkv)), rtol=1e-4)
+        np.testing.assert_allclose(tot, np.full((B, Hkv), Sq * (Hq // Hkv)), rtol=1e-5)
 
 
 @pytest.mark.parametrize("S,W,a,b", [(65536, 100, 4.0, 4.0), (777, 3, 8.0, 2.0)])

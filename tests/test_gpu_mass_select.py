@@ -128,3 +128,74 @@ def test_mass_select_fp16_and_strided_views():
     qs = torch.randn(1, 10000, 4, 128, generator=g).to(torch.bfloat16).to(DEV).transpose(1, 2)
     ks = torch.randn(1, 10000, 2, 128, generator=g).to(torch.bfloat16).to(DEV).transpose(1, 2)
     check(qs, ks, 100, budgets_for(22, 2, 10000, 4, 100), 4, 100)
+
+
+def check_prepared(q, k, W, budget_sets, sinks, recent, mass_ws_bytes=None):
+    """fam_mass_prepare_select, then evict_select_prepared with each budget set
+    on the one prepared workspace, against fam_mass + evict_select and the
+    oracle."""
+    B, Hq, S, _ = q.shape
+    Hkv = k.shape[1]
+    lse = fam.fam_lse(q, k)
+    mws = None
+    if mass_ws_bytes is not None:
+        mws = torch.empty(max(mass_ws_bytes, 16), dtype=torch.uint8, device=DEV)
+    mass, sws = fam.fam_mass_prepare_select(q, k, lse, W, sinks, recent, mass_workspace=mws)
+    ref_mass = fam.fam_mass(q, k, lse, W, workspace=mws)
+    torch.cuda.synchronize()
+    assert torch.equal(mass.view(torch.int32), ref_mass.view(torch.int32)), "masses differ"
+    rows = mass.reshape(B * Hkv, S)
+    for budgets in budget_sets:
+        idx, off = fam.evict_select_prepared(rows, budgets, sinks, recent, sws)
+        ref_idx, ref_off = fam.evict_select(rows, budgets, sinks, recent)
+        torch.cuda.synchronize()
+        assert torch.equal(off, ref_off), f"offsets differ for budgets {budgets}"
+        assert torch.equal(idx, ref_idx), f"index lists differ for budgets {budgets}"
+        o_idx, o_off = so.select(rows.cpu().numpy(), budgets, sinks, recent)
+        assert np.array_equal(idx.cpu().numpy(), o_idx), "index lists differ from the oracle's"
+
+
+@pytest.mark.parametrize("seed,B,Hq,Hkv,S,W,sinks,recent,split", [
+    (11, 1, 8, 2, 9001, 64, 4, 64, True),      # split mass pass: histograms in its reduction
+    (12, 1, 8, 2, 9001, 64, 4, 64, False),     # no split: a histogram launch of its own
+    (13, 2, 4, 2, 12288, 16, 7, 5000, True),   # positions before the first and after the last chunk
+    (14, 1, 6, 3, 70001, 512, 4, 512, True),   # ranges of query rows, ragged rows
+    (15, 8, 8, 8, 8192, 16, 4, 16, True),      # 64 heads: one full batch
+    (16, 1, 4, 2, 4000, 16, 4, 16, True),      # one chunk a head: nothing prepared
+    (17, 9, 8, 8, 8192, 16, 4, 16, True),      # 72 heads, more than one batch: nothing prepared
+])
+def test_prepared_select_matches_two_calls(seed, B, Hq, Hkv, S, W, sinks, recent, split):
+    say(f"fam_mass_prepare_select seed={seed} B={B} Hq={Hq} Hkv={Hkv} S={S} W={W} split={split}")
+    q, k = inputs(seed, B, Hq, Hkv, S)
+    H = B * Hkv
+    forced = min(S, sinks + min(recent, max(0, S - sinks)))
+    sets = [budgets_for(seed, H, S, sinks, recent),
+            [forced] * H,                                   # every head trivial: the last launch alone
+            [S] * H,
+            budgets_for(seed + 100, H, S, sinks, recent)]
+    check_prepared(q, k, W, sets, sinks, recent, None if split else 0)
+
+
+@pytest.mark.parametrize("H,S,sinks,recent", [(8, 131072, 4, 512), (3, 20000, 0, 0), (5, 150001, 4, 64)])
+def test_evict_select_prepare_on_given_scores(H, S, sinks, recent):
+    """evict_select_prepare on given scores (mass-like heavy tails, ties,
+    -0.0, NaN and infinities), then several budget sets on the one workspace;
+    150001 positions exceed the three-launch select (nothing prepared)."""
+    say(f"evict_select_prepare H={H} S={S} sinks={sinks} recent={recent}")
+    g = torch.Generator().manual_seed(H * 1000 + S)
+    x = torch.exp(torch.randn(H, S, generator=g) * 3.0)
+    x[:, ::97] = x[:, 5:6]                     # ties
+    x[0, 10:20] = float("nan")
+    x[-1, 30:40] = -0.0
+    x[-1, 41] = float("inf")
+    x[0, 42] = float("-inf")
+    scores = x.to(DEV)
+    ws = fam.evict_select_prepare(scores, sinks, recent)
+    for seed in range(3):
+        budgets = budgets_for(seed, H, S, sinks, recent)
+        idx, off = fam.evict_select_prepared(scores, budgets, sinks, recent, ws)
+        ref_idx, ref_off = fam.evict_select(scores, budgets, sinks, recent)
+        torch.cuda.synchronize()
+        assert torch.equal(off, ref_off) and torch.equal(idx, ref_idx), f"budgets {budgets}"
+    o_idx, _ = so.select(x.numpy(), budgets, sinks, recent)
+    assert np.array_equal(idx.cpu().numpy(), o_idx)
