@@ -163,11 +163,7 @@ __device__ __forceinline__ void load_chunk(const SelectArgs& p, const float* row
 template <int NT = kThreads>
 __device__ int block_scan(int v, int* sh, int& total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
+  v = wave_scan(v);
   if (lane == 63) sh[wave] = v;
   __syncthreads();
   int before = 0, tot = 0;
@@ -188,13 +184,8 @@ template <typename F>
 __device__ __forceinline__ void wave0_exclusive_scan(int n, F val, int* out) {
   if (threadIdx.x < 64) {
     const int lane = threadIdx.x;
-    int v = lane < n ? val(lane) : 0;
-    const int x = v;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int t = __shfl_up(v, d);
-      if (lane >= d) v += t;
-    }
+    const int x = lane < n ? val(lane) : 0;
+    const int v = wave_scan(x);
     if (lane < n) out[lane] = v - x;
     if (lane == 63) out[n] = v;
   }
