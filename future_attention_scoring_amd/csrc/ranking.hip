@@ -125,12 +125,7 @@ __global__ __launch_bounds__(kScanThreads) void rank_scan(RankArgs p) {
       c[j] = i0 + j < n ? hist[i0 + j] : 0;
       sum += c[j];
     }
-    int incl = sum;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int t = __shfl_up(incl, o);
-      if (lane >= o) incl += t;
-    }
+    const int incl = wave_scan(sum);
     if (lane == 63) sh[wave] = incl;
     __syncthreads();
     int run = carry + incl - sum, all = 0;
@@ -177,12 +172,7 @@ __global__ __launch_bounds__(kRankThreads) void rank_place(RankArgs p, int pass)
       before += t < tile ? c[t] : 0;
     }
     // exclusive scan of the digit totals over the 256 threads
-    int incl = all;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const int u = __shfl_up(incl, o);
-      if (lane >= o) incl += u;
-    }
+    const int incl = wave_scan(all);
     if (lane == 63) ssh[wave] = incl;
     __syncthreads();
     int prev = 0;
