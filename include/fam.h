@@ -458,8 +458,10 @@ fam_status fam_mass_select(const void* q, const void* k, const float* lse, fam_d
  *       prepared for these scores, H, S, sinks and recent, and that nothing
  *       has written since; it may be called any number of times, with any
  *       budgets.
- * The split applies when the H <= 64 heads have more than 4096 and at most
- * 131072 candidates each; for other sizes the preparing calls build nothing
+ * The split applies when there are H <= 64 heads whose at most 131072
+ * candidates span more than one chunk of 4096 positions (chunks start at the
+ * first candidate rounded down to a multiple of 4); for other sizes the
+ * preparing calls build nothing
  * (fam_mass_prepare_select is then fam_mass) and evict_select_prepared is
  * evict_select. A workspace not prepared for these scores gives an
  * unspecified selection.
